@@ -1,0 +1,105 @@
+"""Host-side workload construction: determinism, sizing, block manager (CPU only)."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+
+def test_decode_case_is_deterministic():
+    a = W.make_decode_case("tiny_f32")
+    b = W.make_decode_case("tiny_f32")
+    for name in ("q", "k_pool", "v_pool", "block_tables", "seq_lens", "new_k", "new_v",
+                 "slot_mapping"):
+        assert np.array_equal(getattr(a, name), getattr(b, name))
+    c = W.make_decode_case("tiny_f32", rep=1)
+    assert not np.array_equal(a.q, c.q)
+
+
+def test_decode_case_layout_and_poison():
+    case = W.make_decode_case("tiny_f32")
+    spec = case.spec
+    assert case.k_pool.shape == (64, 2, 16, 64)
+    assert list(case.seq_lens) == [1, 17, 33, 64]
+    nb_used = [W.blocks_for(int(n), 16) for n in case.seq_lens]
+    ids = np.concatenate([case.block_tables[s, :k] for s, k in enumerate(nb_used)])
+    assert len(set(ids.tolist())) == len(ids)                    # no block shared
+    assert case.poison_block not in set(ids.tolist())
+    for s, k in enumerate(nb_used):
+        assert np.all(case.block_tables[s, k:] == case.poison_block)
+    # the newest token's slot holds NaN until the scatter writes it
+    for s, slot in enumerate(case.slot_mapping):
+        blk, row = slot // 16, slot % 16
+        n = int(case.seq_lens[s])
+        assert blk == case.block_tables[s, (n - 1) // 16] and row == (n - 1) % 16
+        assert np.all(case.k_pool[blk, :, row, :] == W.NAN_BITS["f32"])
+    assert np.all(case.k_pool[case.poison_block] == W.NAN_BITS["f32"])
+    assert spec.scale == 1.0 / 8.0
+
+
+def test_fp8_case_scales_cover_amax():
+    case = W.make_decode_case("llama3_70b_fp8kv", num_seqs=6)
+    valid = case.k_pool[case.k_pool != 0x7F]
+    assert case.k_scale > 0 and case.v_scale > 0
+    # some stored code reaches the top binade (the amax maps to ~448)
+    assert ((valid & 0x7F) >= 0x78).any()
+
+
+def test_pool_sizing_rules():
+    c2 = W.make_decode_case("llama2_7b_mha_f16", num_seqs=4)
+    assert c2.k_pool.shape[0] == 8192
+    c3 = W.make_decode_case("llama3_8b_gqa_bf16", num_seqs=5)
+    blocks = sum(W.blocks_for(int(n), 16) for n in c3.seq_lens)
+    assert c3.k_pool.shape[0] == int(np.ceil(1.1 * blocks)) + 1
+    assert c3.block_tables.shape == (5, 512)
+
+
+def test_lognormal_lengths_are_clipped():
+    rng = np.random.default_rng(0)
+    lens = W.draw_lengths(("lognormal", 1200.0, 0.8, 16, 8192), 10000, rng)
+    assert lens.min() >= 16 and lens.max() <= 8192
+    assert 1000 < np.median(lens) < 1400
+
+
+def test_block_manager_oom_and_refcounts():
+    mgr = W.BlockManager(4, 2)
+    t = mgr.allocate(3)
+    assert len(t) == 2
+    with pytest.raises(RuntimeError, match="OOM"):
+        mgr.allocate(5)
+    f = mgr.fork(t)
+    assert all(mgr.ref[b] == 2 for b in t)
+    pair = mgr.copy_on_write(f, 1)
+    assert pair == (t[1], f[1]) and mgr.ref[t[1]] == 1 and mgr.ref[f[1]] == 1
+    assert mgr.copy_on_write(f, 1) is None
+    mgr.release(f)
+    assert mgr.ref[t[0]] == 1
+    mgr.release(t)
+    assert sorted(mgr.free) == [0, 1, 2, 3]
+
+
+def test_block_manager_grow_at_block_size_one():
+    mgr = W.BlockManager(8, 1)
+    t = mgr.allocate(2)
+    mgr.grow(t, 3)
+    assert len(t) == 3
+
+
+def test_mixed_case_structure():
+    case = W.make_mixed_case(num_forks=4, prefix_len=64, chunk_len=16, num_decode=3,
+                             decode_lens=[33, 64, 65])
+    bs = case.spec.block_size
+    assert case.cow_pairs.shape == (3, 2)
+    last = 64 // bs - 1
+    original = case.prefill_tables_shared[0, last]
+    assert np.all(case.prefill_tables_shared[:, last] == original)
+    assert np.all(case.cow_pairs[:, 0] == original)
+    # exactly one fork keeps the original block, the others hold distinct copies
+    now = case.prefill_tables[:, last].tolist()
+    assert now.count(original) == 1
+    assert sorted(b for b in now if b != original) == sorted(case.cow_pairs[:, 1].tolist())
+    # blocks before the divergent one stay shared
+    assert np.all(case.prefill_tables[:, : last] == case.prefill_tables_shared[:, : last])
+    assert case.slot_mapping.shape == (4 * 16 + 3,)
+    assert len(set(case.slot_mapping.tolist())) == len(case.slot_mapping)
+    assert list(case.query_start_loc) == [0, 16, 32, 48, 64]

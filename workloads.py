@@ -1,0 +1,483 @@
+"""Seeded synthetic inputs for the paged KV-cache attention path.
+
+This module draws random numbers and lays them out in the shapes the library
+consumes.  It holds none of the attention arithmetic: no softmax, no dot
+products, no fp8 encoder of its own (fp8 pool contents come from torch's CPU
+cast to ``float8_e4m3fn``).  Both the HIP path and the CPU oracle read the
+arrays produced here; nothing here reads either of them.
+
+Host-side block management (free list, reference counts, fork, copy-on-write
+plan, OOM) also lives here, because the workloads need it to build block
+tables.  It follows the datawhalechina page "17. vLLM PagedAttention"
+(Step 4 and "参考代码与解析": allocate ceil(len / block_size) blocks for a prompt,
+one more block when a decode step crosses a block boundary, raise "OOM" when
+the free list runs short) and the ybb.press page "vLLM 与 LLM 推理部署实战"
+(§2.1 block table + free list; §2.2 reference counts and copy-on-write).
+
+Element storage: every tensor is a numpy array of the element's raw bits
+(f32 -> uint32, f16/bf16 -> uint16, fp8_e4m3 -> uint8).  Pools are
+[num_blocks][num_kv_heads][block_size][head_dim].  Slots that hold no token
+are NaN-poisoned so that a kernel reading them shows up as NaN.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+import torch
+
+BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8_e4m3": torch.float8_e4m3fn}
+TORCH_BITS = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "fp8_e4m3": torch.uint8}
+FP8_MAX = 448.0
+
+
+def to_bits(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the storage type (torch CPU cast, RNE) -> raw bits."""
+    x = np.ascontiguousarray(x_f32, dtype=np.float32)
+    if dtype == "f32":
+        return x.view(np.uint32).copy()
+    t = torch.from_numpy(x)
+    if dtype == "fp8_e4m3":
+        t = t.clamp(-FP8_MAX, FP8_MAX)
+    return t.to(TORCH_DTYPE[dtype]).view(TORCH_BITS[dtype]).numpy().view(BITS_DTYPE[dtype]).copy()
+
+
+def bits_to_torch(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    """View raw bits as a torch CPU tensor of the element type (no copy of values)."""
+    arr = np.ascontiguousarray(bits)
+    signed = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16,
+              np.dtype(np.uint8): np.uint8}[arr.dtype]
+    return torch.from_numpy(arr.view(signed)).view(TORCH_DTYPE[dtype])
+
+
+def torch_to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    """Raw bits of a (CPU or device) torch tensor of the element type."""
+    return t.detach().cpu().contiguous().view(TORCH_BITS[dtype]).numpy().view(BITS_DTYPE[dtype]).copy()
+
+
+def blocks_for(num_tokens: int, block_size: int) -> int:
+    """Blocks needed to hold num_tokens tokens (integer ceiling)."""
+    return -(-num_tokens // block_size) if num_tokens > 0 else 0
+
+
+class BlockManager:
+    """Free list + reference counts for a pool of physical KV blocks.
+
+    ``order`` is the order in which free blocks are handed out (the pages'
+    exercise pops the lowest index first; the workloads pass a seeded
+    permutation so that physical IDs are scattered).
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, order=None):
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = list(range(num_blocks)) if order is None else [int(b) for b in order]
+        self.ref = np.zeros(num_blocks, dtype=np.int64)
+
+    def _take(self) -> int:
+        if not self.free:
+            raise RuntimeError("OOM")
+        b = self.free.pop(0)
+        self.ref[b] = 1
+        return b
+
+    def allocate(self, num_tokens: int) -> list:
+        """Blocks for a new prompt of num_tokens tokens (all or nothing)."""
+        need = blocks_for(num_tokens, self.block_size)
+        if len(self.free) < need:
+            raise RuntimeError("OOM")
+        return [self._take() for _ in range(need)]
+
+    def grow(self, table: list, new_len: int) -> None:
+        """Append blocks so that the table covers new_len tokens."""
+        while blocks_for(new_len, self.block_size) > len(table):
+            table.append(self._take())
+
+    def fork(self, table: list) -> list:
+        """A new sequence sharing every block of ``table`` (reference counts +1)."""
+        for b in table:
+            self.ref[b] += 1
+        return list(table)
+
+    def copy_on_write(self, table: list, logical: int):
+        """Give ``table`` a private copy of logical block ``logical`` if it is shared.
+
+        Returns the (src, dst) pair the device copy must perform, or None.
+        """
+        b = table[logical]
+        if self.ref[b] <= 1:
+            return None
+        dst = self._take()
+        self.ref[b] -= 1
+        table[logical] = dst
+        return (b, dst)
+
+    def release(self, table: list) -> None:
+        for b in table:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        table.clear()
+
+
+# ---------------------------------------------------------------------------
+# Workload specifications
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeSpec:
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    q_dtype: str
+    cache_dtype: str
+    lens: tuple            # ("fixed", values) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
+    pool: tuple            # ("fixed", num_blocks) | ("factor", f)
+    value_std: float
+    max_len: int           # largest length the distribution allows (sizes the block table)
+    partition_size: int = 0   # 0 = library's choice
+    per_tensor_fp8_scale: bool = False
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return blocks_for(self.max_len, self.block_size)
+
+
+DECODE_SPECS = {
+    "tiny_f32": DecodeSpec(
+        "tiny_f32", 4, 2, 2, 64, 16, "f32", "f32", ("fixed", (1, 17, 33, 64)),
+        ("fixed", 64), 1.0, 64,
+        description="4 sequences of lengths 1/17/33/64, 2 q / 2 KV heads, head_dim 64, "
+                    "block 16, 64-block pool, fp32"),
+    "llama2_7b_mha_f16": DecodeSpec(
+        "llama2_7b_mha_f16", 64, 32, 32, 128, 16, "f16", "f16", ("uniform", 128, 2048),
+        ("fixed", 8192), 0.5, 2048,
+        description="Llama-2-7B-shaped layer: batch 64, 32/32 heads, head_dim 128, block 16, "
+                    "lens U[128,2048], 8192-block pool, fp16, values N(0,1)*0.5"),
+    "llama3_8b_gqa_bf16": DecodeSpec(
+        "llama3_8b_gqa_bf16", 256, 32, 8, 128, 16, "bf16", "bf16",
+        ("lognormal", 1200.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
+        description="Llama-3-8B-shaped GQA layer: batch 256, 32/8 heads, head_dim 128, block 16, "
+                    "lens lognormal(median 1200, sigma 0.8) in [16,8192], pool 1.1x, bf16"),
+    "llama3_70b_fp8kv": DecodeSpec(
+        "llama3_70b_fp8kv", 128, 64, 8, 128, 16, "bf16", "fp8_e4m3",
+        ("lognormal", 1500.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
+        partition_size=512, per_tensor_fp8_scale=True,
+        description="70B-shaped layer on one GPU: 128 sequences, 64/8 heads, head_dim 128, block 16, "
+                    "lens lognormal(median 1500, sigma 0.8) in [16,8192], fp8 e4m3 KV with "
+                    "per-tensor scales, bf16 q, 512-token split-KV partitions"),
+}
+
+
+def draw_lengths(spec_lens: tuple, count: int, rng: np.random.Generator) -> np.ndarray:
+    kind = spec_lens[0]
+    if kind == "fixed":
+        vals = np.asarray(spec_lens[1], dtype=np.int64)
+        assert len(vals) == count
+        return vals
+    if kind == "uniform":
+        return rng.integers(spec_lens[1], spec_lens[2] + 1, size=count).astype(np.int64)
+    if kind == "lognormal":
+        median, sigma, lo, hi = spec_lens[1:]
+        raw = np.rint(np.exp(rng.normal(math.log(median), sigma, size=count)))
+        return np.clip(raw, lo, hi).astype(np.int64)
+    raise ValueError(kind)
+
+
+def _rng(name: str, rep: int) -> np.random.Generator:
+    salt = sum((i + 1) * ord(c) for i, c in enumerate(name))
+    return np.random.default_rng(np.random.SeedSequence((415, salt, rep)))
+
+
+@dataclass
+class DecodeCase:
+    """One decode step's inputs: a pool holding every token but the newest,
+    the newest token's K/V and slot, and the queries."""
+    spec: DecodeSpec
+    q: np.ndarray              # bits [S][Hq][D]
+    k_pool: np.ndarray         # bits [NB][Hkv][bs][D]
+    v_pool: np.ndarray
+    block_tables: np.ndarray   # int32 [S][MB]; padding -> poison_block
+    seq_lens: np.ndarray       # int32 [S], includes the new token
+    new_k: np.ndarray          # bits [S][Hkv][D] in the source dtype
+    new_v: np.ndarray
+    src_dtype: str
+    slot_mapping: np.ndarray   # int64 [S]
+    k_scale: float
+    v_scale: float
+    poison_block: int
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_blocks(self) -> int:
+        return self.k_pool.shape[0]
+
+
+def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None = None,
+                     lens=None) -> DecodeCase:
+    """Build a seeded decode step for ``spec`` (optionally with fewer sequences or
+    explicit lengths, for small parity cases)."""
+    if isinstance(spec, str):
+        spec = DECODE_SPECS[spec]
+    rng = _rng(spec.name, rep)
+    S = spec.num_seqs if num_seqs is None else num_seqs
+    H, Hq, D, bs = spec.num_kv_heads, spec.num_q_heads, spec.head_dim, spec.block_size
+    if lens is None:
+        seq_lens = draw_lengths(spec.lens, spec.num_seqs, rng)[:S]
+    else:
+        seq_lens = np.asarray(lens, dtype=np.int64)
+        S = len(seq_lens)
+    need = [blocks_for(int(n), bs) for n in seq_lens]
+    total_blocks = sum(need)
+    if spec.pool[0] == "fixed":
+        nb = max(spec.pool[1], total_blocks + 1)
+    else:
+        nb = int(math.ceil(spec.pool[1] * total_blocks)) + 1
+    mb = max(spec.max_blocks_per_seq, max(need) if need else 1)
+
+    mgr = BlockManager(nb, bs, order=rng.permutation(nb))
+    tables = [mgr.allocate(int(n)) for n in seq_lens]
+    poison_block = mgr._take()
+
+    cache_dt, q_dt = spec.cache_dtype, spec.q_dtype
+    src_dt = q_dt                                  # new K/V arrive in the activation dtype
+    std = np.float32(spec.value_std)
+
+    # Values for every token of every sequence, newest included (float32).
+    k_vals = [rng.standard_normal((blocks_for(int(n), bs), H, bs, D), dtype=np.float32) * std
+              for n in seq_lens]
+    v_vals = [rng.standard_normal((blocks_for(int(n), bs), H, bs, D), dtype=np.float32) * std
+              for n in seq_lens]
+    q_vals = rng.standard_normal((S, Hq, D), dtype=np.float32) * std
+
+    # The newest token's K/V, rounded to the source dtype.
+    new_k_f = np.stack([k_vals[s][(int(n) - 1) // bs, :, (int(n) - 1) % bs, :]
+                        for s, n in enumerate(seq_lens)]) if S else np.zeros((0, H, D), np.float32)
+    new_v_f = np.stack([v_vals[s][(int(n) - 1) // bs, :, (int(n) - 1) % bs, :]
+                        for s, n in enumerate(seq_lens)]) if S else np.zeros((0, H, D), np.float32)
+    new_k = to_bits(new_k_f, src_dt)
+    new_v = to_bits(new_v_f, src_dt)
+
+    k_scale = v_scale = 1.0
+    if spec.per_tensor_fp8_scale:
+        # Per-tensor scale: largest magnitude of the valid cache contents / 448.
+        def amax(vals, new_bits):
+            m = 0.0
+            for s, n in enumerate(seq_lens):
+                flat = vals[s].transpose(1, 0, 2, 3).reshape(H, -1, D)[:, : int(n) - 1, :]
+                if flat.size:
+                    m = max(m, float(np.abs(flat).max()))
+            from_new = np.abs(bits_to_torch(new_bits, src_dt).float().numpy()).max() if S else 0.0
+            return max(m, float(from_new))
+        k_scale = float(np.float32(amax(k_vals, new_k) / FP8_MAX))
+        v_scale = float(np.float32(amax(v_vals, new_v) / FP8_MAX))
+
+    nan = NAN_BITS[cache_dt]
+    k_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[cache_dt])
+    v_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[cache_dt])
+    for s, n in enumerate(seq_lens):
+        n = int(n)
+        ids = np.asarray(tables[s], dtype=np.int64)
+        for vals, pool, sc in ((k_vals[s], k_pool, k_scale), (v_vals[s], v_pool, v_scale)):
+            stored = to_bits(vals / np.float32(sc) if cache_dt == "fp8_e4m3" else vals, cache_dt)
+            # poison every slot from the newest token on (the newest is written by the scatter)
+            flat = stored.transpose(1, 0, 2, 3).reshape(H, -1, D)
+            flat[:, n - 1:, :] = nan
+            pool[ids] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
+
+    block_tables = np.full((S, mb), poison_block, dtype=np.int32)
+    slot_mapping = np.zeros(S, dtype=np.int64)
+    for s, n in enumerate(seq_lens):
+        block_tables[s, : len(tables[s])] = tables[s]
+        pos = int(n) - 1
+        slot_mapping[s] = tables[s][pos // bs] * bs + pos % bs
+
+    return DecodeCase(spec=spec, q=to_bits(q_vals, q_dt), k_pool=k_pool, v_pool=v_pool,
+                      block_tables=block_tables, seq_lens=seq_lens.astype(np.int32),
+                      new_k=new_k, new_v=new_v, src_dtype=src_dt, slot_mapping=slot_mapping,
+                      k_scale=k_scale, v_scale=v_scale, poison_block=poison_block)
+
+
+# ---------------------------------------------------------------------------
+# Mixed chunked-prefill + decode step with a shared, copy-on-write prefix
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MixedSpec:
+    name: str = "mixed_prefix_bf16"
+    num_forks: int = 16
+    prefix_len: int = 1024
+    chunk_len: int = 512
+    num_decode: int = 112
+    decode_lens: tuple = (256, 4096)
+    num_q_heads: int = 32
+    num_kv_heads: int = 8
+    head_dim: int = 128
+    block_size: int = 32
+    dtype: str = "bf16"
+    pool_factor: float = 1.1
+    description: str = ("16 sequences share a 1024-token prefix (ref-counted blocks) and each "
+                        "appends a 512-token causal chunk; 112 others decode one token at lens "
+                        "U[256,4096]; 32/8 heads, head_dim 128, block 32, bf16; copy-on-write "
+                        "of the first divergent block")
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+MIXED_SPEC = MixedSpec()
+
+
+@dataclass
+class MixedCase:
+    spec: MixedSpec
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    cow_pairs: np.ndarray            # int64 [P][2] (src, dst)
+    # scatter of every new token (chunk tokens first, then decode tokens)
+    new_k: np.ndarray                # bits [T][Hkv][D]
+    new_v: np.ndarray
+    slot_mapping: np.ndarray         # int64 [T]
+    # prefill chunk
+    q_chunk: np.ndarray              # bits [Tq][Hq][D]
+    query_start_loc: np.ndarray      # int32 [F+1]
+    prefill_tables: np.ndarray       # int32 [F][MBp] (after copy-on-write)
+    prefill_tables_shared: np.ndarray  # same tables before copy-on-write (all share the prefix)
+    prefill_lens: np.ndarray         # int32 [F]  (prefix + chunk)
+    # decode
+    q_decode: np.ndarray             # bits [Sd][Hq][D]
+    decode_tables: np.ndarray        # int32 [Sd][MBd]
+    decode_lens: np.ndarray          # int32 [Sd]
+    poison_block: int
+
+
+def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int | None = None,
+                    prefix_len: int | None = None, chunk_len: int | None = None,
+                    num_decode: int | None = None, decode_lens=None) -> MixedCase:
+    """Build the mixed step; the optional overrides shrink it for small parity cases."""
+    rng = _rng(spec.name, rep)
+    F = spec.num_forks if num_forks is None else num_forks
+    P = spec.prefix_len if prefix_len is None else prefix_len
+    C = spec.chunk_len if chunk_len is None else chunk_len
+    Sd = spec.num_decode if num_decode is None else num_decode
+    H, Hq, D, bs, dt = spec.num_kv_heads, spec.num_q_heads, spec.head_dim, spec.block_size, spec.dtype
+    if decode_lens is None:
+        dlens = rng.integers(spec.decode_lens[0], spec.decode_lens[1] + 1, size=Sd).astype(np.int64)
+    else:
+        dlens = np.asarray(decode_lens, dtype=np.int64)
+        Sd = len(dlens)
+
+    prefix_blocks = blocks_for(P, bs)
+    chunk_blocks = blocks_for(P + C, bs) - prefix_blocks
+    decode_blocks = sum(blocks_for(int(n), bs) for n in dlens)
+    demand = prefix_blocks + F * chunk_blocks + max(F - 1, 0) + decode_blocks
+    nb = int(math.ceil(spec.pool_factor * demand)) + 1
+    mgr = BlockManager(nb, bs, order=rng.permutation(nb))
+
+    # Shared prefix: one sequence allocates it, the others fork it.
+    base = mgr.allocate(P)
+    prefix_ids = list(base[:prefix_blocks])          # before any fork remaps its table
+    forks = [base] + [mgr.fork(base) for _ in range(F - 1)]
+    # Each fork appends its chunk.
+    for t in forks:
+        mgr.grow(t, P + C)
+    shared_tables = [list(t) for t in forks]
+    # Copy-on-write of the first divergent block.  The prefix is block-aligned
+    # here, so no chunk token lands in a shared block; the last prefix block is
+    # taken as the first divergent one so that the copy happens.
+    cow_pairs = []
+    if prefix_blocks > 0:
+        for t in forks:
+            pair = mgr.copy_on_write(t, prefix_blocks - 1)
+            if pair is not None:
+                cow_pairs.append(pair)
+    dec_tables = [mgr.allocate(int(n)) for n in dlens]
+    poison_block = mgr._take()
+
+    nan = NAN_BITS[dt]
+    k_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[dt])
+    v_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[dt])
+
+    def fill(pool, ids, ntok):
+        vals = rng.standard_normal((len(ids), H, bs, D), dtype=np.float32)
+        bits = to_bits(vals, dt)
+        flat = bits.transpose(1, 0, 2, 3).reshape(H, -1, D)
+        flat[:, ntok:, :] = nan
+        pool[np.asarray(ids, dtype=np.int64)] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
+
+    # prefix contents (the chunk's own K/V come through the scatter)
+    fill(k_pool, prefix_ids, P)
+    fill(v_pool, prefix_ids, P)
+    # decode sequences: everything but the newest token
+    for t, n in zip(dec_tables, dlens):
+        fill(k_pool, t, int(n) - 1)
+        fill(v_pool, t, int(n) - 1)
+
+    # New tokens: F*C chunk tokens then Sd decode tokens.
+    T = F * C + Sd
+    new_k = to_bits(rng.standard_normal((T, H, D), dtype=np.float32), dt)
+    new_v = to_bits(rng.standard_normal((T, H, D), dtype=np.float32), dt)
+    slot_mapping = np.zeros(T, dtype=np.int64)
+    for f, t in enumerate(forks):
+        for i in range(C):
+            pos = P + i
+            slot_mapping[f * C + i] = t[pos // bs] * bs + pos % bs
+    for d, (t, n) in enumerate(zip(dec_tables, dlens)):
+        pos = int(n) - 1
+        slot_mapping[F * C + d] = t[pos // bs] * bs + pos % bs
+
+    mbp = blocks_for(P + C, bs)
+    prefill_tables = np.full((F, max(mbp, 1)), poison_block, dtype=np.int32)
+    prefill_shared = np.full((F, max(mbp, 1)), poison_block, dtype=np.int32)
+    for f in range(F):
+        prefill_tables[f, : len(forks[f])] = forks[f]
+        prefill_shared[f, : len(shared_tables[f])] = shared_tables[f]
+    mbd = max(blocks_for(spec.decode_lens[1], bs), max((len(t) for t in dec_tables), default=1))
+    decode_tables = np.full((Sd, mbd), poison_block, dtype=np.int32)
+    for d, t in enumerate(dec_tables):
+        decode_tables[d, : len(t)] = t
+
+    q_chunk = to_bits(rng.standard_normal((F * C, Hq, D), dtype=np.float32), dt)
+    q_decode = to_bits(rng.standard_normal((Sd, Hq, D), dtype=np.float32), dt)
+    qsl = (np.arange(F + 1, dtype=np.int64) * C).astype(np.int32)
+    return MixedCase(spec=spec, k_pool=k_pool, v_pool=v_pool,
+                     cow_pairs=np.asarray(cow_pairs, dtype=np.int64).reshape(-1, 2),
+                     new_k=new_k, new_v=new_v, slot_mapping=slot_mapping,
+                     q_chunk=q_chunk, query_start_loc=qsl, prefill_tables=prefill_tables,
+                     prefill_tables_shared=prefill_shared,
+                     prefill_lens=np.full(F, P + C, dtype=np.int32),
+                     q_decode=q_decode, decode_tables=decode_tables,
+                     decode_lens=dlens.astype(np.int32), poison_block=poison_block)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting used by the benchmark
+# ---------------------------------------------------------------------------
+
+def effective_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int, cache_dtype: str) -> int:
+    """K and V bytes a decode step must read: sum_s len_s * Hkv * D * (eb_K + eb_V).
+
+    For a Llama-2-7B-shaped fp16 layer (32 KV heads, head_dim 128) this is
+    16 KiB per token, the per-layer figure the ybb.press page gives in §一.
+    """
+    eb = ELEM_BYTES[cache_dtype]
+    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * num_kv_heads * head_dim * 2 * eb
