@@ -1,0 +1,238 @@
+/*
+ * pa.h — C ABI of the paged KV-cache attention library (libpa.so, gfx950).
+ *
+ * Each sequence's keys and values live in fixed-size physical blocks of one
+ * shared pool per tensor; a per-sequence block table maps the sequence's
+ * logical blocks to physical ones.  The calls below write new tokens into
+ * the pool, copy blocks for copy-on-write, and compute attention for decode
+ * tokens and for causal prefill chunks by resolving every block through the
+ * table.
+ *
+ * Pages this interface follows (by title):
+ *   [bogosort]  "五十三：vLLM-PagedAttention" (book.bogosort.top, lesson 53)
+ *   [datawhale] "17. vLLM PagedAttention | 经典推理框架: 模拟 Continuous
+ *               Batching 与 PagedAttention" (datawhalechina llm-algo-leetcode)
+ *   [ybb]       "vLLM 与 LLM 推理部署实战：从 PagedAttention 到生产级服务架构"
+ *   [intelli]   "vLLM与PagedAttention：大模型推理内存优化技术解析"
+ *   [aieng]     "推理引擎内部机制——PagedAttention、连续批处理、分块预填充"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pools.  k_pool and v_pool are separate dense arrays laid out
+ *   [num_blocks][num_kv_heads][block_size][head_dim]   (row-major)
+ *   so one (block, KV head) tile of block_size x head_dim elements is
+ *   contiguous.  A token's slot is physical_block * block_size + offset.
+ * Element types (pa_dtype): f32, f16, bf16 and OCP fp8 E4M3FN (cache only).
+ *   Supported (q, cache) pairs: (f32,f32) (f16,f16) (bf16,bf16) (bf16,fp8)
+ *   (f16,fp8).  Outputs have the query's type.  For an fp8 cache the stored
+ *   code times the per-tensor k_scale / v_scale is the value; the scales are
+ *   applied the same way for other cache types (pass 1.0f).
+ * Shapes.  head_dim is 64 or 128; block_size is 16 or 32; num_q_heads is a
+ *   multiple of num_kv_heads with at most 16 query heads per KV head.  Query
+ *   head h uses KV head h / (num_q_heads / num_kv_heads).
+ * Memory.  Every pointer is device memory owned by the caller, dense, and
+ *   16-byte aligned (block tables, lengths and slot arrays: 4-byte aligned).
+ *   The library allocates nothing, keeps no per-call state and never
+ *   synchronises: each call only enqueues work on `stream` (a hipStream_t;
+ *   NULL = the null stream) and returns.  Results are stream-ordered.
+ * Errors.  Arguments are checked on the host before anything is enqueued; a
+ *   failed check returns a non-zero pa_status and enqueues nothing.  Launch
+ *   failures return PA_ERR_HIP.  pa_last_error() gives a message for the
+ *   last failure on the calling thread.  Device-resident contents (block
+ *   ids, slots, lengths, chunk offsets) are trusted: the kernels clamp
+ *   lengths to the table width, but a block id outside the pool is
+ *   undefined behaviour.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_F16 = 1,
+  PA_DTYPE_BF16 = 2,
+  PA_DTYPE_FP8_E4M3 = 3
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, ... */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not implemented: dtype pair, shape */
+  PA_ERR_WORKSPACE = 3,   /* split decode needs a larger workspace */
+  PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} pa_status;
+
+/*
+ * pa_reshape_and_cache — write new tokens' K/V into their pool slots.
+ *
+ * [datawhale] Step 3 item 3 and Step 4: physical blocks are handed out on
+ * demand as tokens are generated and each token's K/V is stored in its
+ * block; [bogosort] §8: the block table maps logical to physical blocks.
+ * For token t with slot_mapping[t] >= 0, for every KV head h:
+ *   k_pool[slot / block_size][h][slot % block_size][:] = key[t][h][:]
+ * and the same for value / v_pool.  A negative slot skips the token.
+ * If cache_dtype == src_dtype the bits are copied unchanged.  For an fp8
+ * cache ([ybb] §6.2, KV cache in FP8) each element is stored as
+ * e4m3(float32(x) / k_scale) (v_scale for V): one correctly rounded float32
+ * division, round-to-nearest-even, magnitudes above 448 (and infinities)
+ * saturate to 448, NaN stays NaN.
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim], src_dtype; row t
+ *                 starts at key + t * key_token_stride elements
+ *                 (0 = dense, num_kv_heads * head_dim); same for value.
+ *   k_pool,v_pool [num_blocks][num_kv_heads][block_size][head_dim], cache_dtype
+ *   slot_mapping  int64 [num_tokens]; slots must be distinct and
+ *                 < num_blocks * block_size.
+ * src_dtype must equal cache_dtype, or cache_dtype is fp8 and src_dtype is
+ * bf16/f16/f32.  num_tokens == 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
+                               float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_copy_blocks — copy whole blocks for copy-on-write.
+ *
+ * [ybb] §2.2 Copy-on-Write: when several sequences reference one block, a
+ * write to it first duplicates the whole block.  For each pair p,
+ *   block block_pairs[2p+1] of k_pool and of v_pool becomes a copy of block
+ *   block_pairs[2p].
+ * block_bytes is the size of one block of one pool
+ * (num_kv_heads * block_size * head_dim * element bytes); it must be a
+ * multiple of 16.  block_pairs is int64 [num_pairs][2] (src, dst) in device
+ * memory.  Destinations must be distinct and never a source in the same
+ * call.  num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs, int32_t num_pairs,
+                         int64_t block_bytes, void* stream);
+
+/*
+ * Split-KV planning for decode.  A sequence's context is cut into
+ * partitions of partition_size tokens; one workgroup handles one
+ * (sequence, KV head, partition) and, when a sequence has more than one
+ * partition, a log-sum-exp reduce merges the partial results.
+ *
+ * pa_decode_partition_size resolves a requested partition size:
+ *   > 0 : used as given (must be a multiple of 32 and of block_size);
+ *   0   : the library picks one from the batch shape;
+ *   -1  : never split (one partition covers max_seq_len).
+ * It returns the resolved size in tokens (>= max_seq_len means no split),
+ * or a negative value for an invalid request.
+ *
+ * pa_decode_workspace_bytes returns the workspace pa_decode needs for that
+ * plan (0 when nothing is split).  max_seq_len is an upper bound on every
+ * seq_lens[s] (0 = max_blocks_per_seq * block_size).
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                 int32_t max_seq_len, int32_t partition_size);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode — attention of one query token per sequence over its paged
+ * context.
+ *
+ * [bogosort] §8: the attention kernel finds a sequence's past K/V through
+ * the block table; [ybb] §2.3: attention walks every K/V pair, jumping to
+ * each block through the table; [datawhale] Step 2: the blocks named by the
+ * table, in table order and cut to seq_len tokens, form the sequence's
+ * cache.  For sequence s with n = seq_lens[s] (the new token included; its
+ * K/V must already be in the pool) and query head h, kv = h / group:
+ *   logit_j = scale * k_scale * (q[s][h] . Kcode[j])   for j < n
+ *   out[s][h] = v_scale * sum_j softmax(logit)_j * Vcode[j]
+ * Accumulation is float32; probabilities enter the value product in the
+ * query's 16-bit type (f32 queries stay f32).  n <= 0 gives a zero output.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim], q_dtype (written)
+ *   q              [num_seqs][num_q_heads][head_dim], q_dtype
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; entries at or past
+ *                  ceil(n / block_size) are never read
+ *   seq_lens       int32 [num_seqs]; each <= max_seq_len and
+ *                  <= max_blocks_per_seq * block_size (clamped otherwise)
+ *   max_seq_len    upper bound used to size the split grid (0 = table width)
+ *   partition_size see pa_decode_partition_size
+ *   workspace      >= pa_decode_workspace_bytes(...) bytes of device memory,
+ *                  256-byte aligned (may be NULL when that is 0)
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                    int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
+                    float v_scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * The two stages of pa_decode, for callers that time or schedule them
+ * separately.  pa_decode_attention runs the per-(sequence, KV head,
+ * partition) kernel: sequences with a single partition get their final
+ * output in `out`, the others get partial results in `workspace`.
+ * pa_decode_reduce then merges the partials of multi-partition sequences
+ * into `out` (a no-op plan when nothing is split).  Both take exactly the
+ * arguments of pa_decode; calling them in order on one stream equals one
+ * pa_decode call.
+ */
+pa_status pa_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                              float k_scale, float v_scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_reduce(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                           int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_chunk — causal attention of one prefill chunk per sequence
+ * over its paged context.
+ *
+ * [bogosort] §15 Chunked Prefill and [aieng] "分块预填充保护 TTFT 尾部": a long
+ * prompt is prefilled in consecutive chunks (about 512 tokens) interleaved
+ * with decode.  Sequence s has seq_lens[s] = n context tokens, whose last
+ * L = query_start_loc[s+1] - query_start_loc[s] tokens are this chunk; the
+ * chunk's own K/V must already be in the pool (pa_reshape_and_cache).
+ * Chunk query i sits at position n - L + i and attends keys 0 .. n - L + i
+ * (causal, aligned to the end of the context).  Requires n >= L.
+ *
+ *   out, q          [total_q_tokens][num_q_heads][head_dim], q_dtype; the
+ *                   chunk of sequence s is rows query_start_loc[s] ..
+ *                   query_start_loc[s+1] - 1
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, last = total
+ *   max_q_len       >= every chunk length (sizes the grid)
+ * Supported: q/cache bf16 or f16 (same type), num_q_heads / num_kv_heads a
+ * power of two <= 16.
+ */
+pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
+                           const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                           const int32_t* seq_lens, float scale, int32_t block_size,
+                           int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/* Detail message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,232 @@
+"""Python binding of libpa.so — paged KV-cache attention on gfx950.
+
+The functions here carry the C entry points' names and only marshal
+arguments: torch tensors become device pointers, the current torch stream
+becomes the hipStream_t, and a non-zero status becomes an exception.  Every
+step of the computation runs in the library's HIP kernels; there is no other
+code path.  Importing this module loads the shared library and fails loudly
+if it has not been built (``python paged_kv_cache_415_amd/build.py``).
+
+Tensor layouts (all contiguous, on the GPU):
+  q, out            [num_seqs or tokens][num_q_heads][head_dim]
+  k_pool, v_pool    [num_blocks][num_kv_heads][block_size][head_dim]
+  block_tables      int32 [num_seqs][max_blocks_per_seq]
+  seq_lens          int32 [num_seqs]
+  slot_mapping      int64 [num_tokens]
+  block_pairs       int64 [num_pairs][2]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_DTYPE = {
+    torch.float32: 0,
+    torch.float16: 1,
+    torch.bfloat16: 2,
+    torch.float8_e4m3fn: 3,
+}
+STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
+          4: "PA_ERR_HIP"}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python paged_kv_cache_415_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32,
+                                         i32, f32, f32, vp]
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i64, vp]
+    lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.pa_decode_partition_size.restype = i32
+    lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_bytes.restype = sz
+    dec = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32, i32,
+           vp, sz, vp]
+    for name in ("pa_decode", "pa_decode_attention", "pa_decode_reduce"):
+        getattr(lib, name).argtypes = dec
+        getattr(lib, name).restype = i32
+    lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, i32, i32, f32, f32, vp]
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.pa_probe_copy.argtypes = [vp, vp, sz, vp]
+    for name in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_prefill_chunk", "pa_probe_read",
+                 "pa_probe_copy"):
+        getattr(lib, name).restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PagedAttentionError(status, _lib.pa_last_error().decode())
+
+
+def _ptr(t, contiguous: bool = True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    return t.data_ptr()
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype in (torch.uint8,):          # raw fp8 codes
+        return 3
+    try:
+        return PA_DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, k_scale: float = 1.0,
+                         v_scale: float = 1.0, stream=None) -> None:
+    """Scatter key/value [T][Hkv][D] into pool slots (see pa.h)."""
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    nb, hkv, bs, d = k_pool.shape
+    t = slot_mapping.shape[0]
+    for x in (key, value):      # token rows may be strided (e.g. views into a fused QKV buffer)
+        if x.dim() != 3 or x.shape[1:] != (hkv, d) or x.stride(2) != 1 or x.stride(1) != d:
+            raise ValueError("key/value must be [T][num_kv_heads][head_dim] with dense rows")
+    key_stride = key.stride(0) if t > 0 else 0
+    value_stride = value.stride(0) if t > 0 else 0
+    _check(_lib.pa_reshape_and_cache(_ptr(key, False), _ptr(value, False), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(slot_mapping), t, key_stride, value_stride, nb, hkv, d,
+                                     bs, _dtype(key), _dtype(k_pool), k_scale, v_scale,
+                                     _stream(stream)))
+
+
+def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
+    """Copy whole blocks (src, dst) pairs in both pools (see pa.h)."""
+    if block_pairs.dtype != torch.int64:
+        raise TypeError("block_pairs must be int64")
+    block_bytes = k_pool[0].numel() * k_pool.element_size()
+    _check(_lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(block_pairs),
+                               block_pairs.shape[0], block_bytes, _stream(stream)))
+
+
+def pa_decode_partition_size(num_seqs: int, num_kv_heads: int, block_size: int, max_seq_len: int,
+                             partition_size: int = 0) -> int:
+    return _lib.pa_decode_partition_size(num_seqs, num_kv_heads, block_size, max_seq_len,
+                                         partition_size)
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                              block_size: int, max_seq_len: int, partition_size: int = 0) -> int:
+    return _lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                          max_seq_len, partition_size)
+
+
+def decode_workspace(q, k_pool, max_seq_len: int, partition_size: int = 0):
+    """Allocate a workspace tensor for pa_decode (torch caching allocator)."""
+    s, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    n = pa_decode_workspace_bytes(s, hq, hkv, d, bs, max_seq_len, partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def _decode_call(fn, out, q, k_pool, v_pool, block_tables, seq_lens, scale, max_seq_len,
+                 k_scale, v_scale, partition_size, workspace, stream):
+    s, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens),
+              float(scale), bs, s, hq, hkv, d, block_tables.shape[1], int(max_seq_len),
+              _dtype(q), _dtype(k_pool), float(k_scale), float(v_scale), int(partition_size),
+              _ptr(workspace), wbytes, _stream(stream)))
+
+
+def pa_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int = 0,
+              k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+              workspace=None, stream=None) -> None:
+    """Decode attention of one query per sequence over its paged context (see pa.h)."""
+    _decode_call(_lib.pa_decode, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                 max_seq_len, k_scale, v_scale, partition_size, workspace, stream)
+
+
+def pa_decode_attention(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                        max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                        partition_size: int = 0, workspace=None, stream=None) -> None:
+    """First stage of pa_decode (attention kernel only)."""
+    _decode_call(_lib.pa_decode_attention, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                 max_seq_len, k_scale, v_scale, partition_size, workspace, stream)
+
+
+def pa_decode_reduce(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                     max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                     partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Second stage of pa_decode (log-sum-exp merge of split partials)."""
+    _decode_call(_lib.pa_decode_reduce, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                 max_seq_len, k_scale, v_scale, partition_size, workspace, stream)
+
+
+def pa_prefill_chunk(out, q, query_start_loc, k_pool, v_pool, block_tables, seq_lens,
+                     scale: float, max_q_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                     stream=None) -> None:
+    """Causal attention of one chunk per sequence over its paged context (see pa.h)."""
+    t, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    num_seqs = query_start_loc.shape[0] - 1
+    _check(_lib.pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(query_start_loc), _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), float(scale),
+                                 bs, num_seqs, t, int(max_q_len), hq, hkv, d,
+                                 block_tables.shape[1], _dtype(q), _dtype(k_pool),
+                                 float(k_scale), float(v_scale), _stream(stream)))
+
+
+def pa_probe_read(src, sink, stream=None) -> None:
+    _check(_lib.pa_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                              _stream(stream)))
+
+
+def pa_probe_copy(dst, src, stream=None) -> None:
+    _check(_lib.pa_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                              _stream(stream)))
+
+
+__all__ = [
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_attention",
+    "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",
+    "pa_decode_workspace_bytes", "decode_workspace", "pa_probe_read", "pa_probe_copy",
+    "PagedAttentionError", "library", "LIB_PATH",
+]

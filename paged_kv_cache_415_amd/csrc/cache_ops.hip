@@ -1,0 +1,163 @@
+// Slot scatter (reshape_and_cache), whole-block copy (copy-on-write) and
+// the HBM probe kernels.
+//
+// The scatter follows the datawhalechina page "17. vLLM PagedAttention"
+// (Step 3 item 3 / Step 4: each generated token's K/V goes into the
+// physical block handed out for it) with the slot linearisation
+// physical * block_size + offset.  The block copy follows the ybb.press page
+// "vLLM 与 LLM 推理部署实战" §2.2 (a write to a shared block duplicates the
+// whole block first).  Both are pure data movement: one 16-byte load and one
+// store per thread, coalesced along head_dim.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+// One workgroup per token; threads walk the token's Hkv * D elements in
+// 16-byte source vectors.  Same-type copy.
+template <typename ElemBytesTag>
+__global__ __launch_bounds__(256) void scatter_copy_kernel(ScatterParams p) {
+  const int t = blockIdx.x;
+  const int64_t slot = p.slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / p.block_size;
+  const int row = (int)(slot - blk * p.block_size);
+  const int eb = p.src_elem_bytes;
+  const int vec_per_head = p.head_dim * eb / 16;
+  const int nvec = p.num_kv_heads * vec_per_head;
+  const char* ksrc = (const char*)p.key + (int64_t)t * p.key_stride * eb;
+  const char* vsrc = (const char*)p.value + (int64_t)t * p.value_stride * eb;
+  for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+    const int h = i / vec_per_head;
+    const int c = i - h * vec_per_head;
+    const int64_t dst = (((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim) * eb + c * 16;
+    const int64_t src = (int64_t)h * p.head_dim * eb + c * 16;
+    st16((char*)p.k_pool + dst, ld16(ksrc + src));
+    st16((char*)p.v_pool + dst, ld16(vsrc + src));
+  }
+}
+
+template <typename SrcT>
+__device__ __forceinline__ float src_elem(const char* base, int i) {
+  return (float)reinterpret_cast<const SrcT*>(base)[i];
+}
+
+// Quantising scatter into an fp8 E4M3 pool: each thread turns 16 source
+// elements into 16 codes (one 16-byte store).
+template <typename SrcT>
+__global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterParams p) {
+  const int t = blockIdx.x;
+  const int64_t slot = p.slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / p.block_size;
+  const int row = (int)(slot - blk * p.block_size);
+  const int groups_per_head = p.head_dim / 16;
+  const int ngroups = p.num_kv_heads * groups_per_head;
+  const SrcT* ksrc = reinterpret_cast<const SrcT*>(p.key) + (int64_t)t * p.key_stride;
+  const SrcT* vsrc = reinterpret_cast<const SrcT*>(p.value) + (int64_t)t * p.value_stride;
+  for (int i = threadIdx.x; i < ngroups; i += blockDim.x) {
+    const int h = i / groups_per_head;
+    const int c = i - h * groups_per_head;
+    const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 16;
+    const int64_t src = (int64_t)h * p.head_dim + c * 16;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const SrcT* s = which ? vsrc : ksrc;
+      const float scale = which ? p.v_scale : p.k_scale;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float x = (float)s[src + q * 4 + b];
+          acc |= e4m3_encode(x / scale) << (8 * b);   // correctly rounded fp32 divide
+        }
+        w[q] = acc;
+      }
+      u32x4 v = {w[0], w[1], w[2], w[3]};
+      st16((char*)(which ? p.v_pool : p.k_pool) + dst, v);
+    }
+  }
+}
+
+// One workgroup per (pair, chunk of the block); K and V pools both copied.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
+  const int pair = blockIdx.y;
+  const int64_t src = p.pairs[2 * pair];
+  const int64_t dst = p.pairs[2 * pair + 1];
+  const int64_t nvec = p.block_bytes / 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t so = src * p.block_bytes + i * 16;
+    const int64_t d = dst * p.block_bytes + i * 16;
+    st16((char*)p.k_pool + d, ld16((const char*)p.k_pool + so));
+    st16((char*)p.v_pool + d, ld16((const char*)p.v_pool + so));
+  }
+}
+
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream) {
+  if (p.num_tokens == 0) return hipSuccess;
+  dim3 grid(p.num_tokens), block(256);
+  if (p.cache_dtype == p.src_dtype) {
+    hipLaunchKernelGGL(scatter_copy_kernel<void>, grid, block, 0, stream, p);
+  } else if (p.src_dtype == kBF16) {
+    hipLaunchKernelGGL(scatter_fp8_kernel<__bf16>, grid, block, 0, stream, p);
+  } else if (p.src_dtype == kF16) {
+    hipLaunchKernelGGL(scatter_fp8_kernel<_Float16>, grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(scatter_fp8_kernel<float>, grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
+  if (p.num_pairs == 0) return hipSuccess;
+  const int64_t nvec = p.block_bytes / 16;
+  int chunks = (int)((nvec + 255) / 256);
+  if (chunks > 64) chunks = 64;
+  dim3 grid(chunks, p.num_pairs), block(256);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- probes
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* src, int64_t nvec, u32x4* sink) {
+  u32x4 acc = {0, 0, 0, 0};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    acc ^= src[i];
+  }
+  // fold the wave's values so the loads stay live; one store per workgroup
+  for (int m = 32; m >= 1; m >>= 1) {
+    acc.x ^= __shfl_xor(acc.x, m, 64);
+    acc.y ^= __shfl_xor(acc.y, m, 64);
+    acc.z ^= __shfl_xor(acc.z, m, 64);
+    acc.w ^= __shfl_xor(acc.w, m, 64);
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void probe_copy_kernel(u32x4* dst, const u32x4* src, int64_t nvec) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    dst[i] = src[i];
+  }
+}
+
+hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, hipStream_t stream) {
+  const int64_t nvec = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeBlocks), dim3(256), 0, stream,
+                     (const u32x4*)src, nvec, (u32x4*)sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  const int64_t nvec = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(probe_copy_kernel, dim3(kProbeBlocks), dim3(256), 0, stream, (u32x4*)dst,
+                     (const u32x4*)src, nvec);
+  return hipGetLastError();
+}
+
+}  // namespace pa

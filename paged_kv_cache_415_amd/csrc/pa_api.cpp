@@ -1,0 +1,424 @@
+// Host side of the C ABI (include/pa.h): argument checks, split planning and
+// kernel dispatch.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pa.h"
+#include "../../include/pa_probe.h"
+#include "pa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+pa_status ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case PA_DTYPE_F32: return 4;
+    case PA_DTYPE_F16: return 2;
+    case PA_DTYPE_BF16: return 2;
+    case PA_DTYPE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape / type checks shared by decode and prefill.
+pa_status check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int max_blocks, pa_dtype q_dtype, pa_dtype cache_dtype) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "head counts and max_blocks_per_seq must be positive");
+  if (num_q_heads % num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "too many KV heads");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
+  if (elem_bytes(q_dtype) == 0 || elem_bytes(cache_dtype) == 0)
+    return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
+  const bool same = q_dtype == cache_dtype && q_dtype != PA_DTYPE_FP8_E4M3;
+  const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3 &&
+                   (q_dtype == PA_DTYPE_BF16 || q_dtype == PA_DTYPE_F16);
+  if (!same && !fp8) return fail(PA_ERR_UNSUPPORTED, "unsupported (q, cache) dtype pair");
+  return PA_OK;
+}
+
+struct Plan {
+  int partition;
+  int max_parts;
+  int max_len;
+  size_t workspace;
+};
+
+int auto_partition(int num_seqs, int num_kv_heads, int max_len) {
+  // Enough workgroups to keep 256 CUs busy several times over without
+  // writing many partials: split only when the unsplit grid is small
+  // relative to the machine or the contexts are long.
+  const long long unsplit = (long long)num_seqs * num_kv_heads;
+  if (max_len <= 512) return -1;
+  if (unsplit >= 4096 && max_len <= 1024) return -1;
+  return 512;
+}
+
+int resolve_partition(int num_seqs, int num_kv_heads, int block_size, int max_len, int request) {
+  if (request == 0) request = auto_partition(num_seqs, num_kv_heads, max_len);
+  if (request == -1) {
+    int p = max_len < 32 ? 32 : max_len;
+    p = (p + 31) / 32 * 32;                       // whole 32-token steps
+    p = (p + block_size - 1) / block_size * block_size;
+    return p;
+  }
+  if (request < 0 || request % 32 || request % block_size) return -1;
+  return request;
+}
+
+size_t workspace_for(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+  if (max_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  const size_t o = rows * head_dim * sizeof(float);
+  const size_t ml = rows * sizeof(float);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return up(o) + 2 * up(ml);
+}
+
+pa_status plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks, int max_seq_len, int partition_size,
+                      Plan* plan) {
+  const long long cap = (long long)max_blocks * block_size;
+  if (cap > (1 << 30)) return fail(PA_ERR_UNSUPPORTED, "block table too wide");
+  if (max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len < 0");
+  int max_len = (max_seq_len == 0 || max_seq_len > cap) ? (int)cap : max_seq_len;
+  const int part = resolve_partition(num_seqs, num_kv_heads, block_size, max_len, partition_size);
+  if (part <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "partition_size %d: use 0, -1 or a positive multiple of 32 and of block_size",
+                partition_size);
+  plan->partition = part;
+  plan->max_len = max_len;
+  plan->max_parts = (max_len + part - 1) / part;
+  if (plan->max_parts < 1) plan->max_parts = 1;
+  plan->workspace = workspace_for(num_seqs, num_q_heads, head_dim, plan->max_parts);
+  // LDS of one workgroup: its block-table slice plus the four waves' states.
+  const size_t ntab = (size_t)(part + block_size - 1) / block_size;
+  const size_t lds = (ntab * 4 + 15) / 16 * 16 + 2 * 4 * 16 * 4 +
+                     (size_t)4 * (num_q_heads / num_kv_heads) * head_dim * 4;
+  if (lds > 65536)
+    return fail(PA_ERR_UNSUPPORTED,
+                "partition of %d tokens needs %zu bytes of LDS; use a smaller partition_size",
+                part, lds);
+  return PA_OK;
+}
+
+enum class Stage { kBoth, kAttention, kReduce };
+
+pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                      float scale, int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
+                      float v_scale, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
+  pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, q_dtype, cache_dtype);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, "scale, k_scale and v_scale must be finite");
+  Plan plan;
+  st = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   max_seq_len, partition_size, &plan);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer (tensors need 16 bytes, int arrays 4)");
+  if (plan.workspace > 0) {
+    if (!workspace || workspace_bytes < plan.workspace)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace,
+                  workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  }
+  if (plan.max_parts > 0x7FFFFFFF / 2) return fail(PA_ERR_UNSUPPORTED, "too many partitions");
+
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  if (plan.workspace > 0) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * plan.max_parts;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* ws = static_cast<char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_m = reinterpret_cast<float*>(ws + up(rows * head_dim * sizeof(float)));
+    p.part_l = reinterpret_cast<float*>(ws + up(rows * head_dim * sizeof(float)) + up(rows * sizeof(float)));
+  }
+  p.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
+  p.v_scale = v_scale;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_len = plan.max_len;
+  p.partition = plan.partition;
+  p.max_parts = plan.max_parts;
+  p.q_dtype = q_dtype;
+  p.cache_dtype = cache_dtype;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (stage != Stage::kReduce) {
+    hipError_t e = pa::launch_decode_attention(p, s);
+    if (e != hipSuccess) return hip_status(e, "decode attention launch");
+  }
+  if (stage != Stage::kAttention) {
+    hipError_t e = pa::launch_decode_reduce(p, s);
+    if (e != hipSuccess) return hip_status(e, "decode reduce launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
+                               float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or non-positive heads/block_size");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
+  const int seb = elem_bytes(src_dtype), ceb = elem_bytes(cache_dtype);
+  if (seb == 0 || ceb == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
+  const bool same = src_dtype == cache_dtype;
+  const bool quant = cache_dtype == PA_DTYPE_FP8_E4M3 && src_dtype != PA_DTYPE_FP8_E4M3;
+  if (!same && !quant) return fail(PA_ERR_UNSUPPORTED, "unsupported (src, cache) dtype pair");
+  if (quant && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0 && v_scale > 0))
+    return fail(PA_ERR_INVALID_ARG, "fp8 scales must be finite and positive");
+  const int64_t dense = (int64_t)num_kv_heads * head_dim;
+  if (key_token_stride == 0) key_token_stride = dense;
+  if (value_token_stride == 0) value_token_stride = dense;
+  if (key_token_stride < dense || value_token_stride < dense)
+    return fail(PA_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_dim");
+  if ((key_token_stride * seb) % 16 || (value_token_stride * seb) % 16)
+    return fail(PA_ERR_INVALID_ARG, "token strides must keep rows 16-byte aligned");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  pa::ScatterParams p{};
+  p.key = key;
+  p.value = value;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.slot_mapping = slot_mapping;
+  p.key_stride = key_token_stride;
+  p.value_stride = value_token_stride;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.src_dtype = src_dtype;
+  p.cache_dtype = cache_dtype;
+  p.src_elem_bytes = seb;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  return hip_status(pa::launch_scatter(p, static_cast<hipStream_t>(stream)), "scatter launch");
+}
+
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs, int32_t num_pairs,
+                         int64_t block_bytes, void* stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs < 0");
+  if (num_pairs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_pairs > 65535");
+  if (block_bytes <= 0 || block_bytes % 16)
+    return fail(PA_ERR_INVALID_ARG, "block_bytes must be a positive multiple of 16");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !block_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_pairs, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  pa::CopyParams p{};
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.pairs = block_pairs;
+  p.block_bytes = block_bytes;
+  p.num_pairs = num_pairs;
+  return hip_status(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "copy launch");
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                 int32_t max_seq_len, int32_t partition_size) {
+  if (max_seq_len <= 0 || (block_size != 16 && block_size != 32)) return -1;
+  return resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_seq_len <= 0) return 0;
+  const int part = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  if (part <= 0) return 0;
+  const int max_parts = (max_seq_len + part - 1) / part;
+  return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                    int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
+                    float v_scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_impl(Stage::kBoth, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                              float k_scale, float v_scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(Stage::kAttention, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_reduce(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                           int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_impl(Stage::kReduce, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
+                           const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                           const int32_t* seq_lens, float scale, int32_t block_size,
+                           int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, void* stream) {
+  if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
+  pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, q_dtype, cache_dtype);
+  if (st != PA_OK) return st;
+  if (cache_dtype != q_dtype || q_dtype == PA_DTYPE_F32)
+    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16/f16 queries with a cache of the same type");
+  const int group = num_q_heads / num_kv_heads;
+  if (group & (group - 1)) return fail(PA_ERR_UNSUPPORTED, "prefill needs a power-of-two group");
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, "scales must be finite");
+  if ((long long)max_blocks_per_seq * block_size > (1 << 30))
+    return fail(PA_ERR_UNSUPPORTED, "block table too wide");
+  if ((size_t)max_blocks_per_seq * 4 + 2 * 64 * (head_dim + 8) * 2 > 160 * 1024)
+    return fail(PA_ERR_UNSUPPORTED, "block table row does not fit in LDS");
+  if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !query_start_loc || !k_pool || !v_pool || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  const int qpos = 128 / group;
+  if ((max_q_len + qpos - 1) / qpos > 0x7FFFFFFF / 2) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  pa::PrefillParams p{};
+  p.out = out;
+  p.q = q;
+  p.query_start_loc = query_start_loc;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
+  p.v_scale = v_scale;
+  p.num_seqs = num_seqs;
+  p.total_q = total_q_tokens;
+  p.max_q_len = max_q_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.q_dtype = q_dtype;
+  return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+pa_status pa_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes % 16 || !aligned(src, 16) || !aligned(sink, 16))
+    return fail(PA_ERR_INVALID_ARG, "probe_read: null/misaligned pointer or size not /16");
+  return hip_status(pa::launch_probe_read(src, bytes, sink, static_cast<hipStream_t>(stream)),
+                    "probe launch");
+}
+
+pa_status pa_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!src || !dst || bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
+    return fail(PA_ERR_INVALID_ARG, "probe_copy: null/misaligned pointer or size not /16");
+  return hip_status(pa::launch_probe_copy(dst, src, bytes, static_cast<hipStream_t>(stream)),
+                    "probe launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal interface between the host-side C ABI (pa_api.cpp) and the
+// kernel translation units.  Parameters travel to the kernels by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Element-type codes; numerically equal to the public pa_dtype values.
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
+
+constexpr int kProbeBlocks = 2048;
+
+struct ScatterParams {
+  const void* key;
+  const void* value;
+  void* k_pool;
+  void* v_pool;
+  const int64_t* slot_mapping;
+  int64_t key_stride;    // elements between consecutive tokens of `key`
+  int64_t value_stride;
+  int num_tokens;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int src_dtype;
+  int cache_dtype;
+  int src_elem_bytes;
+  float k_scale;
+  float v_scale;
+};
+
+struct CopyParams {
+  void* k_pool;
+  void* v_pool;
+  const int64_t* pairs;
+  int64_t block_bytes;
+  int num_pairs;
+};
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int* block_tables;
+  const int* seq_lens;
+  float* part_o;       // [S][Hq][max_parts][D]
+  float* part_m;       // [S][Hq][max_parts]  running max (log2 domain)
+  float* part_l;       // [S][Hq][max_parts]  sum of exponentials
+  float qk_scale_log2; // scale * k_scale * log2(e)
+  float v_scale;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int head_dim;
+  int block_size;
+  int max_blocks;      // block-table row length
+  int max_len;         // clamp for seq_lens: min(max_seq_len, max_blocks * block_size)
+  int partition;       // tokens per partition
+  int max_parts;       // partitions in the grid
+  int q_dtype;
+  int cache_dtype;
+};
+
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const int* query_start_loc;
+  const void* k_pool;
+  const void* v_pool;
+  const int* block_tables;
+  const int* seq_lens;
+  float qk_scale_log2;
+  float v_scale;
+  int num_seqs;
+  int total_q;
+  int max_q_len;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int head_dim;
+  int block_size;
+  int max_blocks;
+  int q_dtype;
+};
+
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,180 @@
+"""GPU parity of pa_reshape_and_cache + pa_decode against the fp64 oracle.
+
+Tolerances (max-abs on outputs): 5e-3 for fp32 queries, 2e-2 for fp16 / bf16
+queries (including fp8 caches).  Scatter results must be byte-identical over
+the whole pool, NaN-poisoned slots included.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_cases import TOL, DecodeRun, as_f64, custom_spec, lib, max_abs, oracle_step, up, up_int
+
+pytestmark = pytest.mark.gpu
+
+FULL_CONFIGS = ["tiny_f32", "llama2_7b_mha_f16", "llama3_8b_gqa_bf16", "llama3_70b_fp8kv"]
+
+
+@pytest.fixture(scope="module")
+def full_cases():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            case = W.make_decode_case(name)
+            cache[name] = (case, oracle_step(case))
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", FULL_CONFIGS)
+def test_full_config_scatter_and_decode(name, full_cases):
+    """Every output of the full workload, in the launch configuration the bench uses."""
+    case, (ref, okp, ovp) = full_cases(name)
+    print(f"[decode parity] {name}: S={len(case.seq_lens)} tokens={int(case.seq_lens.sum())}",
+          flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    dt = case.spec.cache_dtype
+    assert np.array_equal(W.torch_to_bits(run.k_pool, dt), okp), "K pool differs after scatter"
+    assert np.array_equal(W.torch_to_bits(run.v_pool, dt), ovp), "V pool differs after scatter"
+    out = run.decode()
+    err = max_abs(out, ref)
+    print(f"[decode parity] {name}: max-abs {err:.3e}", flush=True)
+    assert err <= TOL[case.spec.q_dtype]
+
+
+@pytest.mark.parametrize("partition", [32, 64, 160, 512, -1])
+def test_split_sizes_agree(partition):
+    sub = W.make_decode_case("llama3_8b_gqa_bf16", lens=[1, 31, 32, 33, 200, 511, 512, 513, 2500])
+    sref, _, _ = oracle_step(sub)
+    run = DecodeRun(sub)
+    run.scatter()
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, sref) <= TOL["bf16"]
+
+
+def test_stages_equal_single_call():
+    case = W.make_decode_case("llama3_70b_fp8kv", lens=[5, 700, 1500, 3000])
+    run = DecodeRun(case)
+    run.scatter()
+    a = run.decode(partition_size=512)
+    b = run.decode(partition_size=512, stages=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bitwise_repeatable():
+    case = W.make_decode_case("llama3_8b_gqa_bf16", num_seqs=24)
+    run = DecodeRun(case)
+    run.scatter()
+    a = run.decode()
+    for _ in range(3):
+        assert torch.equal(run.decode().view(torch.int16), a.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_mha_f16", "llama3_70b_fp8kv"])
+def test_permuting_physical_blocks_is_bitwise_invisible(name):
+    case = W.make_decode_case(name, num_seqs=12)
+    run = DecodeRun(case)
+    run.scatter()
+    a = run.decode()
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(case.num_blocks)          # block b moves to perm[b]
+    kp = np.empty_like(case.k_pool)
+    vp = np.empty_like(case.v_pool)
+    kp[perm] = case.k_pool
+    vp[perm] = case.v_pool
+    moved = W.DecodeCase(**{**case.__dict__, "k_pool": kp, "v_pool": vp,
+                            "block_tables": perm[case.block_tables].astype(np.int32),
+                            "slot_mapping": perm[case.slot_mapping // case.spec.block_size]
+                            * case.spec.block_size + case.slot_mapping % case.spec.block_size,
+                            "poison_block": int(perm[case.poison_block])})
+    run2 = DecodeRun(moved)
+    run2.scatter()
+    b = run2.decode()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("q_dt,c_dt", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
+                                       ("bf16", "fp8_e4m3"), ("f16", "fp8_e4m3")])
+def test_length_one_returns_its_value_row(q_dt, c_dt):
+    spec = custom_spec(f"len1_{q_dt}_{c_dt}", 8, 2, 128, 16, q_dt, c_dt)
+    case = W.make_decode_case(spec, lens=[1, 1, 1])
+    if c_dt == "fp8_e4m3":
+        case.k_scale = case.v_scale = 1.0
+    ref, _, _ = oracle_step(case)
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode()
+    # p = 1 exactly, so the output is the stored value row rounded once to q's type
+    exp = torch.from_numpy(ref).to(out.dtype)
+    assert torch.equal(out.cpu().view(torch.int16 if q_dt != "f32" else torch.int32),
+                       exp.view(torch.int16 if q_dt != "f32" else torch.int32))
+
+
+@pytest.mark.parametrize("q_dt", ["bf16", "f16"])
+def test_fp8_every_code_decodes_exactly(q_dt):
+    """Length-1 sequences whose value rows hold every finite E4M3 code."""
+    spec = custom_spec(f"codes_{q_dt}", 1, 1, 128, 16, q_dt, "fp8_e4m3")
+    case = W.make_decode_case(spec, lens=[1, 1])
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] + [0, 0], np.uint8)
+    for s in range(2):
+        blk = case.block_tables[s, 0]
+        case.v_pool[blk, 0, 0, :] = codes[s * 128:(s + 1) * 128]
+        case.k_pool[blk, 0, 0, :] = 0          # logit 0: the single token gets p = 1
+    # scatter of the newest token is skipped so the planted rows stay
+    case.slot_mapping[:] = -1
+    case.k_scale = case.v_scale = 1.0
+    run = DecodeRun(case)
+    run.scatter()
+    out = as_f64(run.decode())
+    want = oracle.e4m3_value_table()[codes].reshape(2, 1, 128)
+    bad = np.nonzero(out != want)
+    assert bad[0].size == 0, f"codes decoded wrongly: {[(int(codes[s*128+d]), out[s,0,d]) for s,_,d in zip(*bad)][:8]}"
+
+
+def test_zero_length_sequence_gives_zeros():
+    case = W.make_decode_case("llama3_8b_gqa_bf16", lens=[40, 1, 17])
+    run = DecodeRun(case)
+    run.scatter()
+    run.lens = up_int(np.array([40, 0, 17], np.int32))
+    out = run.decode(partition_size=32)
+    ref, _, _ = oracle_step(case)
+    assert torch.count_nonzero(out[1]) == 0
+    assert max_abs(out[[0, 2]], ref[[0, 2]]) <= TOL["bf16"]
+
+
+SWEEP = [
+    # (q, cache, Hq, Hkv, D, bs)
+    ("bf16", "bf16", 8, 8, 128, 16),
+    ("bf16", "bf16", 16, 1, 128, 32),
+    ("bf16", "bf16", 6, 2, 64, 16),
+    ("f16", "f16", 32, 4, 64, 32),
+    ("f16", "f16", 4, 2, 128, 32),
+    ("bf16", "fp8_e4m3", 8, 1, 64, 16),
+    ("f16", "fp8_e4m3", 12, 3, 128, 32),
+    ("bf16", "fp8_e4m3", 64, 8, 128, 32),
+    ("f32", "f32", 4, 1, 128, 32),
+    ("f32", "f32", 5, 5, 64, 16),
+]
+LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 600, 1031]
+
+
+@pytest.mark.parametrize("q_dt,c_dt,hq,hkv,d,bs", SWEEP)
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_shape_sweep(q_dt, c_dt, hq, hkv, d, bs, partition):
+    if partition > 0 and partition % bs:
+        pytest.skip("partition must be a multiple of block_size")
+    spec = custom_spec(f"sweep_{q_dt}_{c_dt}_{hq}_{hkv}_{d}_{bs}", hq, hkv, d, bs, q_dt, c_dt)
+    case = W.make_decode_case(spec, lens=LENS)
+    ref, okp, ovp = oracle_step(case)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(run.k_pool, c_dt), okp)
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL[q_dt]

@@ -1,0 +1,155 @@
+"""GPU parity of pa_prefill_chunk and of the mixed chunked-prefill + decode
+step with a shared, copy-on-write prefix (tolerance 2e-2 max-abs)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_cases import TOL, as_f64, lib, max_abs, up, up_int
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype):
+    """Pool holding each sequence's whole context (chunk included) + packed queries."""
+    need = [-(-n // bs) for n in ctxs]
+    nb = sum(need) + 2
+    ids = rng.permutation(nb)
+    poison = int(ids[-1])
+    nan = W.NAN_BITS[dtype]
+    kp = np.full((nb, hkv, bs, d), nan, W.BITS_DTYPE[dtype])
+    vp = np.full((nb, hkv, bs, d), nan, W.BITS_DTYPE[dtype])
+    tables = np.full((len(ctxs), max(need)), poison, np.int32)
+    cur = 0
+    for s, n in enumerate(ctxs):
+        for b in range(need[s]):
+            tables[s, b] = ids[cur]
+            cur += 1
+        for pool in (kp, vp):
+            vals = W.to_bits(rng.standard_normal((need[s], hkv, bs, d)).astype(np.float32), dtype)
+            flat = vals.transpose(1, 0, 2, 3).reshape(hkv, -1, d)
+            flat[:, n:, :] = nan
+            pool[tables[s, :need[s]]] = flat.reshape(hkv, need[s], bs, d).transpose(1, 0, 2, 3)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = W.to_bits(rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32), dtype)
+    return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32)
+
+
+CASES = [
+    # (chunks, contexts, Hq, Hkv, D, bs, dtype)
+    ([5, 16, 1], [5, 40, 70], 4, 1, 128, 16, "bf16"),
+    ([33, 100], [33, 300], 8, 2, 128, 32, "bf16"),
+    ([64, 7], [200, 7], 32, 8, 128, 32, "bf16"),
+    ([130], [131], 16, 1, 128, 16, "f16"),
+    ([17, 50], [60, 99], 2, 2, 64, 16, "f16"),
+    ([40], [555], 8, 1, 64, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("chunks,ctxs,hq,hkv,d,bs,dtype", CASES)
+def test_prefill_matches_oracle(chunks, ctxs, hq, hkv, d, bs, dtype):
+    rng = np.random.default_rng(sum(chunks) + hq + d)
+    q, qsl, kp, vp, tables, lens = _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype)
+    scale = 1.0 / np.sqrt(d)
+    ref = oracle.prefill_chunk_attention(q, dtype, qsl, kp, vp, dtype, tables, lens, scale, bs, hkv)
+    gq = up(q, dtype)
+    out = torch.empty_like(gq)
+    lib().pa_prefill_chunk(out, gq, up_int(qsl), up(kp, dtype), up(vp, dtype), up_int(tables),
+                           up_int(lens), scale, max(chunks))
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= TOL[dtype]
+
+
+def test_prefill_last_row_matches_decode():
+    rng = np.random.default_rng(5)
+    chunks, ctxs = [9, 30], [100, 64]
+    q, qsl, kp, vp, tables, lens = _random_chunks(rng, chunks, ctxs, 8, 2, 128, 16, "bf16")
+    pa = lib()
+    gq = up(q, "bf16")
+    gk, gv, gt, gl = up(kp, "bf16"), up(vp, "bf16"), up_int(tables), up_int(lens)
+    out = torch.empty_like(gq)
+    pa.pa_prefill_chunk(out, gq, up_int(qsl), gk, gv, gt, gl, 0.1, 30)
+    last = gq[torch.tensor([8, 38], device=gq.device)].contiguous()
+    dec = torch.empty_like(last)
+    pa.pa_decode(dec, last, gk, gv, gt, gl, 0.1, max_seq_len=100, partition_size=-1)
+    torch.cuda.synchronize()
+    diff = np.abs(as_f64(out[[8, 38]]) - as_f64(dec)).max()
+    assert diff <= TOL["bf16"]
+
+
+def _mixed_step(case):
+    """Device: copy-on-write -> scatter -> prefill chunk + decode (one stream)."""
+    pa = lib()
+    s = case.spec
+    dt = s.dtype
+    kp, vp = up(case.k_pool, dt), up(case.v_pool, dt)
+    pa.pa_copy_blocks(kp, vp, up_int(case.cow_pairs))
+    pa.pa_reshape_and_cache(up(case.new_k, dt), up(case.new_v, dt), kp, vp, up_int(case.slot_mapping))
+    qc, qd = up(case.q_chunk, dt), up(case.q_decode, dt)
+    out_c, out_d = torch.empty_like(qc), torch.empty_like(qd)
+    pa.pa_prefill_chunk(out_c, qc, up_int(case.query_start_loc), kp, vp, up_int(case.prefill_tables),
+                        up_int(case.prefill_lens), s.scale, int(np.diff(case.query_start_loc).max()))
+    max_len = int(case.decode_lens.max())
+    ws = pa.decode_workspace(qd, kp, max_len)
+    pa.pa_decode(out_d, qd, kp, vp, up_int(case.decode_tables), up_int(case.decode_lens), s.scale,
+                 max_seq_len=max_len, workspace=ws)
+    torch.cuda.synchronize()
+    return out_c, out_d, kp, vp
+
+
+def _oracle_pools(case):
+    s = case.spec
+    kp, vp = oracle.copy_blocks(case.k_pool, case.v_pool, case.cow_pairs)
+    return oracle.reshape_and_cache(kp, vp, s.dtype, case.new_k, case.new_v, s.dtype,
+                                    case.slot_mapping, s.block_size)
+
+
+def test_mixed_step_small_full_compare():
+    case = W.make_mixed_case(num_forks=4, prefix_len=96, chunk_len=40, num_decode=5,
+                             decode_lens=[33, 64, 65, 300, 1000])
+    s = case.spec
+    out_c, out_d, kp, vp = _mixed_step(case)
+    okp, ovp = _oracle_pools(case)
+    assert np.array_equal(W.torch_to_bits(kp, s.dtype), okp)
+    assert np.array_equal(W.torch_to_bits(vp, s.dtype), ovp)
+    ref_c = oracle.prefill_chunk_attention(case.q_chunk, s.dtype, case.query_start_loc, okp, ovp,
+                                           s.dtype, case.prefill_tables, case.prefill_lens,
+                                           s.scale, s.block_size, s.num_kv_heads)
+    ref_d = oracle.decode_attention(case.q_decode, s.dtype, okp, ovp, s.dtype, case.decode_tables,
+                                    case.decode_lens, s.scale, s.block_size, s.num_kv_heads)
+    assert max_abs(out_c, ref_c) <= TOL["bf16"]
+    assert max_abs(out_d, ref_d) <= TOL["bf16"]
+
+
+def test_mixed_step_full_size():
+    """The full mixed workload; prefill checked on sampled (row, head) outputs."""
+    case = W.make_mixed_case()
+    s = case.spec
+    print(f"[mixed] forks={len(case.prefill_lens)} decode={len(case.decode_lens)} "
+          f"pool={case.k_pool.shape[0]}", flush=True)
+    out_c, out_d, kp, vp = _mixed_step(case)
+    okp, ovp = _oracle_pools(case)
+    assert np.array_equal(W.torch_to_bits(kp, s.dtype), okp)
+    assert np.array_equal(W.torch_to_bits(vp, s.dtype), ovp)
+    ref_d = oracle.decode_attention(case.q_decode, s.dtype, okp, ovp, s.dtype, case.decode_tables,
+                                    case.decode_lens, s.scale, s.block_size, s.num_kv_heads)
+    assert max_abs(out_d, ref_d) <= TOL["bf16"]
+    rng = np.random.default_rng(7)
+    total = int(case.query_start_loc[-1])
+    rows = [(int(t), int(h)) for t, h in zip(rng.integers(0, total, 300),
+                                             rng.integers(0, s.num_q_heads, 300))]
+    # every chunk's first and last rows, on every head of one KV group
+    for f in range(len(case.prefill_lens)):
+        for t in (int(case.query_start_loc[f]), int(case.query_start_loc[f + 1]) - 1):
+            rows += [(t, h) for h in range(4)]
+    ref_c = oracle.prefill_chunk_attention(case.q_chunk, s.dtype, case.query_start_loc, okp, ovp,
+                                           s.dtype, case.prefill_tables, case.prefill_lens,
+                                           s.scale, s.block_size, s.num_kv_heads, rows=rows)
+    got = as_f64(out_c)
+    sampled = np.stack([got[t, h] for t, h in rows])
+    assert not np.isnan(got).any()
+    err = float(np.abs(sampled - ref_c).max())
+    print(f"[mixed] prefill sampled max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]

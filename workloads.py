@@ -56,6 +56,14 @@ def bits_to_torch(bits: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(arr.view(signed)).view(TORCH_DTYPE[dtype])
 
 
+def bits_to_device(bits: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload raw bits and view them on the device as the element type."""
+    arr = np.ascontiguousarray(bits)
+    signed = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16,
+              np.dtype(np.uint8): np.uint8}[arr.dtype]
+    return torch.from_numpy(arr.view(signed)).to(device).view(TORCH_DTYPE[dtype])
+
+
 def torch_to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     """Raw bits of a (CPU or device) torch tensor of the element type."""
     return t.detach().cpu().contiguous().view(TORCH_BITS[dtype]).numpy().view(BITS_DTYPE[dtype]).copy()
