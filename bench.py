@@ -1,0 +1,345 @@
+"""Benchmark of the paged KV-cache decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--rotate R]
+
+One step is one pass of the decode hot path over one batch: scatter of each
+sequence's newest K/V into its pool slot (pa_reshape_and_cache), then paged
+decode attention (pa_decode_attention) and the log-sum-exp merge of split
+partials (pa_decode_reduce), all on torch's current stream.  For the mixed
+workload a step is copy-on-write (pa_copy_blocks), the scatter of every new
+token, the causal prefill chunks (pa_prefill_chunk) and the decodes.
+
+The default workload is the Llama-2-7B-shaped layer (64 sequences, 32/32
+heads, head_dim 128, block 16, lengths U[128, 2048], fp16).  Throughput is
+effective KV bytes per second: sum over sequences of len * Hkv * D * (bytes
+of K + bytes of V), the K and V the method must read, divided by the time
+of the whole step.  Batch layouts (lengths, shuffled physical ids, tables,
+slots) come from workloads.py; element values are drawn on the device with
+torch's seeded generator (same distributions).  R batches with separate
+pools are rotated so that no step finds its KV in the 256 MB last-level
+cache.
+
+Printed: one JSON line with the step rate, a roofline object for the
+dominant kernel (its average duration measured with HIP events on the
+launch stream) and a CPU baseline (the fp64 oracle on a bounded sample, on
+this host's cores).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, vendor figure
+METRIC = "pa_decode effective KV GB/s (% of HBM peak); decode tokens/s per layer"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama2_7b_mha_f16",
+                    help="llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | tiny_f32 "
+                         "| mixed_prefix_bf16")
+    ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="decode partition size override (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Device batches
+# ---------------------------------------------------------------------------
+
+def _randn(shape, gen, dev, std=1.0):
+    import torch
+    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    return x.mul_(std) if std != 1.0 else x
+
+
+def _to_cache(x, dtype: str):
+    """float32 values -> stored element type; fp8 gets a per-tensor amax/448 scale."""
+    import torch
+    import workloads as W
+    if dtype == "fp8_e4m3":
+        scale = float((x.abs().max() / W.FP8_MAX).item())
+        return (x / scale).clamp_(-W.FP8_MAX, W.FP8_MAX).to(torch.float8_e4m3fn), scale
+    return x.to(W.TORCH_DTYPE[dtype]), 1.0
+
+
+class DecodeBatch:
+    """One decode batch resident in HBM (values drawn on the device)."""
+
+    def __init__(self, lay, seed: int, dev):
+        import torch
+        import workloads as W
+        s = lay.spec
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        shape = (lay.num_blocks, s.num_kv_heads, s.block_size, s.head_dim)
+        self.k_pool, self.k_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.cache_dtype)
+        self.v_pool, self.v_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.cache_dtype)
+        S = len(lay.seq_lens)
+        qdt = W.TORCH_DTYPE[s.q_dtype]
+        self.q = _randn((S, s.num_q_heads, s.head_dim), gen, dev, s.value_std).to(qdt)
+        self.new_k = _randn((S, s.num_kv_heads, s.head_dim), gen, dev, s.value_std).to(qdt)
+        self.new_v = _randn((S, s.num_kv_heads, s.head_dim), gen, dev, s.value_std).to(qdt)
+        self.tables = torch.from_numpy(lay.block_tables).to(dev)
+        self.lens = torch.from_numpy(lay.seq_lens.astype("int32")).to(dev)
+        self.slots = torch.from_numpy(lay.slot_mapping).to(dev)
+        self.out = torch.empty_like(self.q)
+
+
+def run_decode_bench(args, dev):
+    import numpy as np
+    import torch
+    import paged_kv_cache_415_amd as pa
+    import workloads as W
+
+    spec = W.DECODE_SPECS[args.config]
+    lay = W.make_decode_layout(spec, rep=0)
+    max_len = int(lay.seq_lens.max())
+    part = spec.partition_size if args.partition is None else args.partition
+    batches = [DecodeBatch(lay, seed=4150 + r, dev=dev) for r in range(max(1, args.rotate))]
+    torch.cuda.synchronize()
+    b0 = batches[0]
+    resolved = pa.pa_decode_partition_size(len(lay.seq_lens), spec.num_kv_heads, spec.block_size,
+                                           max_len, part)
+    ws = pa.decode_workspace(b0.q, b0.k_pool, max_len, part)
+
+    def step(b, ev=None):
+        pa.pa_reshape_and_cache(b.new_k, b.new_v, b.k_pool, b.v_pool, b.slots, b.k_scale, b.v_scale)
+        if ev is not None:
+            ev[0].record()
+        pa.pa_decode_attention(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
+                               max_len, b.k_scale, b.v_scale, part, ws)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_decode_reduce(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
+                            max_len, b.k_scale, b.v_scale, part, ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(batches[i % len(batches)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(batches[i % len(batches)], evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    red_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    assert not torch.isnan(b0.out).any(), "NaN in decode output"
+
+    eff = W.effective_kv_bytes(lay.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
+    ms_step = elapsed * 1e3 / args.steps
+    attn_avg = float(np.mean(attn_ms))
+    S = len(lay.seq_lens)
+    value = eff / (ms_step * 1e-3) / 1e9
+    achieved = eff / (attn_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
+        "ms_per_step": round(ms_step, 5),
+        "dtype": spec.cache_dtype if spec.cache_dtype == spec.q_dtype else
+        f"{spec.q_dtype}+{spec.cache_dtype}",
+        "config": {"workload": spec.description, "name": spec.name, "num_seqs": S,
+                   "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_dim": spec.head_dim, "block_size": spec.block_size,
+                   "total_context_tokens": int(lay.seq_lens.sum()), "max_seq_len": max_len,
+                   "partition_size": resolved, "rotated_batches": len(batches)},
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel" if spec.cache_dtype != "f32"
+                     else "decode_f32_kernel",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": eff,
+                     "avg_launch_ms": round(attn_avg, 5)},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
+        "decode_gbps_attention_plus_reduce": round(
+            eff / ((attn_avg + float(np.mean(red_ms))) * 1e-3) / 1e9, 1),
+        "reduce_avg_ms": round(float(np.mean(red_ms)), 5),
+        "attention_p10_p50_p90_ms": [round(float(x), 5) for x in
+                                      np.percentile(attn_ms, [10, 50, 90])],
+        "effective_kv_bytes_per_step": eff,
+    }
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Mixed chunked-prefill + decode step (copy-on-write, scatter, prefill, decode)
+# ---------------------------------------------------------------------------
+
+def run_mixed_bench(args, dev):
+    import numpy as np
+    import torch
+    import paged_kv_cache_415_amd as pa
+    import workloads as W
+
+    case = W.make_mixed_case()
+    s = case.spec
+    dt = s.dtype
+    up = lambda a: W.bits_to_device(a, dt, dev)
+    upi = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kp, vp = up(case.k_pool), up(case.v_pool)
+    pairs = upi(case.cow_pairs)
+    nk, nv, slots = up(case.new_k), up(case.new_v), upi(case.slot_mapping)
+    qc, qd = up(case.q_chunk), up(case.q_decode)
+    qsl, ptab, plen = upi(case.query_start_loc), upi(case.prefill_tables), upi(case.prefill_lens)
+    dtab, dlen = upi(case.decode_tables), upi(case.decode_lens)
+    out_c, out_d = torch.empty_like(qc), torch.empty_like(qd)
+    max_q = int(np.diff(case.query_start_loc).max())
+    max_len = int(case.decode_lens.max())
+    ws = pa.decode_workspace(qd, kp, max_len)
+
+    def step(ev=None):
+        pa.pa_copy_blocks(kp, vp, pairs)
+        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
+        if ev is not None:
+            ev[0].record()
+        pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = elapsed * 1e3 / args.steps
+    # causal (query, key) pairs of the chunks: query i of a chunk of L in a
+    # context of n sees n - L + i + 1 keys; 4 * D flops per pair and head
+    pairs_per_head = 0
+    for f in range(len(case.prefill_lens)):
+        n, L = int(case.prefill_lens[f]), int(np.diff(case.query_start_loc)[f])
+        pairs_per_head += sum(n - L + i + 1 for i in range(L))
+    flops = pairs_per_head * s.num_q_heads * 4 * s.head_dim
+    eff = W.effective_kv_bytes(case.decode_lens, s.num_kv_heads, s.head_dim, dt)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    dec_gbps = eff / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(eff / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "ms_per_step": round(ms_step, 5), "dtype": dt,
+        "config": {"workload": s.description, "name": s.name,
+                   "prefill_tokens": int(case.query_start_loc[-1]),
+                   "decode_seqs": int(len(case.decode_lens)), "cow_pairs": int(len(case.cow_pairs))},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(tflops, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(pre_ms, 5)},
+        "decode_roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel",
+                            "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                            "algorithmic_bytes_per_launch": eff, "avg_launch_ms": round(dec_ms, 5)},
+        "prefill_tokens_per_s": round(int(case.query_start_loc[-1]) / (pre_ms * 1e-3), 1),
+        "decode_tokens_per_s_per_layer": round(len(case.decode_lens) / (ms_step * 1e-3), 1),
+    }
+
+
+# ---------------------------------------------------------------------------
+# Practical HBM read rate of a plain streaming kernel (context for the peak)
+# ---------------------------------------------------------------------------
+
+def probe_read_gbps(dev, nbytes=4 << 30, iters=10):
+    import torch
+    import paged_kv_cache_415_amd as pa
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty(16 * 2048, dtype=torch.uint8, device=dev)
+    pa.pa_probe_read(src, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        pa.pa_probe_read(src, sink)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    del src
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(args):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import workloads as W
+
+    name = args.config if args.config in W.DECODE_SPECS else "llama3_8b_gqa_bf16"
+    spec = W.DECODE_SPECS[name]
+    nseq = 16
+    case = W.make_decode_case(spec, rep=0, num_seqs=nseq)
+    eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
+    passes, spent = 0, 0.0
+    with threadpool_limits(1):
+        while spent < args.cpu_seconds or passes == 0:
+            t0 = time.perf_counter()
+            oracle.decode_attention(case.q, spec.q_dtype, case.k_pool, case.v_pool,
+                                    spec.cache_dtype, case.block_tables, case.seq_lens,
+                                    spec.scale, spec.block_size, spec.num_kv_heads,
+                                    case.k_scale, case.v_scale)
+            spent += time.perf_counter() - t0
+            passes += 1
+    return {"value": round(eff * passes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 oracle decode of the first {nseq} sequences of the {name} batch "
+                      f"({int(case.seq_lens.sum())} context tokens, all heads), {passes} passes "
+                      f"in {spent:.1f} s, BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_415_amd  # noqa: F401  (fails loudly if libpa.so is missing)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.config == "mixed_prefix_bf16":
+        res = run_mixed_bench(args, dev)
+    else:
+        res = run_decode_bench(args, dev)
+    res["probe_read_gbps"] = round(probe_read_gbps(dev), 1)
+    line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": res.pop("dtype"), "data": "synthetic",
+            "config": res.pop("config"), "roofline": res.pop("roofline")}
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args)
+    line.update(res)
+    line["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -239,15 +239,31 @@ class DecodeCase:
         return self.k_pool.shape[0]
 
 
-def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None = None,
-                     lens=None) -> DecodeCase:
-    """Build a seeded decode step for ``spec`` (optionally with fewer sequences or
-    explicit lengths, for small parity cases)."""
+@dataclass
+class DecodeLayout:
+    """The integer part of a decode step: lengths, block tables and slots.
+
+    ``rng`` is the case's generator, positioned just after the draws that
+    built the layout, so value draws continue the same stream."""
+    spec: DecodeSpec
+    seq_lens: np.ndarray       # int64 [S], includes the new token
+    tables: list               # per sequence, its physical block ids
+    block_tables: np.ndarray   # int32 [S][MB]; padding -> poison_block
+    slot_mapping: np.ndarray   # int64 [S], slot of each sequence's newest token
+    num_blocks: int
+    poison_block: int
+    rng: np.random.Generator
+
+
+def make_decode_layout(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None = None,
+                       lens=None) -> DecodeLayout:
+    """Seeded lengths, shuffled physical block ids, padded block tables and the
+    newest token's slot for every sequence (no element values)."""
     if isinstance(spec, str):
         spec = DECODE_SPECS[spec]
     rng = _rng(spec.name, rep)
     S = spec.num_seqs if num_seqs is None else num_seqs
-    H, Hq, D, bs = spec.num_kv_heads, spec.num_q_heads, spec.head_dim, spec.block_size
+    bs = spec.block_size
     if lens is None:
         seq_lens = draw_lengths(spec.lens, spec.num_seqs, rng)[:S]
     else:
@@ -264,6 +280,27 @@ def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None 
     mgr = BlockManager(nb, bs, order=rng.permutation(nb))
     tables = [mgr.allocate(int(n)) for n in seq_lens]
     poison_block = mgr._take()
+
+    block_tables = np.full((S, mb), poison_block, dtype=np.int32)
+    slot_mapping = np.zeros(S, dtype=np.int64)
+    for s, n in enumerate(seq_lens):
+        block_tables[s, : len(tables[s])] = tables[s]
+        pos = int(n) - 1
+        slot_mapping[s] = tables[s][pos // bs] * bs + pos % bs
+    return DecodeLayout(spec=spec, seq_lens=seq_lens, tables=tables, block_tables=block_tables,
+                        slot_mapping=slot_mapping, num_blocks=nb, poison_block=poison_block,
+                        rng=rng)
+
+
+def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None = None,
+                     lens=None) -> DecodeCase:
+    """Build a seeded decode step for ``spec`` (optionally with fewer sequences or
+    explicit lengths, for small parity cases)."""
+    lay = make_decode_layout(spec, rep, num_seqs, lens)
+    spec, rng, seq_lens, tables = lay.spec, lay.rng, lay.seq_lens, lay.tables
+    S = len(seq_lens)
+    H, Hq, D, bs = spec.num_kv_heads, spec.num_q_heads, spec.head_dim, spec.block_size
+    nb, poison_block = lay.num_blocks, lay.poison_block
 
     cache_dt, q_dt = spec.cache_dtype, spec.q_dtype
     src_dt = q_dt                                  # new K/V arrive in the activation dtype
@@ -311,13 +348,7 @@ def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None 
             flat[:, n - 1:, :] = nan
             pool[ids] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
 
-    block_tables = np.full((S, mb), poison_block, dtype=np.int32)
-    slot_mapping = np.zeros(S, dtype=np.int64)
-    for s, n in enumerate(seq_lens):
-        block_tables[s, : len(tables[s])] = tables[s]
-        pos = int(n) - 1
-        slot_mapping[s] = tables[s][pos // bs] * bs + pos % bs
-
+    block_tables, slot_mapping = lay.block_tables, lay.slot_mapping
     return DecodeCase(spec=spec, q=to_bits(q_vals, q_dt), k_pool=k_pool, v_pool=v_pool,
                       block_tables=block_tables, seq_lens=seq_lens.astype(np.int32),
                       new_k=new_k, new_v=new_v, src_dtype=src_dt, slot_mapping=slot_mapping,
