@@ -264,6 +264,19 @@ def run_mixed_bench(args, dev):
 # Practical HBM read rate of a plain streaming kernel (context for the peak)
 # ---------------------------------------------------------------------------
 
+def probe_copy_once(dev, nbytes=1 << 30):
+    """One plain copy of a known size: the reference for the HBM byte counters."""
+    import torch
+    import paged_kv_cache_415_amd as pa
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    pa.pa_probe_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+    return nbytes
+
+
 def probe_read_gbps(dev, nbytes=4 << 30, iters=10):
     import torch
     import paged_kv_cache_415_amd as pa
@@ -330,6 +343,7 @@ def main():
     else:
         res = run_decode_bench(args, dev)
     res["probe_read_gbps"] = round(probe_read_gbps(dev), 1)
+    res["probe_copy_bytes"] = probe_copy_once(dev)
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",

@@ -5,14 +5,23 @@
 // query attends every cached token of the sequence, whose K/V are found
 // block by block through the block table.
 //
-// Work decomposition: one workgroup of four wave64s per
-// (sequence, KV head, partition of `partition` tokens).  The partition's
-// slice of the block table is staged in LDS once; each wave then walks
-// 32-token steps of the partition (steps w, w+4, ...), keeping its own
-// online-softmax state (running max m, running sum l, unnormalised output).
-// The four waves merge through LDS at the end.  A sequence with one
-// partition gets its output written directly; longer sequences write
-// partial (o, m, l) triples that lse_reduce_kernel merges.
+// Scheduling.  The grid is persistent: as many workgroups (four independent
+// wave64s each) as stay resident on the device.  Every workgroup first reads
+// the batch's lengths into LDS and forms the prefix sum of each sequence's
+// count of 32-token steps ("units").  The units of all (sequence, KV head)
+// pairs, laid end to end, are then cut into one contiguous range per wave, so
+// every wave streams the same number of KV bytes whatever the length mix.  A
+// range that covers a pair partly yields a partial result (o, m, l); a pair
+// covered by one wave gets its output written directly.  The log-sum-exp
+// reduce kernel merges the partials.  Two other cuts exist: fixed partitions
+// of a given length from each sequence's start (items handed out round-robin),
+// and whole pairs (no partials at all).
+//
+// Within a segment a wave walks 32-token steps with the next step's K/V loads
+// in flight while the current step is computed (two register buffers).  The
+// block-table entries of the segment sit in two registers per lane (a window
+// of 128 consecutive entries); the block id of a tile is read out with
+// v_readlane, so tile addresses are scalar.
 //
 // Matrix cores: all query heads of a KV group are the 16 columns of one
 // MFMA tile (group <= 16; unused columns are zero queries), so each K/V
@@ -26,6 +35,8 @@
 // head's own lanes.  The value operand wants 4+4 tokens of one dimension
 // per lane while the cache stores dimensions contiguously; each lane loads
 // 16-byte row pieces and transposes them in registers with byte permutes.
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -52,232 +63,214 @@ struct Mma<_Float16> {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kStep = 32;       // tokens per step (one unit of work)
+constexpr int kMaxPlanSeqs = 8000;
 
-// Dynamic LDS: block-table slice, per-wave (m, l) and per-wave outputs.
-struct DecodeSmem {
-  int* tab;
-  float* m;   // [kWaves][16]
-  float* l;   // [kWaves][16]
-  float* o;   // [kWaves][group][D]
-};
-
-__device__ __forceinline__ DecodeSmem carve(char* base, int ntab, int group, int dim) {
-  DecodeSmem s;
-  s.tab = reinterpret_cast<int*>(base);
-  int off = ((ntab * 4 + 15) / 16) * 16;
-  s.m = reinterpret_cast<float*>(base + off);
-  s.l = s.m + kWaves * 16;
-  s.o = s.l + kWaves * 16;
-  (void)group;
-  (void)dim;
-  return s;
-}
-
-size_t decode_smem_bytes(int partition, int block_size, int group, int dim) {
-  const int ntab = (partition + block_size - 1) / block_size;
-  return ((ntab * 4 + 15) / 16) * 16 + 2 * kWaves * 16 * 4 + (size_t)kWaves * group * dim * 4;
-}
-
-// Shared prologue: clamp the length, find this workgroup's token range and
-// stage the block-table slice.  Returns false when the workgroup has no work.
-struct Range {
-  int len, start, end, nparts;
-};
-
-__device__ __forceinline__ bool decode_prologue(const DecodeParams& p, const DecodeSmem& sm,
-                                                Range& r) {
-  const int seq = blockIdx.z, part = blockIdx.x;
-  int len = p.seq_lens[seq];
-  len = len < p.max_len ? len : p.max_len;
-  r.len = len;
-  r.start = part * p.partition;
-  r.nparts = len > 0 ? (len + p.partition - 1) / p.partition : 0;
-  if (r.start >= len) return false;
-  r.end = min(len, r.start + p.partition);
-  const int nblk = (r.end - r.start + p.block_size - 1) / p.block_size;
-  const int* row = p.block_tables + (int64_t)seq * p.max_blocks + r.start / p.block_size;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) sm.tab[i] = row[i];
-  __syncthreads();
-  return true;
-}
-
-// Zero output for sequences with no tokens (written once, by partition 0).
-template <typename QT>
-__device__ __forceinline__ void zero_output(const DecodeParams& p) {
-  const int seq = blockIdx.z, kvh = blockIdx.y;
-  QT* out = reinterpret_cast<QT*>(p.out) + ((int64_t)seq * p.num_q_heads + kvh * p.group) * p.head_dim;
-  for (int i = threadIdx.x; i < p.group * p.head_dim; i += kThreads) out[i] = (QT)0.0f;
-}
-
-// Merge the four waves' states and write the output or the partials.
-template <typename QT>
-__device__ __forceinline__ void merge_and_store(const DecodeParams& p, const DecodeSmem& sm,
-                                                const Range& r) {
-  __syncthreads();
-  const int seq = blockIdx.z, kvh = blockIdx.y, part = blockIdx.x;
-  const int D = p.head_dim, g = p.group;
-  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
-    const int j = idx / D, d = idx - j * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w * 16 + j]);
-    float O = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.m[w * 16 + j];
-      if (mw != -INFINITY) {       // idle waves left no state
-        const float wt = __builtin_amdgcn_exp2f(mw - M);
-        O += wt * sm.o[(w * g + j) * D + d];
-        L += wt * sm.l[w * 16 + j];
-      }
-    }
-    const int h = kvh * g + j;
-    if (r.nparts == 1) {
-      QT* out = reinterpret_cast<QT*>(p.out);
-      out[((int64_t)seq * p.num_q_heads + h) * D + d] = (QT)(O / L * p.v_scale);
-    } else {
-      const int64_t b = ((int64_t)seq * p.num_q_heads + h) * p.max_parts + part;
-      p.part_o[b * D + d] = O;
-      if (d == 0) {
-        p.part_m[b] = M;
-        p.part_l[b] = L;
-      }
-    }
-  }
-}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // ---------------------------------------------------------------------------
-// MFMA decode for 16-bit and fp8 caches.
+// Plan: clamped lengths and the exclusive prefix sum of per-sequence counts
+// (units for the balanced cut, items for the fixed / whole cuts) in LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int plan_count(const DecodeParams& p, int len) {
+  const int u = (len + kStep - 1) / kStep;
+  if (p.mode == kSplitBalanced) return u;
+  if (p.mode == kSplitNone) return u > 0 ? 1 : 0;
+  return (u + p.chunk - 1) / p.chunk;
+}
+
+__device__ void build_plan(const DecodeParams& p, int* lens, int* pre) {
+  __shared__ int wave_sum[kWaves];
+  const int S = p.num_seqs;
+  const int per = (S + kThreads - 1) / kThreads;
+  const int b = min(S, (int)threadIdx.x * per), e = min(S, b + per);
+  int sum = 0;
+  for (int s = b; s < e; ++s) {
+    int n = p.seq_lens[s];
+    n = n < 0 ? 0 : (n > p.max_len ? p.max_len : n);
+    lens[s] = n;
+    const int c = plan_count(p, n);
+    pre[s] = c;
+    sum += c;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w = 0; w < wave; ++w) run += wave_sum[w];
+  for (int s = b; s < e; ++s) {
+    const int c = pre[s];
+    pre[s] = run;
+    run += c;
+  }
+  if (threadIdx.x == kThreads - 1) pre[S] = run;
+  __syncthreads();
+}
+
+// Largest s in [0, S) with pre[s] <= x, for 0 <= x < pre[S].
+__device__ __forceinline__ int find_seq(const int* pre, int S, int x) {
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uni(pre[mid]) <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Block-table entries of one sequence, 128 consecutive ones held as two
+// registers per lane; entry b is read out with v_readlane.
+template <int BS>
+struct TableWindow {
+  const int* row;
+  int nblk;
+  int base;   // multiple of 64
+  int a, b;   // entries base + lane, base + 64 + lane
+
+  __device__ __forceinline__ void init(const int* r, int n, int first) {
+    const int lane = threadIdx.x & 63;
+    row = r;
+    nblk = n;
+    base = first & ~63;
+    a = (base + lane < nblk) ? row[base + lane] : 0;
+    b = (base + 64 + lane < nblk) ? row[base + 64 + lane] : 0;
+  }
+  // Make entries up to `last` readable.  Callers advance by at most two
+  // blocks at a time, and a step's blocks never straddle a multiple of 64.
+  __device__ __forceinline__ void ensure(int last) {
+    if (last >= base + 64) {
+      const int lane = threadIdx.x & 63;
+      base += 64;
+      a = b;
+      b = (base + 64 + lane < nblk) ? row[base + 64 + lane] : 0;
+    }
+  }
+  __device__ __forceinline__ int get(int bi) const {
+    const int r = bi - base;
+    return r < 64 ? __builtin_amdgcn_readlane(a, r) : __builtin_amdgcn_readlane(b, r - 64);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA segment for 16-bit and fp8 caches.
 //   QT: query / output / MFMA operand type (__bf16 or _Float16)
 //   FP8: cache holds E4M3 codes (decoded exactly to QT)
 // ---------------------------------------------------------------------------
 template <typename QT, bool FP8, int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
-  extern __shared__ __align__(16) char smem_raw[];
-  constexpr int NC = D / 32;     // QK MFMAs per 16-token tile (K = 32 dims each)
-  constexpr int DPL = D / 16;    // value dims per lane = PV MFMAs per 32-token step
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int VW = DPL * EB / 4;   // dwords per V row piece (1, 2 or 4)
-  const DecodeSmem sm = carve(smem_raw, (p.partition + BS - 1) / BS, p.group, D);
-  Range r;
-  if (p.seq_lens[blockIdx.z] <= 0) {
-    if (blockIdx.x == 0) zero_output<QT>(p);
-    return;
-  }
-  if (!decode_prologue(p, sm, r)) return;
+struct MfmaDecode {
+  static constexpr int NC = D / 32;             // QK MFMAs per 16-token tile
+  static constexpr int DPL = D / 16;            // value dims per lane = PV MFMAs per step
+  static constexpr int EB = FP8 ? 1 : 2;
+  static constexpr int VW = DPL * EB / 4;       // dwords per V row piece
+  static constexpr int KL = FP8 ? D / 64 : NC;  // 16-byte K loads per lane and tile
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int G = lane >> 4;      // 16-lane group: selects k-slots / token rows
-  const int c16 = lane & 15;    // column (query head) or row (token / dim) index
-  const int kvh = blockIdx.y, seq = blockIdx.z;
-  const int g = p.group;
+  struct Buf {
+    u32x4 k[2][KL];
+    uint32_t v[2][4][VW];
+  };
 
-  // Query operand (B of S^T = K Q^T): head column c16, 8 dims per MFMA.
-  // The dims a lane group covers in MFMA c follow the order in which K row
-  // pieces are loaded (any permutation of the reduction index is allowed as
-  // long as K and Q agree).
-  u32x4 qop[NC];
-  {
-    const QT* qrow = reinterpret_cast<const QT*>(p.q) +
-                     ((int64_t)seq * p.num_q_heads + kvh * g + c16) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int d0 = FP8 ? (64 * (c >> 1) + 16 * G + 8 * (c & 1)) : (32 * c + 8 * G);
-      qop[c] = (c16 < g) ? ld16(qrow + d0) : u32x4{0, 0, 0, 0};
-    }
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[DPL];
-#pragma unroll
-  for (int n = 0; n < DPL; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int ntok = r.end - r.start;
-  const int nsteps = (ntok + 31) >> 5;
-  const char* kpool = reinterpret_cast<const char*>(p.k_pool);
-  const char* vpool = reinterpret_cast<const char*>(p.v_pool);
-
-  for (int t = wave; t < nsteps; t += kWaves) {
-    const int rel0 = t * 32;                   // token offset of the step in the partition
-    u32x4 ka[2][NC];
-    uint32_t vw[2][4][VW];
+  // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).  Tiles
+  // that start past the end re-read the last block (their tokens are masked).
+  static __device__ __forceinline__ void load(Buf& buf, TableWindow<BS>& win, const DecodeParams& p,
+                                              int kvh, int j) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, c16 = lane & 15;
+    const char* kpool = reinterpret_cast<const char*>(p.k_pool);
+    const char* vpool = reinterpret_cast<const char*>(p.v_pool);
+    win.ensure(min((j * kStep + kStep - 1) / BS, win.nblk - 1));
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int rel = rel0 + 16 * tau;
-      if (rel < ntok) {
-        const int blk = sm.tab[rel / BS];
-        const int row0 = rel % BS;
-        const int64_t tile = (((int64_t)blk * p.num_kv_heads + kvh) * BS + row0) * D;   // elements
-        // K: this lane's token row c16
-        const char* kt = kpool + (tile + (int64_t)c16 * D) * EB;
-        if constexpr (FP8) {
+      const int rel = j * kStep + 16 * tau;
+      const int bi = min(rel / BS, win.nblk - 1);
+      const int row0 = rel % BS;
+      const int blk = win.get(bi);
+      const int64_t tile = (((int64_t)blk * p.num_kv_heads + kvh) * BS + row0) * D;  // elements
+      const char* kt = kpool + (tile + (int64_t)c16 * D) * EB;
+      if constexpr (FP8) {
 #pragma unroll
-          for (int h = 0; h < D / 64; ++h) {
-            const u32x4 raw = ld16(kt + 64 * h + 16 * G);
-            ka[tau][2 * h] = u32x4{fp8x2_to<QT>(raw.x, false), fp8x2_to<QT>(raw.x, true),
-                                   fp8x2_to<QT>(raw.y, false), fp8x2_to<QT>(raw.y, true)};
-            ka[tau][2 * h + 1] = u32x4{fp8x2_to<QT>(raw.z, false), fp8x2_to<QT>(raw.z, true),
-                                       fp8x2_to<QT>(raw.w, false), fp8x2_to<QT>(raw.w, true)};
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < NC; ++c) ka[tau][c] = ld16(kt + (32 * c + 8 * G) * 2);
-        }
-        // V: token rows 4G + i, dims DPL*c16 .. DPL*c16 + DPL - 1
-        const char* vt = vpool + (tile + (int64_t)(4 * G) * D + DPL * c16) * EB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const char* src = vt + (int64_t)i * D * EB;
-          if constexpr (VW == 4) {
-            const u32x4 x = ld16(src);
-            vw[tau][i][0] = x.x; vw[tau][i][1] = x.y; vw[tau][i][2] = x.z; vw[tau][i][3] = x.w;
-          } else if constexpr (VW == 2) {
-            const u32x2 x = ld8(src);
-            vw[tau][i][0] = x.x; vw[tau][i][1] = x.y;
-          } else {
-            vw[tau][i][0] = ld4(src);
-          }
-        }
-        // rows past the end hold stale or poisoned data: zero their values
-        // (a zero probability does not cancel a NaN in the product)
-        if (rel + 16 > ntok) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (rel + 4 * G + i >= ntok) {
-#pragma unroll
-              for (int w = 0; w < VW; ++w) vw[tau][i][w] = 0u;
-            }
-        }
+        for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16(kt + 64 * h + 16 * G);
       } else {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) ka[tau][c] = u32x4{0, 0, 0, 0};
+        for (int c = 0; c < KL; ++c) buf.k[tau][c] = ld16(kt + (32 * c + 8 * G) * 2);
+      }
+      const char* vt = vpool + (tile + (int64_t)(4 * G) * D + DPL * c16) * EB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int w = 0; w < VW; ++w) vw[tau][i][w] = 0u;
+      for (int i = 0; i < 4; ++i) {
+        const char* src = vt + (int64_t)i * D * EB;
+        if constexpr (VW == 4) {
+          const u32x4 x = ld16(src);
+          buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y; buf.v[tau][i][2] = x.z; buf.v[tau][i][3] = x.w;
+        } else if constexpr (VW == 2) {
+          const u32x2 x = ld8(src);
+          buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y;
+        } else {
+          buf.v[tau][i][0] = ld4(src);
+        }
       }
     }
+  }
 
+  struct State {
+    float m, l;
+    f32x4 acc[DPL];
+  };
+
+  static __device__ __forceinline__ void compute(Buf& buf, State& st, const u32x4 (&qop)[NC],
+                                                 float qk_scale_log2, int len, int j) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4;
+    const int rel0 = j * kStep;
+    // rows past the end hold stale or poisoned data: zero their values
+    // (a zero probability does not cancel a NaN in the product)
+    if (rel0 + kStep > len) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (rel0 + 16 * tau + 4 * G + i >= len) {
+#pragma unroll
+            for (int w = 0; w < VW; ++w) buf.v[tau][i][w] = 0u;
+          }
+    }
     // Scores: S^T tile tau, lane (G, c16) holds tokens 4G+i of head c16.
     float s[2][4];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
+      u32x4 ka[NC];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int h = 0; h < KL; ++h) {
+          const u32x4 raw = buf.k[tau][h];
+          ka[2 * h] = u32x4{fp8x2_to<QT>(raw.x, false), fp8x2_to<QT>(raw.x, true),
+                            fp8x2_to<QT>(raw.y, false), fp8x2_to<QT>(raw.y, true)};
+          ka[2 * h + 1] = u32x4{fp8x2_to<QT>(raw.z, false), fp8x2_to<QT>(raw.z, true),
+                                fp8x2_to<QT>(raw.w, false), fp8x2_to<QT>(raw.w, true)};
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ka[c] = buf.k[tau][c];
+      }
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sc = Mma<QT>::mma(ka[tau][c], qop[c], sc);
+      for (int c = 0; c < NC; ++c) sc = Mma<QT>::mma(ka[c], qop[c], sc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rel = rel0 + 16 * tau + 4 * G + i;
-        s[tau][i] = (rel < ntok) ? sc[i] * p.qk_scale_log2 : -INFINITY;
+        s[tau][i] = (rel < len) ? mul_rn(sc[i], qk_scale_log2) : -INFINITY;
       }
     }
     float smax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                        fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     smax = xor_max(smax, 16);
     smax = xor_max(smax, 32);
-    const float m_new = fmaxf(m_run, smax);     // finite: every step has a valid token
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    const float m_new = fmaxf(st.m, smax);     // finite: every step has a valid token
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
     uint32_t pw[4];
     float psum = 0.f;
 #pragma unroll
@@ -292,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         psum += lo_f32<QT>(w) + hi_f32<QT>(w);
       }
     }
-    l_run = l_run * alpha + psum;
+    st.l = st.l * alpha + psum;
     const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]};
 
     // Values: A operand for dim DPL*c16 + n holds tokens 4G+0..3 of tile 0
@@ -305,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         uint32_t x[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-          const uint32_t r0 = vw[tau][0][w], r1 = vw[tau][1][w], r2 = vw[tau][2][w], r3 = vw[tau][3][w];
+          const uint32_t r0 = buf.v[tau][0][w], r1 = buf.v[tau][1][w];
+          const uint32_t r2 = buf.v[tau][2][w], r3 = buf.v[tau][3][w];
           const uint32_t ta = (k & 1) ? perm(r1, r0, 0x07030501u) : perm(r1, r0, 0x06020400u);
           const uint32_t tc = (k & 1) ? perm(r3, r2, 0x07030501u) : perm(r3, r2, 0x06020400u);
           x[tau] = (k & 2) ? perm(tc, ta, 0x07060302u) : perm(tc, ta, 0x05040100u);
@@ -315,190 +309,364 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       } else {
         const int w = n >> 1;
         const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-        a = u32x4{perm(vw[0][1][w], vw[0][0][w], sel), perm(vw[0][3][w], vw[0][2][w], sel),
-                  perm(vw[1][1][w], vw[1][0][w], sel), perm(vw[1][3][w], vw[1][2][w], sel)};
+        a = u32x4{perm(buf.v[0][1][w], buf.v[0][0][w], sel), perm(buf.v[0][3][w], buf.v[0][2][w], sel),
+                  perm(buf.v[1][1][w], buf.v[1][0][w], sel), perm(buf.v[1][3][w], buf.v[1][2][w], sel)};
       }
-      acc[n] = acc[n] * alpha;
-      acc[n] = Mma<QT>::mma(a, pop, acc[n]);
+      st.acc[n] = st.acc[n] * alpha;
+      st.acc[n] = Mma<QT>::mma(a, pop, st.acc[n]);
     }
   }
 
-  // Wave state -> LDS.  lane (G, c16) holds head c16, dims DPL*(4G+i) + n.
-  float l_tot = xor_sum(l_run, 16);
-  l_tot = xor_sum(l_tot, 32);
-  if (c16 < g) {
-    if (G == 0) {
-      sm.m[wave * 16 + c16] = m_run;
-      sm.l[wave * 16 + c16] = l_tot;
+  // One wave: steps [j0, j1) of pair (s, kvh), then the output or a partial.
+  static __device__ void segment(const DecodeParams& p, int s, int kvh, int len, int j0, int j1,
+                                 int part, int nparts) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, c16 = lane & 15;
+    const int g = p.group;
+
+    // Query operand (B of S^T = K Q^T): head column c16, 8 dims per MFMA.
+    // The dims a lane group covers in MFMA c follow the order in which K row
+    // pieces are loaded (any permutation of the reduction index is allowed as
+    // long as K and Q agree).
+    u32x4 qop[NC];
+    {
+      const QT* qrow = reinterpret_cast<const QT*>(p.q) +
+                       ((int64_t)s * p.num_q_heads + kvh * g + c16) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int d0 = FP8 ? (64 * (c >> 1) + 16 * G + 8 * (c & 1)) : (32 * c + 8 * G);
+        qop[c] = (c16 < g) ? ld16(qrow + d0) : u32x4{0, 0, 0, 0};
+      }
     }
-    float* o = sm.o + (wave * g + c16) * D;
+
+    TableWindow<BS> win;
+    win.init(p.block_tables + (int64_t)s * p.max_blocks, (len + BS - 1) / BS, (j0 * kStep) / BS);
+
+    State st;
+    st.m = -INFINITY;
+    st.l = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int n = 0; n < DPL; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Two buffers in flight; the prefetch past the segment's end re-reads
+    // its last step (an L2 hit), which keeps every load unconditional.
+    Buf A, B;
+    load(A, win, p, kvh, j0);
+    for (int j = j0; j < j1; j += 2) {
+      load(B, win, p, kvh, min(j + 1, j1 - 1));
+      compute(A, st, qop, p.qk_scale_log2, len, j);
+      if (j + 1 >= j1) break;
+      load(A, win, p, kvh, min(j + 2, j1 - 1));
+      compute(B, st, qop, p.qk_scale_log2, len, j + 1);
+    }
+
+    // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
+    float l_tot = xor_sum(st.l, 16);
+    l_tot = xor_sum(l_tot, 32);
+    if (c16 < g) {
+      const int hq = kvh * g + c16;
+      if (nparts == 1) {
+        QT* orow = reinterpret_cast<QT*>(p.out) + ((int64_t)s * p.num_q_heads + hq) * D;
+        const float inv = p.v_scale / l_tot;
 #pragma unroll
-      for (int n = 0; n < DPL; ++n) o[DPL * (4 * G + i) + n] = acc[n][i];
+        for (int i = 0; i < 4; ++i) {
+          uint32_t w[DPL / 2];
+#pragma unroll
+          for (int n = 0; n < DPL; n += 2) w[n / 2] = pack2<QT>(st.acc[n][i] * inv, st.acc[n + 1][i] * inv);
+          QT* dst = orow + DPL * (4 * G + i);
+          if constexpr (DPL == 8) st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+          else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+        }
+      } else {
+        const int64_t b = ((int64_t)s * p.num_q_heads + hq) * p.max_parts + part;
+        float* o = p.part_o + b * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* dst = o + DPL * (4 * G + i);
+#pragma unroll
+          for (int n = 0; n < DPL; n += 4)
+            *reinterpret_cast<f32x4*>(dst + n) =
+                f32x4{st.acc[n][i], st.acc[n + 1][i], st.acc[n + 2][i], st.acc[n + 3][i]};
+        }
+        if (G == 0) {
+          p.part_m[b] = st.m;
+          p.part_l[b] = l_tot;
+        }
+      }
+    }
+    if (part == 0 && p.nparts != nullptr && lane == 0) p.nparts[s * p.num_kv_heads + kvh] = nparts;
   }
-  merge_and_store<QT>(p, sm, r);
-}
+};
 
 // ---------------------------------------------------------------------------
-// fp32 decode (VALU): the small fp32 workloads.  Same grid, partitions and
-// merge as the MFMA kernel; each wave handles one token at a time with the
-// head dimension spread over its lanes.
+// fp32 segment (VALU): the small fp32 workloads.  One token at a time, the
+// head dimension spread over the lanes.
 // ---------------------------------------------------------------------------
 template <int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeParams p) {
-  extern __shared__ __align__(16) char smem_raw[];
-  constexpr int E = D / 64;
-  const DecodeSmem sm = carve(smem_raw, (p.partition + BS - 1) / BS, p.group, D);
-  Range r;
-  if (p.seq_lens[blockIdx.z] <= 0) {
-    if (blockIdx.x == 0) zero_output<float>(p);
-    return;
-  }
-  if (!decode_prologue(p, sm, r)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kvh = blockIdx.y, seq = blockIdx.z, g = p.group;
-  const float* q = reinterpret_cast<const float*>(p.q) + ((int64_t)seq * p.num_q_heads + kvh * g) * D;
-  float qv[16][E], acc[16][E], m[16], l[16];
+struct F32Decode {
+  static __device__ void segment(const DecodeParams& p, int s, int kvh, int len, int j0, int j1,
+                                 int part, int nparts) {
+    constexpr int E = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int g = p.group;
+    const float* q = reinterpret_cast<const float*>(p.q) + ((int64_t)s * p.num_q_heads + kvh * g) * D;
+    float qv[16][E], acc[16][E], m[16], l[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
+    for (int j = 0; j < 16; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      qv[j][e] = (j < g) ? q[j * D + lane + 64 * e] : 0.f;
-      acc[j][e] = 0.f;
+      for (int e = 0; e < E; ++e) {
+        qv[j][e] = (j < g) ? q[j * D + lane + 64 * e] : 0.f;
+        acc[j][e] = 0.f;
+      }
     }
-  }
-  const float* kpool = reinterpret_cast<const float*>(p.k_pool);
-  const float* vpool = reinterpret_cast<const float*>(p.v_pool);
-  for (int tok = r.start + wave; tok < r.end; tok += kWaves) {
-    const int rel = tok - r.start;
-    const int blk = sm.tab[rel / BS];
-    const int64_t rowoff = (((int64_t)blk * p.num_kv_heads + kvh) * BS + rel % BS) * D;
-    float kv[E], vv[E];
+    TableWindow<BS> win;
+    win.init(p.block_tables + (int64_t)s * p.max_blocks, (len + BS - 1) / BS, (j0 * kStep) / BS);
+    const float* kpool = reinterpret_cast<const float*>(p.k_pool);
+    const float* vpool = reinterpret_cast<const float*>(p.v_pool);
+    const int t_end = min(j1 * kStep, len);
+    for (int t = j0 * kStep; t < t_end; ++t) {
+      const int bi = t / BS;
+      win.ensure(bi);
+      const int blk = win.get(bi);
+      const int64_t rowoff = (((int64_t)blk * p.num_kv_heads + kvh) * BS + t % BS) * D;
+      float kv[E], vv[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      kv[e] = kpool[rowoff + lane + 64 * e];
-      vv[e] = vpool[rowoff + lane + 64 * e];
+      for (int e = 0; e < E; ++e) {
+        kv[e] = kpool[rowoff + lane + 64 * e];
+        vv[e] = vpool[rowoff + lane + 64 * e];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j < g) {
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) dot += qv[j][e] * kv[e];
+#pragma unroll
+          for (int msk = 32; msk >= 1; msk >>= 1) dot = xor_sum(dot, msk);
+          const float sc = mul_rn(dot, p.qk_scale_log2);
+          const float m_new = fmaxf(m[j], sc);
+          const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+          const float pr = __builtin_amdgcn_exp2f(sc - m_new);
+          l[j] = l[j] * alpha + pr;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[j][e] = acc[j][e] * alpha + pr * vv[e];
+          m[j] = m_new;
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < g) {
-        float dot = 0.f;
+        const int hq = kvh * g + j;
+        if (nparts == 1) {
+          float* orow = reinterpret_cast<float*>(p.out) + ((int64_t)s * p.num_q_heads + hq) * D;
+          const float inv = p.v_scale / l[j];
 #pragma unroll
-        for (int e = 0; e < E; ++e) dot += qv[j][e] * kv[e];
+          for (int e = 0; e < E; ++e) orow[lane + 64 * e] = acc[j][e] * inv;
+        } else {
+          const int64_t b = ((int64_t)s * p.num_q_heads + hq) * p.max_parts + part;
 #pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) dot = xor_sum(dot, msk);
-        const float sc = dot * p.qk_scale_log2;
-        const float m_new = fmaxf(m[j], sc);
-        const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
-        const float pr = __builtin_amdgcn_exp2f(sc - m_new);
-        l[j] = l[j] * alpha + pr;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[j][e] = acc[j][e] * alpha + pr * vv[e];
-        m[j] = m_new;
+          for (int e = 0; e < E; ++e) p.part_o[b * D + lane + 64 * e] = acc[j][e];
+          if (lane == 0) {
+            p.part_m[b] = m[j];
+            p.part_l[b] = l[j];
+          }
+        }
       }
     }
+    if (part == 0 && p.nparts != nullptr && lane == 0) p.nparts[s * p.num_kv_heads + kvh] = nparts;
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j < g) {
-      if (lane == 0) {
-        sm.m[wave * 16 + j] = m[j];
-        sm.l[wave * 16 + j] = l[j];
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) sm.o[(wave * g + j) * D + lane + 64 * e] = acc[j][e];
+};
+
+// ---------------------------------------------------------------------------
+// The persistent kernel: plan, zero outputs of empty sequences, then walk
+// this wave's segments.
+// ---------------------------------------------------------------------------
+template <class Seg, typename QT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) int plan_lds[];
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  int* lens = plan_lds;
+  int* pre = plan_lds + S;
+  build_plan(p, lens, pre);
+
+  // Sequences with no tokens get a zero output.
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    if (lens[s] == 0) {
+      QT* out = reinterpret_cast<QT*>(p.out) + (int64_t)s * p.num_q_heads * p.head_dim;
+      for (int i = threadIdx.x; i < p.num_q_heads * p.head_dim; i += kThreads) out[i] = (QT)0.0f;
     }
   }
-  merge_and_store<float>(p, sm, r);
+
+  const int wave = uni(threadIdx.x >> 6);
+  const int W = gridDim.x * kWaves;
+  const int w = blockIdx.x * kWaves + wave;
+  const int total = uni(pre[S]);
+  const int T = total * H;
+
+  if (p.mode == kSplitBalanced) {
+    int chunk = (T + W - 1) / W;
+    chunk = chunk < p.chunk ? p.chunk : chunk;
+    const int64_t u0 = (int64_t)w * chunk;
+    if (u0 >= T) return;
+    int u = (int)u0;
+    const int uend = min(T, u + chunk);
+    int s = find_seq(pre, S, u / H);
+    int base = uni(pre[s]);
+    int U = uni(pre[s + 1]) - base;
+    int h = (u - base * H) / U;
+    int j = u - base * H - h * U;
+    while (true) {
+      const int ps = base * H + h * U;                 // first unit of the pair
+      const int j1 = min(U, j + (uend - u));
+      const int wf = ps / chunk, wl = (ps + U - 1) / chunk;
+      Seg::segment(p, s, h, uni(lens[s]), j, j1, w - wf, wl - wf + 1);
+      u += j1 - j;
+      if (u >= uend) break;
+      j = 0;
+      if (++h == H) {
+        h = 0;
+        do {
+          ++s;
+        } while (uni(pre[s + 1]) == uni(pre[s]));
+        base = uni(pre[s]);
+        U = uni(pre[s + 1]) - base;
+      }
+    }
+  } else {
+    for (int i = w; i < T; i += W) {
+      const int s = find_seq(pre, S, i / H);
+      const int base = uni(pre[s]);
+      const int q = uni(pre[s + 1]) - base;
+      const int rel = i - base * H;
+      const int h = rel / q, part = rel - h * q;
+      const int len = uni(lens[s]);
+      const int U = (len + kStep - 1) / kStep;
+      const int j0 = part * p.chunk;
+      const int j1 = min(U, j0 + p.chunk);
+      Seg::segment(p, s, h, len, j0, j1, part, q);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of split partials:
+// Log-sum-exp merge of split partials of one (sequence, KV head) pair:
 //   M = max_i m_i,  out = v_scale * sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
 // ---------------------------------------------------------------------------
 template <typename QT>
-__global__ __launch_bounds__(128) void lse_reduce_kernel(DecodeParams p) {
-  const int h = blockIdx.x, seq = blockIdx.y;
-  int len = p.seq_lens[seq];
+__global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
+  const int h = blockIdx.x, s = blockIdx.y;
+  int len = p.seq_lens[s];
   len = len < p.max_len ? len : p.max_len;
   if (len <= 0) return;
-  const int nparts = (len + p.partition - 1) / p.partition;
-  if (nparts <= 1) return;
-  const int64_t b = ((int64_t)seq * p.num_q_heads + h) * p.max_parts;
-  float M = -INFINITY;
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, p.part_m[b + i]);
-  float L = 0.f;
-  for (int i = 0; i < nparts; ++i) L += __builtin_amdgcn_exp2f(p.part_m[b + i] - M) * p.part_l[b + i];
-  const float inv = p.v_scale / L;
-  QT* out = reinterpret_cast<QT*>(p.out) + ((int64_t)seq * p.num_q_heads + h) * p.head_dim;
-  for (int d = threadIdx.x; d < p.head_dim; d += blockDim.x) {
-    float O = 0.f;
-    for (int i = 0; i < nparts; ++i)
-      O += __builtin_amdgcn_exp2f(p.part_m[b + i] - M) * p.part_o[(b + i) * p.head_dim + d];
-    out[d] = (QT)(O * inv);
+  const int np = p.nparts[s * p.num_kv_heads + h];
+  if (np <= 1) return;
+  const int D = p.head_dim;
+  for (int idx = threadIdx.x; idx < p.group * D; idx += blockDim.x) {
+    const int j = idx / D, d = idx - j * D;
+    const int hq = h * p.group + j;
+    const int64_t b = ((int64_t)s * p.num_q_heads + hq) * p.max_parts;
+    float M = -INFINITY;
+    for (int i = 0; i < np; ++i) M = fmaxf(M, p.part_m[b + i]);
+    float L = 0.f, O = 0.f;
+    for (int i = 0; i < np; ++i) {
+      const float wt = __builtin_amdgcn_exp2f(p.part_m[b + i] - M);
+      L += wt * p.part_l[b + i];
+      O += wt * p.part_o[(b + i) * D + d];
+    }
+    reinterpret_cast<QT*>(p.out)[((int64_t)s * p.num_q_heads + hq) * D + d] = (QT)(O / L * p.v_scale);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
-template <typename QT, bool FP8, int D>
-static void launch_mfma_bs(const DecodeParams& p, dim3 grid, size_t smem, hipStream_t s) {
-  if (p.block_size == 16)
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, FP8, D, 16>), grid, dim3(kThreads), smem, s, p);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<QT, FP8, D, 32>), grid, dim3(kThreads), smem, s, p);
+size_t decode_plan_lds_bytes(int num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int); }
+int decode_max_plan_seqs() { return kMaxPlanSeqs; }
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  });
+  return g_cu_count[dev];
 }
 
-template <typename QT, bool FP8>
-static void launch_mfma(const DecodeParams& p, dim3 grid, size_t smem, hipStream_t s) {
-  if (p.head_dim == 128)
-    launch_mfma_bs<QT, FP8, 128>(p, grid, smem, s);
-  else
-    launch_mfma_bs<QT, FP8, 64>(p, grid, smem, s);
+// Upper bound of the waves that can have work, from host-known sizes.
+int64_t wave_work_bound(const DecodeParams& p) {
+  const int64_t umax = (p.max_len + kStep - 1) / kStep;
+  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+  if (p.mode == kSplitBalanced) return (pairs * umax + p.chunk - 1) / p.chunk;
+  if (p.mode == kSplitNone) return pairs;
+  return pairs * ((umax + p.chunk - 1) / p.chunk);
 }
 
-hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream) {
-  if (p.num_seqs == 0) return hipSuccess;
-  const dim3 grid(p.max_parts, p.num_kv_heads, p.num_seqs);
-  const size_t smem = decode_smem_bytes(p.partition, p.block_size, p.group, p.head_dim);
-  if (p.cache_dtype == kF32) {
-    if (p.head_dim == 128) {
-      if (p.block_size == 16)
-        hipLaunchKernelGGL((decode_f32_kernel<128, 16>), grid, dim3(kThreads), smem, stream, p);
-      else
-        hipLaunchKernelGGL((decode_f32_kernel<128, 32>), grid, dim3(kThreads), smem, stream, p);
-    } else {
-      if (p.block_size == 16)
-        hipLaunchKernelGGL((decode_f32_kernel<64, 16>), grid, dim3(kThreads), smem, stream, p);
-      else
-        hipLaunchKernelGGL((decode_f32_kernel<64, 32>), grid, dim3(kThreads), smem, stream, p);
-    }
-  } else {
-    const bool fp8 = p.cache_dtype == kFP8;
-    if (p.q_dtype == kBF16) {
-      if (fp8) launch_mfma<__bf16, true>(p, grid, smem, stream);
-      else launch_mfma<__bf16, false>(p, grid, smem, stream);
-    } else {
-      if (fp8) launch_mfma<_Float16, true>(p, grid, smem, stream);
-      else launch_mfma<_Float16, false>(p, grid, smem, stream);
-    }
-  }
+template <class Seg, typename QT>
+hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
+  const size_t lds = decode_plan_lds_bytes(p.num_seqs);
+  auto kernel = decode_kernel<Seg, QT>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
+                                                   kThreads, lds) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  int64_t grid = (int64_t)cu_count() * per_cu;
+  const int64_t need = (wave_work_bound(p) + kWaves - 1) / kWaves;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
+template <typename QT, bool FP8, int D>
+hipError_t launch_mfma_bs(const DecodeParams& p, hipStream_t s) {
+  if (p.block_size == 16) return launch_persistent<MfmaDecode<QT, FP8, D, 16>, QT>(p, s);
+  return launch_persistent<MfmaDecode<QT, FP8, D, 32>, QT>(p, s);
+}
+
+template <typename QT, bool FP8>
+hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
+  if (p.head_dim == 128) return launch_mfma_bs<QT, FP8, 128>(p, s);
+  return launch_mfma_bs<QT, FP8, 64>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream) {
+  if (p.num_seqs == 0) return hipSuccess;
+  if (p.cache_dtype == kF32) {
+    if (p.head_dim == 128) {
+      if (p.block_size == 16) return launch_persistent<F32Decode<128, 16>, float>(p, stream);
+      return launch_persistent<F32Decode<128, 32>, float>(p, stream);
+    }
+    if (p.block_size == 16) return launch_persistent<F32Decode<64, 16>, float>(p, stream);
+    return launch_persistent<F32Decode<64, 32>, float>(p, stream);
+  }
+  const bool fp8 = p.cache_dtype == kFP8;
+  if (p.q_dtype == kBF16) return fp8 ? launch_mfma<__bf16, true>(p, stream) : launch_mfma<__bf16, false>(p, stream);
+  return fp8 ? launch_mfma<_Float16, true>(p, stream) : launch_mfma<_Float16, false>(p, stream);
+}
+
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
-  if (p.num_seqs == 0 || p.max_parts <= 1) return hipSuccess;
-  const dim3 grid(p.num_q_heads, p.num_seqs);
+  if (p.num_seqs == 0 || p.mode == kSplitNone) return hipSuccess;
+  const dim3 grid(p.num_kv_heads, p.num_seqs);
   if (p.q_dtype == kF32)
-    hipLaunchKernelGGL(lse_reduce_kernel<float>, grid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(lse_reduce_kernel<float>, grid, dim3(256), 0, stream, p);
   else if (p.q_dtype == kBF16)
-    hipLaunchKernelGGL(lse_reduce_kernel<__bf16>, grid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(lse_reduce_kernel<__bf16>, grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel<_Float16>, grid, dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(lse_reduce_kernel<_Float16>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // kernel dispatch.  Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -70,41 +71,54 @@ pa_status check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim,
 }
 
 struct Plan {
-  int partition;
+  int mode;
+  int chunk;      // units of 32 tokens
   int max_parts;
   int max_len;
   size_t workspace;
 };
 
-int auto_partition(int num_seqs, int num_kv_heads, int max_len) {
-  // Enough workgroups to keep 256 CUs busy several times over without
-  // writing many partials: split only when the unsplit grid is small
-  // relative to the machine or the contexts are long.
-  const long long unsplit = (long long)num_seqs * num_kv_heads;
-  if (max_len <= 512) return -1;
-  if (unsplit >= 4096 && max_len <= 1024) return -1;
-  return 512;
+constexpr int kUnit = 32;              // tokens per unit of decode work
+constexpr int kMaxPlanSeqs = 8000;     // sequences whose plan fits in 64 KB of LDS
+
+// Resolved partition request: > 0 fixed partitions of that many tokens,
+// 0 balanced cut, -1 never split; any other value is invalid.
+bool valid_request(int request, int block_size) {
+  if (request == 0 || request == -1) return true;
+  return request > 0 && request % kUnit == 0 && request % block_size == 0;
 }
 
-int resolve_partition(int num_seqs, int num_kv_heads, int block_size, int max_len, int request) {
-  if (request == 0) request = auto_partition(num_seqs, num_kv_heads, max_len);
-  if (request == -1) {
-    int p = max_len < 32 ? 32 : max_len;
-    p = (p + 31) / 32 * 32;                       // whole 32-token steps
-    p = (p + block_size - 1) / block_size * block_size;
-    return p;
-  }
-  if (request < 0 || request % 32 || request % block_size) return -1;
-  return request;
-}
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
-size_t workspace_for(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
-  if (max_parts <= 1) return 0;
+size_t workspace_for(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_parts) {
   const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-  const size_t o = rows * head_dim * sizeof(float);
-  const size_t ml = rows * sizeof(float);
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return up(o) + 2 * up(ml);
+  return up256(rows * head_dim * sizeof(float)) + 2 * up256(rows * sizeof(float)) +
+         up256((size_t)num_seqs * num_kv_heads * sizeof(int));
+}
+
+void fill_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_len,
+               int request, Plan* plan) {
+  const int umax = (max_len + kUnit - 1) / kUnit;
+  plan->max_len = max_len;
+  if (request == -1) {
+    plan->mode = pa::kSplitNone;
+    plan->chunk = umax > 0 ? umax : 1;
+    plan->max_parts = 1;
+    plan->workspace = 0;
+    return;
+  }
+  if (request == 0) {
+    // Balanced cut: ranges of at least max(8 units, a sixteenth of the
+    // longest context), so a pair splits into at most 17 partials.
+    plan->mode = pa::kSplitBalanced;
+    plan->chunk = std::max(8, (umax + 15) / 16);
+    plan->max_parts = (umax + plan->chunk - 1) / plan->chunk + 1;
+  } else {
+    plan->mode = pa::kSplitFixed;
+    plan->chunk = request / kUnit;
+    plan->max_parts = std::max(1, (umax + plan->chunk - 1) / plan->chunk);
+  }
+  plan->workspace = workspace_for(num_seqs, num_q_heads, num_kv_heads, head_dim, plan->max_parts);
 }
 
 pa_status plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -113,25 +127,18 @@ pa_status plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_
   const long long cap = (long long)max_blocks * block_size;
   if (cap > (1 << 30)) return fail(PA_ERR_UNSUPPORTED, "block table too wide");
   if (max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len < 0");
-  int max_len = (max_seq_len == 0 || max_seq_len > cap) ? (int)cap : max_seq_len;
-  const int part = resolve_partition(num_seqs, num_kv_heads, block_size, max_len, partition_size);
-  if (part <= 0)
+  if (num_seqs > kMaxPlanSeqs)
+    return fail(PA_ERR_UNSUPPORTED, "num_seqs %d > %d per call", num_seqs, kMaxPlanSeqs);
+  if (!valid_request(partition_size, block_size))
     return fail(PA_ERR_INVALID_ARG,
                 "partition_size %d: use 0, -1 or a positive multiple of 32 and of block_size",
                 partition_size);
-  plan->partition = part;
-  plan->max_len = max_len;
-  plan->max_parts = (max_len + part - 1) / part;
-  if (plan->max_parts < 1) plan->max_parts = 1;
-  plan->workspace = workspace_for(num_seqs, num_q_heads, head_dim, plan->max_parts);
-  // LDS of one workgroup: its block-table slice plus the four waves' states.
-  const size_t ntab = (size_t)(part + block_size - 1) / block_size;
-  const size_t lds = (ntab * 4 + 15) / 16 * 16 + 2 * 4 * 16 * 4 +
-                     (size_t)4 * (num_q_heads / num_kv_heads) * head_dim * 4;
-  if (lds > 65536)
-    return fail(PA_ERR_UNSUPPORTED,
-                "partition of %d tokens needs %zu bytes of LDS; use a smaller partition_size",
-                part, lds);
+  const int max_len = (max_seq_len == 0 || max_seq_len > cap) ? (int)cap : max_seq_len;
+  const long long units = (long long)num_seqs * ((max_len + kUnit - 1) / kUnit) * num_kv_heads;
+  if (units > (1LL << 30))
+    return fail(PA_ERR_UNSUPPORTED, "batch too large: %lld (sequence, KV head, 32-token) units",
+                units);
+  fill_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_len, partition_size, plan);
   return PA_OK;
 }
 
@@ -167,7 +174,6 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
                   workspace_bytes);
     if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   }
-  if (plan.max_parts > 0x7FFFFFFF / 2) return fail(PA_ERR_UNSUPPORTED, "too many partitions");
 
   pa::DecodeParams p{};
   p.out = out;
@@ -178,11 +184,13 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   p.seq_lens = seq_lens;
   if (plan.workspace > 0) {
     const size_t rows = (size_t)num_seqs * num_q_heads * plan.max_parts;
-    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     char* ws = static_cast<char*>(workspace);
+    const size_t o_bytes = up256(rows * head_dim * sizeof(float));
+    const size_t ml_bytes = up256(rows * sizeof(float));
     p.part_o = reinterpret_cast<float*>(ws);
-    p.part_m = reinterpret_cast<float*>(ws + up(rows * head_dim * sizeof(float)));
-    p.part_l = reinterpret_cast<float*>(ws + up(rows * head_dim * sizeof(float)) + up(rows * sizeof(float)));
+    p.part_m = reinterpret_cast<float*>(ws + o_bytes);
+    p.part_l = reinterpret_cast<float*>(ws + o_bytes + ml_bytes);
+    p.nparts = reinterpret_cast<int*>(ws + o_bytes + 2 * ml_bytes);
   }
   p.qk_scale_log2 = scale * k_scale * 1.4426950408889634f;
   p.v_scale = v_scale;
@@ -194,7 +202,8 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   p.block_size = block_size;
   p.max_blocks = max_blocks_per_seq;
   p.max_len = plan.max_len;
-  p.partition = plan.partition;
+  p.mode = plan.mode;
+  p.chunk = plan.chunk;
   p.max_parts = plan.max_parts;
   p.q_dtype = q_dtype;
   p.cache_dtype = cache_dtype;
@@ -287,18 +296,22 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs,
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                  int32_t max_seq_len, int32_t partition_size) {
+  (void)num_seqs;
+  (void)num_kv_heads;
   if (max_seq_len <= 0 || (block_size != 16 && block_size != 32)) return -1;
-  return resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  if (!valid_request(partition_size, block_size)) return -1;
+  if (partition_size == -1) return (max_seq_len + kUnit - 1) / kUnit * kUnit;
+  return partition_size;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_seq_len,
                                  int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || max_seq_len <= 0) return 0;
-  const int part = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
-  if (part <= 0) return 0;
-  const int max_parts = (max_seq_len + part - 1) / part;
-  return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 0;
+  if (!valid_request(partition_size, block_size)) return 0;
+  Plan plan;
+  fill_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size, &plan);
+  return plan.workspace;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -107,6 +107,13 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
+// Product rounded on its own (never fused into a following add): a logit
+// formed this way minus the running max is exactly 0 for the max itself.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // ------------------------------------------------------ wave reductions
 
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }

@@ -39,6 +39,14 @@ struct CopyParams {
   int num_pairs;
 };
 
+// How a decode call cuts each (sequence, KV head) pair's context into the
+// segments that single waves process.  Units are 32-token steps.
+enum : int {
+  kSplitBalanced = 0,  // the batch's units are cut into equal contiguous ranges, one per wave
+  kSplitFixed = 1,     // fixed partitions of `chunk` units from each sequence's start
+  kSplitNone = 2       // every pair is processed whole by one wave
+};
+
 struct DecodeParams {
   void* out;
   const void* q;
@@ -46,9 +54,10 @@ struct DecodeParams {
   const void* v_pool;
   const int* block_tables;
   const int* seq_lens;
-  float* part_o;       // [S][Hq][max_parts][D]
-  float* part_m;       // [S][Hq][max_parts]  running max (log2 domain)
-  float* part_l;       // [S][Hq][max_parts]  sum of exponentials
+  float* part_o;       // [S][Hq][max_parts][D]  unnormalised partial outputs
+  float* part_m;       // [S][Hq][max_parts]     running max (log2 domain)
+  float* part_l;       // [S][Hq][max_parts]     sum of exponentials
+  int* nparts;         // [S][Hkv]               segments of each pair
   float qk_scale_log2; // scale * k_scale * log2(e)
   float v_scale;
   int num_seqs;
@@ -59,8 +68,9 @@ struct DecodeParams {
   int block_size;
   int max_blocks;      // block-table row length
   int max_len;         // clamp for seq_lens: min(max_seq_len, max_blocks * block_size)
-  int partition;       // tokens per partition
-  int max_parts;       // partitions in the grid
+  int mode;            // kSplit*
+  int chunk;           // units: fixed partition length, or the shortest balanced range
+  int max_parts;       // partial slots per (sequence, query head)
   int q_dtype;
   int cache_dtype;
 };

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kt * kKeyTile + 16 * a + 4 * G + i;
-          s[a][b][i] = (key <= lim[b]) ? sc[i] * p.qk_scale_log2 : -INFINITY;
+          s[a][b][i] = (key <= lim[b]) ? mul_rn(sc[i], p.qk_scale_log2) : -INFINITY;
         }
       }
     }

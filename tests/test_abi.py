@@ -95,22 +95,32 @@ def test_decode_workspace_required(lib):
     assert b"workspace" in lib.pa_last_error()
 
 
-def test_decode_lds_limit(lib):
-    st = _decode(lib, S=1, mb=1 << 16, msl=1 << 20, part=-1)
-    assert st == UNSUPPORTED
+def test_decode_batch_limits(lib):
+    # the per-call plan holds every sequence's length in LDS
+    assert _decode(lib, S=8001, mb=4, msl=64) == UNSUPPORTED
+    # (sequence, KV head, 32-token) units must stay below 2**30
+    assert _decode(lib, S=8000, hkv=64, hq=64, mb=1 << 16, msl=1 << 20, part=-1) == UNSUPPORTED
 
 
 def test_partition_planning(pa):
     assert pa.pa_decode_partition_size(256, 8, 16, 8192, 512) == 512
     assert pa.pa_decode_partition_size(256, 8, 16, 8192, 48) < 0
+    assert pa.pa_decode_partition_size(256, 8, 16, 8192, 80) < 0      # not a multiple of 32
     assert pa.pa_decode_partition_size(4, 2, 16, 64, -1) >= 64
-    assert pa.pa_decode_partition_size(4, 2, 16, 300, 0) >= 300     # short contexts: no split
+    assert pa.pa_decode_partition_size(4, 2, 16, 300, 0) == 0          # balanced cut
     assert pa.pa_decode_workspace_bytes(4, 2, 2, 64, 16, 64, -1) == 0
-    # [S][Hq][parts][D] floats + two [S][Hq][parts] arrays, each 256-byte aligned
-    n = pa.pa_decode_workspace_bytes(128, 64, 8, 128, 16, 8192, 512)
-    rows = 128 * 64 * 16
     up = lambda x: -(-x // 256) * 256
-    assert n == up(rows * 128 * 4) + 2 * up(rows * 4)
+
+    def layout(S, hq, hkv, d, parts):
+        rows = S * hq * parts
+        return up(rows * d * 4) + 2 * up(rows * 4) + up(S * hkv * 4)
+
+    # fixed partitions: ceil(8192 / 512) = 16 partials per (sequence, query head)
+    assert pa.pa_decode_workspace_bytes(128, 64, 8, 128, 16, 8192, 512) == layout(128, 64, 8, 128, 16)
+    # balanced cut: ranges of >= max(8, ceil(256 / 16)) = 16 units -> at most 16 + 1 partials
+    assert pa.pa_decode_workspace_bytes(128, 64, 8, 128, 16, 8192, 0) == layout(128, 64, 8, 128, 17)
+    # short contexts: ranges of >= 8 units; 2 units -> 1 + 1 partials
+    assert pa.pa_decode_workspace_bytes(4, 2, 2, 64, 16, 64, 0) == layout(4, 2, 2, 64, 2)
 
 
 @pytest.mark.parametrize("kw,code", [
