@@ -162,10 +162,12 @@ def run_decode_bench(args, dev):
                    "head_dim": spec.head_dim, "block_size": spec.block_size,
                    "total_context_tokens": int(lay.seq_lens.sum()), "max_seq_len": max_len,
                    "partition_size": resolved, "rotated_batches": len(batches)},
-        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel" if spec.cache_dtype != "f32"
-                     else "decode_f32_kernel",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<MfmaDecode>" if spec.cache_dtype != "f32"
+                     else "decode_kernel<F32Decode>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": decode_traffic_bytes() if spec.name == "llama2_7b_mha_f16" else None,
+                     "traffic_unit": "bytes per launch",
                      "algorithmic_bytes_per_launch": eff,
                      "avg_launch_ms": round(attn_avg, 5)},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -251,13 +253,50 @@ def run_mixed_bench(args, dev):
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(pre_ms, 5)},
-        "decode_roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel",
+        "decode_roofline": {"bound": "hbm", "kernel": "decode_kernel<MfmaDecode>",
                             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                             "algorithmic_bytes_per_launch": eff, "avg_launch_ms": round(dec_ms, 5)},
         "prefill_tokens_per_s": round(int(case.query_start_loc[-1]) / (pre_ms * 1e-3), 1),
         "decode_tokens_per_s_per_layer": round(len(case.decode_lens) / (ms_step * 1e-3), 1),
     }
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the decode kernel from committed rocprofv3 counter runs
+# ---------------------------------------------------------------------------
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_mfma_llama2_7b_mha_f16.md")
+KERNEL_SOURCES = ["decode.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_415_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def decode_traffic_bytes():
+    """Bytes per launch from the FETCH_SIZE / WRITE_SIZE runs recorded in
+    profiles/, each scaled by what the same counter reads for a copy of known
+    size; None when the counters were taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    line = next((l for l in text.splitlines() if l.startswith("decode_traffic:")), None)
+    if line is None:
+        return None
+    kv = dict(item.split("=", 1) for item in line.split()[1:])
+    if kv.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    copy_bytes = float(kv["copy_bytes"])
+    fetch = float(kv["fetch_kib"]) * copy_bytes / float(kv["copy_fetch_kib"])
+    write = float(kv["write_kib"]) * copy_bytes / float(kv["copy_write_kib"])
+    return int(round(fetch + write))
 
 
 # ---------------------------------------------------------------------------

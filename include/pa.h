@@ -116,21 +116,29 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs,
                          int64_t block_bytes, void* stream);
 
 /*
- * Split-KV planning for decode.  A sequence's context is cut into
- * partitions of partition_size tokens; one workgroup handles one
- * (sequence, KV head, partition) and, when a sequence has more than one
- * partition, a log-sum-exp reduce merges the partial results.
+ * Split-KV planning for decode.  The decode kernel is persistent: each of
+ * its waves processes one or more segments, a segment being a run of
+ * 32-token steps of one (sequence, KV head) pair.  A pair whose context is
+ * cut into several segments gets partial results (unnormalised output,
+ * running max, running sum) in the workspace, and a log-sum-exp reduce
+ * merges them.  partition_size chooses the cut:
+ *   0   : balanced (the default) — the (sequence, KV head, 32-token step)
+ *         units of the whole batch are cut into equal contiguous ranges, one
+ *         per wave, from the lengths on the device; a pair is cut into at
+ *         most 17 segments;
+ *   > 0 : fixed partitions of partition_size tokens from each sequence's
+ *         start (a multiple of 32 and of block_size);
+ *   -1  : never split: every pair is processed whole by one wave.
  *
- * pa_decode_partition_size resolves a requested partition size:
- *   > 0 : used as given (must be a multiple of 32 and of block_size);
- *   0   : the library picks one from the batch shape;
- *   -1  : never split (one partition covers max_seq_len).
- * It returns the resolved size in tokens (>= max_seq_len means no split),
- * or a negative value for an invalid request.
+ * pa_decode_partition_size validates a request and returns it resolved: the
+ * partition length for > 0, 0 for the balanced cut, a value >= max_seq_len
+ * for -1, or a negative value for an invalid request.
  *
- * pa_decode_workspace_bytes returns the workspace pa_decode needs for that
- * plan (0 when nothing is split).  max_seq_len is an upper bound on every
- * seq_lens[s] (0 = max_blocks_per_seq * block_size).
+ * pa_decode_workspace_bytes returns the workspace pa_decode needs (0 for -1):
+ * fp32 partial outputs [S][Hq][max_parts][D], maxima and sums
+ * [S][Hq][max_parts] and int32 segment counts [S][Hkv], each 256-byte
+ * aligned.  max_seq_len is an upper bound on every seq_lens[s]
+ * (0 = max_blocks_per_seq * block_size).
  */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                  int32_t max_seq_len, int32_t partition_size);
@@ -162,7 +170,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   max_seq_len    upper bound used to size the split grid (0 = table width)
  *   partition_size see pa_decode_partition_size
  *   workspace      >= pa_decode_workspace_bytes(...) bytes of device memory,
- *                  256-byte aligned (may be NULL when that is 0)
+ *                  256-byte aligned (may be NULL when that is 0); its
+ *                  contents need no initialisation
+ * Limits: num_seqs <= 8000 (the per-call plan lives in LDS) and
+ * num_seqs * ceil(max_seq_len / 32) * num_kv_heads <= 2^30; beyond them the
+ * call returns PA_ERR_UNSUPPORTED.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, const int32_t* seq_lens, float scale,
@@ -174,13 +186,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_
 
 /*
  * The two stages of pa_decode, for callers that time or schedule them
- * separately.  pa_decode_attention runs the per-(sequence, KV head,
- * partition) kernel: sequences with a single partition get their final
- * output in `out`, the others get partial results in `workspace`.
- * pa_decode_reduce then merges the partials of multi-partition sequences
- * into `out` (a no-op plan when nothing is split).  Both take exactly the
- * arguments of pa_decode; calling them in order on one stream equals one
- * pa_decode call.
+ * separately.  pa_decode_attention runs the attention kernel: pairs
+ * processed as one segment (and empty sequences, which get zeros) have
+ * their final output in `out`, the others leave partial results and their
+ * segment count in `workspace`.  pa_decode_reduce then merges those
+ * partials into `out` (nothing to do for partition_size -1).  Both take
+ * exactly the arguments of pa_decode; calling them in order on one stream
+ * equals one pa_decode call.
  */
 pa_status pa_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, const int32_t* seq_lens, float scale,

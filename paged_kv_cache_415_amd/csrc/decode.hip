@@ -17,9 +17,8 @@
 // of a given length from each sequence's start (items handed out round-robin),
 // and whole pairs (no partials at all).
 //
-// Within a segment a wave walks 32-token steps with the next step's K/V loads
-// in flight while the current step is computed (two register buffers).  The
-// block-table entries of the segment sit in two registers per lane (a window
+// Within a segment a wave walks 32-token steps; K/V are read with 16-byte
+// non-temporal loads (each byte is used once).  The block-table entries of the segment sit in two registers per lane (a window
 // of 128 consecutive entries); the block id of a tile is read out with
 // v_readlane, so tile addresses are scalar.
 //
@@ -174,8 +173,8 @@ struct MfmaDecode {
     uint32_t v[2][4][VW];
   };
 
-  // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).  Tiles
-  // that start past the end re-read the last block (their tokens are masked).
+  // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).  A tile
+  // that starts past the end re-reads the last block (its tokens are masked).
   static __device__ __forceinline__ void load(Buf& buf, TableWindow<BS>& win, const DecodeParams& p,
                                               int kvh, int j) {
     const int lane = threadIdx.x & 63;
@@ -193,23 +192,23 @@ struct MfmaDecode {
       const char* kt = kpool + (tile + (int64_t)c16 * D) * EB;
       if constexpr (FP8) {
 #pragma unroll
-        for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16(kt + 64 * h + 16 * G);
+        for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16_nt(kt + 64 * h + 16 * G);
       } else {
 #pragma unroll
-        for (int c = 0; c < KL; ++c) buf.k[tau][c] = ld16(kt + (32 * c + 8 * G) * 2);
+        for (int c = 0; c < KL; ++c) buf.k[tau][c] = ld16_nt(kt + (32 * c + 8 * G) * 2);
       }
       const char* vt = vpool + (tile + (int64_t)(4 * G) * D + DPL * c16) * EB;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const char* src = vt + (int64_t)i * D * EB;
         if constexpr (VW == 4) {
-          const u32x4 x = ld16(src);
+          const u32x4 x = ld16_nt(src);
           buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y; buf.v[tau][i][2] = x.z; buf.v[tau][i][3] = x.w;
         } else if constexpr (VW == 2) {
-          const u32x2 x = ld8(src);
+          const u32x2 x = ld8_nt(src);
           buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y;
         } else {
-          buf.v[tau][i][0] = ld4(src);
+          buf.v[tau][i][0] = ld4_nt(src);
         }
       }
     }
@@ -348,16 +347,13 @@ struct MfmaDecode {
 #pragma unroll
     for (int n = 0; n < DPL; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two buffers in flight; the prefetch past the segment's end re-reads
-    // its last step (an L2 hit), which keeps every load unconditional.
-    Buf A, B;
-    load(A, win, p, kvh, j0);
-    for (int j = j0; j < j1; j += 2) {
-      load(B, win, p, kvh, min(j + 1, j1 - 1));
-      compute(A, st, qop, p.qk_scale_log2, len, j);
-      if (j + 1 >= j1) break;
-      load(A, win, p, kvh, min(j + 2, j1 - 1));
-      compute(B, st, qop, p.qk_scale_log2, len, j + 1);
+    // One step's K/V in registers at a time: the register budget then allows
+    // two waves per SIMD, whose loads overlap each other's compute (measured
+    // faster on MI355X than two register buffers at one wave per SIMD).
+    for (int j = j0; j < j1; ++j) {
+      Buf buf;
+      load(buf, win, p, kvh, j);
+      compute(buf, st, qop, p.qk_scale_log2, len, j);
     }
 
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n

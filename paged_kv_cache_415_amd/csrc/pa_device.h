@@ -24,6 +24,18 @@ __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<c
 __device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Streaming loads (non-temporal hint): data read once, kept out of the way
+// of the caches' normal replacement.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld8_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ uint32_t ld4_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 // ------------------------------------------------------- 16-bit packing
 
 // Two float32 -> packed 16-bit pair (round to nearest even), low half = a.
