@@ -24,10 +24,14 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 
 ARCH = "gfx950"
-# Packed fp32 VALU ops are kept out of generated code.
+# Packed fp32 VALU ops are kept out of generated code.  MFMA accumulators
+# are kept in ordinary VGPRs: the decode loop rescales them on the VALU, and
+# the AGPR form made the compiler copy every accumulator between the two
+# register files on each step.
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -64,6 +64,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;       // tokens per step (one unit of work)
 constexpr int kMaxPlanSeqs = 8000;
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -267,24 +268,33 @@ struct MfmaDecode {
                        fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     smax = xor_max(smax, 16);
     smax = xor_max(smax, 32);
-    const float m_new = fmaxf(st.m, smax);     // finite: every step has a valid token
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
+    // Lazy rescaling: the reference max moves (and the accumulators are
+    // rescaled) only when some head's max exceeds it by more than
+    // kRescaleSlack, so probabilities stay <= 2^kRescaleSlack.  The first
+    // step always sets it (st.m starts at -inf; every step has a valid token).
+    if (__builtin_amdgcn_ballot_w64(smax > st.m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(st.m, smax);
+      const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+      st.m = m_new;
+      st.l *= alpha;
+#pragma unroll
+      for (int n = 0; n < DPL; ++n) st.acc[n] = st.acc[n] * alpha;
+    }
     uint32_t pw[4];
     float psum = 0.f;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
-        const float a = __builtin_amdgcn_exp2f(s[tau][i] - m_new);
-        const float b = __builtin_amdgcn_exp2f(s[tau][i + 1] - m_new);
+        const float a = __builtin_amdgcn_exp2f(s[tau][i] - st.m);
+        const float b = __builtin_amdgcn_exp2f(s[tau][i + 1] - st.m);
         const uint32_t w = pack2<QT>(a, b);
         pw[tau * 2 + i / 2] = w;
         // sum the rounded probabilities so that the weights stay normalised
         psum += lo_f32<QT>(w) + hi_f32<QT>(w);
       }
     }
-    st.l = st.l * alpha + psum;
+    st.l += psum;
     const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]};
 
     // Values: A operand for dim DPL*c16 + n holds tokens 4G+0..3 of tile 0
@@ -311,7 +321,6 @@ struct MfmaDecode {
         a = u32x4{perm(buf.v[0][1][w], buf.v[0][0][w], sel), perm(buf.v[0][3][w], buf.v[0][2][w], sel),
                   perm(buf.v[1][1][w], buf.v[1][0][w], sel), perm(buf.v[1][3][w], buf.v[1][2][w], sel)};
       }
-      st.acc[n] = st.acc[n] * alpha;
       st.acc[n] = Mma<QT>::mma(a, pop, st.acc[n]);
     }
   }
@@ -395,8 +404,9 @@ struct MfmaDecode {
 };
 
 // ---------------------------------------------------------------------------
-// fp32 segment (VALU): the small fp32 workloads.  One token at a time, the
-// head dimension spread over the lanes.
+// fp32 segment (VALU): the small fp32 workloads.  The head dimension is
+// spread over the lanes; tokens are taken one at a time from groups of 16
+// whose rows were loaded together.
 // ---------------------------------------------------------------------------
 template <int D, int BS>
 struct F32Decode {
@@ -422,33 +432,44 @@ struct F32Decode {
     const float* kpool = reinterpret_cast<const float*>(p.k_pool);
     const float* vpool = reinterpret_cast<const float*>(p.v_pool);
     const int t_end = min(j1 * kStep, len);
-    for (int t = j0 * kStep; t < t_end; ++t) {
-      const int bi = t / BS;
-      win.ensure(bi);
-      const int blk = win.get(bi);
-      const int64_t rowoff = (((int64_t)blk * p.num_kv_heads + kvh) * BS + t % BS) * D;
-      float kv[E], vv[E];
+    // 16 tokens' rows are loaded before any is used, so one memory latency
+    // covers 16 tokens (past the end, the last token's row is re-read).
+    constexpr int kGroup = 16;
+    for (int t0 = j0 * kStep; t0 < t_end; t0 += kGroup) {
+      float kv[kGroup][E], vv[kGroup][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        kv[e] = kpool[rowoff + lane + 64 * e];
-        vv[e] = vpool[rowoff + lane + 64 * e];
+      for (int k = 0; k < kGroup; ++k) {
+        const int t = min(t0 + k, t_end - 1);
+        const int bi = t / BS;
+        win.ensure(bi);
+        const int blk = win.get(bi);
+        const int64_t rowoff = (((int64_t)blk * p.num_kv_heads + kvh) * BS + t % BS) * D;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kv[k][e] = kpool[rowoff + lane + 64 * e];
+          vv[k][e] = vpool[rowoff + lane + 64 * e];
+        }
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < g) {
-          float dot = 0.f;
+      for (int k = 0; k < kGroup; ++k) {
+        if (t0 + k >= t_end) break;
 #pragma unroll
-          for (int e = 0; e < E; ++e) dot += qv[j][e] * kv[e];
+        for (int j = 0; j < 16; ++j) {
+          if (j < g) {
+            float dot = 0.f;
 #pragma unroll
-          for (int msk = 32; msk >= 1; msk >>= 1) dot = xor_sum(dot, msk);
-          const float sc = mul_rn(dot, p.qk_scale_log2);
-          const float m_new = fmaxf(m[j], sc);
-          const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
-          const float pr = __builtin_amdgcn_exp2f(sc - m_new);
-          l[j] = l[j] * alpha + pr;
+            for (int e = 0; e < E; ++e) dot += qv[j][e] * kv[k][e];
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[j][e] = acc[j][e] * alpha + pr * vv[e];
-          m[j] = m_new;
+            for (int msk = 32; msk >= 1; msk >>= 1) dot = xor_sum(dot, msk);
+            const float sc = mul_rn(dot, p.qk_scale_log2);
+            const float m_new = fmaxf(m[j], sc);
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+            const float pr = __builtin_amdgcn_exp2f(sc - m_new);
+            l[j] = l[j] * alpha + pr;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[j][e] = acc[j][e] * alpha + pr * vv[k][e];
+            m[j] = m_new;
+          }
         }
       }
     }

@@ -108,10 +108,10 @@ void fill_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
     return;
   }
   if (request == 0) {
-    // Balanced cut: ranges of at least max(8 units, a sixteenth of the
+    // Balanced cut: ranges of at least max(2 units, a sixteenth of the
     // longest context), so a pair splits into at most 17 partials.
     plan->mode = pa::kSplitBalanced;
-    plan->chunk = std::max(8, (umax + 15) / 16);
+    plan->chunk = std::max(2, (umax + 15) / 16);
     plan->max_parts = (umax + plan->chunk - 1) / plan->chunk + 1;
   } else {
     plan->mode = pa::kSplitFixed;

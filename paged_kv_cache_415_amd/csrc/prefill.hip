@@ -7,11 +7,14 @@
 // keys 0 .. n - L + i, all read through the block table.
 //
 // Work decomposition: one workgroup (four wave64s) per (tile of query rows,
-// KV head, sequence).  A tile holds 128 query rows = (128 / group)
+// KV head, sequence), mapped so that all query tiles of one (sequence, KV
+// head) run on one XCD.  A tile holds 128 query rows = (128 / group)
 // consecutive chunk positions x the group's query heads, so one staged K/V
 // tile serves every head of the group.  The workgroup walks the context in
 // 64-key tiles: the tile's rows are gathered through the LDS-cached block
-// table into LDS with 16-byte loads, then each wave (32 query rows) forms
+// table with 16-byte loads (the next tile's loads are in flight while the
+// current one is computed) and stored to LDS, then each wave (32 query rows)
+// forms
 //   S^T[key][row] = K[key][:] . Q[row][:]            (v_mfma_f32_16x16x32)
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row]     (v_mfma_f32_16x16x32)
 // with an online softmax per query row.  As in the decode kernel, the score
@@ -44,6 +47,11 @@ struct PMma<_Float16> {
 constexpr int kPThreads = 256;
 constexpr int kRowsPerWG = 128;
 constexpr int kKeyTile = 64;
+constexpr float kSlack = 8.0f;   // log2 units
+constexpr int kXcds = 8;
+template <typename T> constexpr uint32_t kOnes = 0;                  // two 1.0 values
+template <> constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
+template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;         // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 size_t prefill_smem_bytes(int head_dim, int max_blocks) {
   const int stride = head_dim + 8;  // padded row, in elements
@@ -61,12 +69,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   T* v_lds = k_lds + kKeyTile * STRIDE;
   int* tab = reinterpret_cast<int*>(v_lds + kKeyTile * STRIDE);
 
-  const int seq = blockIdx.z, kvh = blockIdx.y;
+  // Workgroup `lin` runs on XCD lin % kXcds.  Each XCD gets a contiguous
+  // range of work items (query tile fastest), so the query tiles that read
+  // one (sequence, KV head) context run on the same XCD and share its L2.
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xq = nwg / kXcds, xr = nwg % kXcds;
+  const int xcd = lin % kXcds, slot = lin / kXcds;
+  const int work = xcd * xq + min(xcd, xr) + slot;   // a bijection of [0, nwg)
+  const int qtile = work % gridDim.x;
+  const int kvh = (work / gridDim.x) % gridDim.y;
+  const int seq = work / (gridDim.x * gridDim.y);
   const int g = p.group;
   const int qpos = kRowsPerWG / g;          // chunk positions per workgroup
   const int q0 = p.query_start_loc[seq];
   const int L = p.query_start_loc[seq + 1] - q0;
-  const int p0 = blockIdx.x * qpos;
+  const int p0 = qtile * qpos;
   if (p0 >= L) return;
   int n = p.seq_lens[seq];
   const int cap = p.max_blocks * BS;
@@ -81,6 +99,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = lane >> 4, c16 = lane & 15;
+  // logit = c * (q . k) with c = scale * k_scale * log2(e); a negative c is
+  // applied as |c| with q negated, so maxima of raw products are maxima of
+  // logits
+  // (a zero scale runs as the smallest normal float, which rounds every
+  // logit to 0 just the same but keeps -inf * scale = -inf for masked keys)
+  const bool neg = p.qk_scale_log2 < 0.f;
+  const float cscale = fmaxf(neg ? -p.qk_scale_log2 : p.qk_scale_log2, 1.17549435e-38f);
 
   // This lane's query row in each of the wave's two column tiles.
   int pos[2], head[2];
@@ -97,41 +122,72 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     const T* qrow = reinterpret_cast<const T*>(p.q) +
                     ((int64_t)(q0 + pos[b]) * p.num_q_heads + kvh * g + head[b]) * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qop[b][c] = valid[b] ? ld16(qrow + 32 * c + 8 * G) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NC; ++c) {
+      qop[b][c] = valid[b] ? ld16(qrow + 32 * c + 8 * G) : u32x4{0, 0, 0, 0};
+      if (neg) qop[b][c] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
   }
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x4 acc[2][DPL];
+  // Running max (in logit units, log2 domain), unnormalised outputs, and the
+  // row sums of the rounded probabilities, formed on the matrix cores by a
+  // value product against an all-ones operand (every row of acc_l holds the
+  // column's sum).
+  float m_run[2] = {-INFINITY, -INFINITY};
+  f32x4 acc[2][DPL], acc_l[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < 2; ++b) {
+    acc_l[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nn = 0; nn < DPL; ++nn) acc[b][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4 ones = {kOnes<T>, kOnes<T>, kOnes<T>, kOnes<T>};
+  // first tile that needs the causal mask: every row sees keys <= ctx0 + p0
+  const int min_lim = ctx0 + p0;
 
   const char* kpool = reinterpret_cast<const char*>(p.k_pool);
   const char* vpool = reinterpret_cast<const char*>(p.v_pool);
   const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
   __syncthreads();   // block-table slice visible
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // ---- gather the 64-key K/V tile through the block table into LDS
+  // The next tile's K/V rows are fetched into registers while the current
+  // tile is computed; they go to LDS between two barriers.
+  constexpr int NV = kKeyTile * VPR / kPThreads;   // 16-byte vectors per thread and tile
+  u32x4 kx[NV], vx[NV];
+  auto gather = [&](int kt) {
 #pragma unroll
-    for (int it = 0; it < kKeyTile * VPR / kPThreads; ++it) {
+    for (int it = 0; it < NV; ++it) {
       const int idx = it * kPThreads + threadIdx.x;
       const int row = idx / VPR, vec = idx % VPR;
       const int key = kt * kKeyTile + row;
-      u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+      kx[it] = u32x4{0, 0, 0, 0};
+      vx[it] = u32x4{0, 0, 0, 0};
       if (key < kend) {
         const int blk = tab[key / BS];
         const int64_t off = ((((int64_t)blk * p.num_kv_heads + kvh) * BS + key % BS) * D + vec * 8) * 2;
-        kx = ld16(kpool + off);
-        vx = ld16(vpool + off);
+        kx[it] = ld16(kpool + off);
+        vx[it] = ld16(vpool + off);
       }
-      st16(k_lds + row * STRIDE + vec * 8, kx);
-      st16(v_lds + row * STRIDE + vec * 8, vx);
     }
-    __syncthreads();
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int idx = it * kPThreads + threadIdx.x;
+      const int row = idx / VPR, vec = idx % VPR;
+      st16(k_lds + row * STRIDE + vec * 8, kx[it]);
+      st16(v_lds + row * STRIDE + vec * 8, vx[it]);
+    }
+  };
+  gather(0);
+  stash();
+  __syncthreads();
 
-    // ---- scores for 4 key row-tiles x 2 query column-tiles
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const bool more = kt + 1 < ntiles;     // uniform over the workgroup
+    if (more) gather(kt + 1);
+
+    // ---- raw products q.k for 4 key row-tiles x 2 query column-tiles
+    const bool diag = kt * kKeyTile + kKeyTile - 1 > min_lim;   // uniform
     float s[4][2][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -145,44 +201,52 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
 #pragma unroll
         for (int c = 0; c < NC; ++c) sc = PMma<T>::mma(ka[c], qop[b][c], sc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt * kKeyTile + 16 * a + 4 * G + i;
-          s[a][b][i] = (key <= lim[b]) ? mul_rn(sc[i], p.qk_scale_log2) : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) s[a][b][i] = sc[i];
       }
     }
-    // ---- online softmax per query row (lane column), probabilities -> operands
-    u32x4 pop[2][2];   // [key pair][column tile]
-    float alpha[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = -INFINITY;
+    if (diag) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[a][b][i]);
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kt * kKeyTile + 16 * a + 4 * G + i > lim[b]) s[a][b][i] = -INFINITY;
+    }
+    // ---- online softmax per query row (lane column), probabilities -> operands
+    u32x4 pop[2][2];   // [key pair][column tile]
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float mx = fmaxf(fmaxf(fmaxf(s[0][b][0], s[0][b][1]), fmaxf(s[0][b][2], s[0][b][3])),
+                       fmaxf(fmaxf(s[1][b][0], s[1][b][1]), fmaxf(s[1][b][2], s[1][b][3])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][b][0], s[2][b][1]), fmaxf(s[2][b][2], s[2][b][3])),
+                           fmaxf(fmaxf(s[3][b][0], s[3][b][1]), fmaxf(s[3][b][2], s[3][b][3]))));
       mx = xor_max(mx, 16);
       mx = xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[b], mx);
-      alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_new);
-      m_run[b] = m_new;
-      float psum = 0.f;
+      mx *= cscale;   // cscale > 0: -inf stays -inf
+      // Lazy rescaling (as in decode): the reference max moves only when a
+      // row's max exceeds it by more than kSlack, so p <= 2^kSlack.  A row
+      // whose keys are all masked in this tile has mx = -inf and keeps it.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[b] + kSlack) != 0) {
+        const float m_new = fmaxf(m_run[b], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
+        m_run[b] = m_new;
+        acc_l[b] = acc_l[b] * alpha;
+#pragma unroll
+        for (int nn = 0; nn < DPL; ++nn) acc[b][nn] = acc[b][nn] * alpha;
+      }
+      // p = 2^(c * (q.k) - m): one fused multiply-add per score
+      const float nm = -m_run[b];
       uint32_t w[4][2];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const uint32_t pw = pack2<T>(__builtin_amdgcn_exp2f(s[a][b][i] - m_new),
-                                       __builtin_amdgcn_exp2f(s[a][b][i + 1] - m_new));
-          w[a][i / 2] = pw;
-          psum += lo_f32<T>(pw) + hi_f32<T>(pw);
-        }
-      l_run[b] = l_run[b] * alpha[b] + psum;
+        for (int i = 0; i < 4; i += 2)
+          w[a][i / 2] = pack2<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i], cscale, nm)),
+                                 __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i + 1], cscale, nm)));
 #pragma unroll
       for (int ap = 0; ap < 2; ++ap)
         pop[ap][b] = u32x4{w[2 * ap][0], w[2 * ap][1], w[2 * ap + 1][0], w[2 * ap + 1][1]};
-#pragma unroll
-      for (int nn = 0; nn < DPL; ++nn) acc[b][nn] = acc[b][nn] * alpha[b];
     }
     // ---- values: A operand rows = dims DPL*c16 + nn, k-slots = keys of a pair
 #pragma unroll
@@ -210,17 +274,21 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[b][nn] = PMma<T>::mma(va, pop[ap][b], acc[b][nn]);
       }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[ap][b], acc_l[b]);
     }
-    __syncthreads();   // tile consumed before the next gather overwrites it
+    if (more) {
+      __syncthreads();   // every wave is done with this tile
+      stash();
+      __syncthreads();   // the next tile is visible
+    }
   }
 
   // ---- normalise and store: lane (G, c16) holds dims DPL*(4G+i) + nn of its row
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    float l = xor_sum(l_run[b], 16);
-    l = xor_sum(l, 32);
     if (!valid[b]) continue;
-    const float inv = p.v_scale / l;
+    const float inv = p.v_scale / acc_l[b][0];
     T* orow = reinterpret_cast<T*>(p.out) +
               ((int64_t)(q0 + pos[b]) * p.num_q_heads + kvh * g + head[b]) * D;
 #pragma unroll

@@ -119,7 +119,7 @@ def test_partition_planning(pa):
     assert pa.pa_decode_workspace_bytes(128, 64, 8, 128, 16, 8192, 512) == layout(128, 64, 8, 128, 16)
     # balanced cut: ranges of >= max(8, ceil(256 / 16)) = 16 units -> at most 16 + 1 partials
     assert pa.pa_decode_workspace_bytes(128, 64, 8, 128, 16, 8192, 0) == layout(128, 64, 8, 128, 17)
-    # short contexts: ranges of >= 8 units; 2 units -> 1 + 1 partials
+    # short contexts: ranges of >= 2 units; 2 units -> 1 + 1 partials
     assert pa.pa_decode_workspace_bytes(4, 2, 2, 64, 16, 64, 0) == layout(4, 2, 2, 64, 2)
 
 

@@ -178,3 +178,70 @@ def test_shape_sweep(q_dt, c_dt, hq, hkv, d, bs, partition):
     assert np.array_equal(W.torch_to_bits(run.k_pool, c_dt), okp)
     out = run.decode(partition_size=partition)
     assert max_abs(out, ref) <= TOL[q_dt]
+
+
+def _rewrite_k_dim0(case, values_per_seq, k_scale=None):
+    """Set dimension 0 of every K row of head 0 to the given per-token values
+    (the newest token's through the scatter input); other dims keep their
+    values.  For an fp8 cache the pool is re-encoded with k_scale."""
+    s = case.spec
+    bs, dt = s.block_size, s.cache_dtype
+    old_scale = case.k_scale
+    kf = W.bits_to_torch(case.k_pool, dt).float().numpy() * np.float32(old_scale)
+    nk = W.bits_to_torch(case.new_k, case.src_dtype).float().numpy()
+    for q, vals in enumerate(values_per_seq):
+        n = int(case.seq_lens[q])
+        for j in range(n - 1):
+            kf[case.block_tables[q, j // bs], 0, j % bs, 0] = vals[j]
+        nk[q, 0, 0] = vals[n - 1]
+    if k_scale is not None:
+        case.k_scale = float(np.float32(k_scale))
+    case.k_pool = W.to_bits(kf / np.float32(case.k_scale) if dt == "fp8_e4m3" else kf, dt)
+    case.new_k = W.to_bits(nk, case.src_dtype)
+
+
+@pytest.mark.parametrize("q_dt,c_dt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8_e4m3"),
+                                       ("f32", "f32")])
+@pytest.mark.parametrize("partition", [0, -1])
+def test_running_max_moves_many_times(q_dt, c_dt, partition):
+    """Logits that rise along the context, fall, jump at the last token or
+    saw-tooth: the running max must move many times inside one segment, by
+    small and by large steps (the decode kernel defers rescaling until the
+    max has grown by 2^8)."""
+    spec = custom_spec(f"trend_{q_dt}_{c_dt}", 4, 1, 128, 16, q_dt, c_dt)
+    lens = [1500, 700, 64, 333]
+    case = W.make_decode_case(spec, lens=lens)
+    trends = [np.linspace(0.0, 85.0, 1500), np.linspace(85.0, 0.0, 700),
+              np.r_[np.zeros(63), 100.0], (np.arange(333) % 50) * 1.5]
+    _rewrite_k_dim0(case, trends, k_scale=100.0 / 448.0 if c_dt == "fp8_e4m3" else None)
+    qf = np.zeros((len(lens), 4, 128), np.float32)
+    qf[:, :, 0] = [8.0, 4.0, -8.0, 1.0]          # logit = scale * q0 * k0
+    case.q = W.to_bits(qf, q_dt)
+    ref, okp, _ = oracle_step(case)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(run.k_pool, c_dt), okp)
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL[q_dt]
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.4])
+def test_decode_any_scale(scale):
+    """Zero scale (uniform weights) and a negative scale against the oracle."""
+    spec = custom_spec("scale_sweep", 8, 2, 128, 16, "bf16", "bf16")
+    case = W.make_decode_case(spec, lens=[1, 40, 333, 1000])
+    s = case.spec
+    kp, vp = oracle.reshape_and_cache(case.k_pool, case.v_pool, s.cache_dtype, case.new_k,
+                                      case.new_v, case.src_dtype, case.slot_mapping, s.block_size)
+    ref = oracle.decode_attention(case.q, s.q_dtype, kp, vp, s.cache_dtype, case.block_tables,
+                                  case.seq_lens, scale, s.block_size, s.num_kv_heads)
+    run = DecodeRun(case)
+    run.scatter()
+    pa = lib()
+    out = torch.empty_like(run.q)
+    ws = pa.decode_workspace(run.q, run.k_pool, run.max_len, 0)
+    pa.pa_decode(out, run.q, run.k_pool, run.v_pool, run.tables, run.lens, scale,
+                 max_seq_len=run.max_len, workspace=ws)
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= TOL["bf16"]

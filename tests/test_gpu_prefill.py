@@ -153,3 +153,46 @@ def test_mixed_step_full_size():
     err = float(np.abs(sampled - ref_c).max())
     print(f"[mixed] prefill sampled max-abs {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_rising_logits_move_the_running_max(dtype):
+    """Each row's logits rise along the keys, so every 64-key tile raises
+    every row's max (the kernel defers rescaling until the max has grown by
+    2^8): many small and some large moves per row."""
+    rng = np.random.default_rng(11)
+    chunks, ctxs = [200, 37], [700, 300]
+    hq, hkv, d, bs = 8, 2, 128, 16
+    q, qsl, kp, vp, tables, lens = _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype)
+    kf = W.bits_to_torch(kp, dtype).float().numpy()
+    for s, n in enumerate(ctxs):
+        for j in range(n):
+            kf[tables[s, j // bs], :, j % bs, 0] = 0.12 * j * (1 if s == 0 else -1) + (j % 7)
+    kp = W.to_bits(kf, dtype)
+    qf = np.zeros((int(qsl[-1]), hq, d), np.float32)
+    qf[:, :, 0] = np.linspace(0.5, 4.0, hq)
+    q = W.to_bits(qf, dtype)
+    scale = 1.0 / np.sqrt(d)
+    ref = oracle.prefill_chunk_attention(q, dtype, qsl, kp, vp, dtype, tables, lens, scale, bs, hkv)
+    gq = up(q, dtype)
+    out = torch.empty_like(gq)
+    lib().pa_prefill_chunk(out, gq, up_int(qsl), up(kp, dtype), up(vp, dtype), up_int(tables),
+                           up_int(lens), scale, max(chunks))
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 1e-3, 0.4])
+def test_prefill_any_scale(scale):
+    """Zero scale (every visible key equally weighted) and a negative scale
+    (the kernel folds the sign into the query) against the oracle."""
+    rng = np.random.default_rng(21)
+    chunks, ctxs = [70, 9], [150, 9]
+    q, qsl, kp, vp, tables, lens = _random_chunks(rng, chunks, ctxs, 8, 2, 128, 32, "bf16")
+    ref = oracle.prefill_chunk_attention(q, "bf16", qsl, kp, vp, "bf16", tables, lens, scale, 32, 2)
+    gq = up(q, "bf16")
+    out = torch.empty_like(gq)
+    lib().pa_prefill_chunk(out, gq, up_int(qsl), up(kp, "bf16"), up(vp, "bf16"), up_int(tables),
+                           up_int(lens), scale, max(chunks))
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= TOL["bf16"]
