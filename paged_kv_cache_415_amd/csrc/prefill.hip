@@ -49,13 +49,31 @@ constexpr int kRowsPerWG = 128;
 constexpr int kKeyTile = 64;
 constexpr float kSlack = 8.0f;   // log2 units
 constexpr int kXcds = 8;
+// Column of key k (0..63) of a tile in the transposed V tile: the key index
+// [ap:1][h:1][G:2][i:2] becomes [ap][G][h][i], so that the keys a lane holds
+// in the probability operand (tiles 2ap and 2ap+1, rows 4G + i) are adjacent.
+__device__ __forceinline__ int vt_col(int k) {
+  return (k & 0x20) | ((k & 0x0C) << 1) | ((k & 0x10) >> 2) | (k & 3);
+}
+
+// Byte offset of (dimension d, column col) in the transposed V tile: rows of
+// 64 keys (128 B), taken in pairs as 256-byte lines whose sixteen 16-byte
+// chunks are XOR-swizzled by d / (D/16), so that the 16 lanes reading one
+// operand (dimensions (D/16) * c16 + nn) hit 16 different chunks.
+template <int D>
+__device__ __forceinline__ int vt_offset(int d, int col) {
+  const int swz = (d / (D / 16)) & 15;
+  const int chunk = (((d & 1) << 3) | (col >> 3)) ^ swz;
+  return (d >> 1) * 256 + chunk * 16 + (col & 7) * 2;
+}
+
 template <typename T> constexpr uint32_t kOnes = 0;                  // two 1.0 values
 template <> constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
 template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;         // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 size_t prefill_smem_bytes(int head_dim, int max_blocks) {
-  const int stride = head_dim + 8;  // padded row, in elements
-  return (size_t)2 * kKeyTile * stride * 2 + (size_t)max_blocks * 4;
+  const int stride = head_dim + 8;  // padded K row, in elements
+  return (size_t)kKeyTile * stride * 2 + (size_t)head_dim * kKeyTile * 2 + (size_t)max_blocks * 4;
 }
 
 template <typename T, int D, int BS>
@@ -63,11 +81,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   extern __shared__ __align__(16) char smem_raw[];
   constexpr int NC = D / 32;
   constexpr int DPL = D / 16;
-  constexpr int STRIDE = D + 8;             // LDS row stride (elements): spreads banks
+  constexpr int STRIDE = D + 8;             // K row stride in LDS (elements): spreads banks
   constexpr int VPR = D / 8;                // 16-byte vectors per row
+  constexpr int KPT = kKeyTile * VPR / kPThreads;   // keys per thread in a tile's gather
   T* k_lds = reinterpret_cast<T*>(smem_raw);
-  T* v_lds = k_lds + kKeyTile * STRIDE;
-  int* tab = reinterpret_cast<int*>(v_lds + kKeyTile * STRIDE);
+  char* vt_lds = reinterpret_cast<char*>(k_lds + kKeyTile * STRIDE);   // V^T, D x 64 keys
+  int* tab = reinterpret_cast<int*>(vt_lds + D * kKeyTile * 2);
 
   // Workgroup `lin` runs on XCD lin % kXcds.  Each XCD gets a contiguous
   // range of work items (query tile fastest), so the query tiles that read
@@ -150,32 +169,45 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   __syncthreads();   // block-table slice visible
 
   // The next tile's K/V rows are fetched into registers while the current
-  // tile is computed; they go to LDS between two barriers.
-  constexpr int NV = kKeyTile * VPR / kPThreads;   // 16-byte vectors per thread and tile
-  u32x4 kx[NV], vx[NV];
+  // tile is computed; they go to LDS between two barriers.  Thread t loads
+  // the 16-byte piece `vec` of KPT consecutive keys (a 16-lane group reads a
+  // whole 256-byte row).  K is stored row-major; V is stored transposed (one
+  // LDS row per dimension) with its keys permuted by vt_col, in the order in
+  // which the probability operand holds them, so a lane's eight keys of one
+  // dimension are 16 contiguous bytes (one ds_read_b128, no byte permutes).
+  const int g_vec = threadIdx.x % VPR, g_kq = threadIdx.x / VPR;
+  u32x4 kx[KPT], vx[KPT];
   auto gather = [&](int kt) {
 #pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int idx = it * kPThreads + threadIdx.x;
-      const int row = idx / VPR, vec = idx % VPR;
-      const int key = kt * kKeyTile + row;
-      kx[it] = u32x4{0, 0, 0, 0};
-      vx[it] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < KPT; ++i) {
+      const int key = kt * kKeyTile + g_kq * KPT + i;
+      kx[i] = u32x4{0, 0, 0, 0};
+      vx[i] = u32x4{0, 0, 0, 0};
       if (key < kend) {
         const int blk = tab[key / BS];
-        const int64_t off = ((((int64_t)blk * p.num_kv_heads + kvh) * BS + key % BS) * D + vec * 8) * 2;
-        kx[it] = ld16(kpool + off);
-        vx[it] = ld16(vpool + off);
+        const int64_t off = ((((int64_t)blk * p.num_kv_heads + kvh) * BS + key % BS) * D + g_vec * 8) * 2;
+        kx[i] = ld16(kpool + off);
+        vx[i] = ld16(vpool + off);
       }
     }
   };
   auto stash = [&]() {
 #pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int idx = it * kPThreads + threadIdx.x;
-      const int row = idx / VPR, vec = idx % VPR;
-      st16(k_lds + row * STRIDE + vec * 8, kx[it]);
-      st16(v_lds + row * STRIDE + vec * 8, vx[it]);
+    for (int i = 0; i < KPT; ++i) st16(k_lds + (g_kq * KPT + i) * STRIDE + g_vec * 8, kx[i]);
+    // transpose KPT keys x 8 dims into 8 dims x KPT keys (16-bit lanes)
+    const int col = vt_col(g_kq * KPT);     // KPT consecutive keys stay consecutive
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = g_vec * 8 + e;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      char* dst = vt_lds + vt_offset<D>(d, col);
+      if constexpr (KPT == 4) {
+        const uint32_t w0 = perm(vx[1][e >> 1], vx[0][e >> 1], sel);
+        const uint32_t w1 = perm(vx[3][e >> 1], vx[2][e >> 1], sel);
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = perm(vx[1][e >> 1], vx[0][e >> 1], sel);
+      }
     }
   };
   gather(0);
@@ -248,29 +280,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
       for (int ap = 0; ap < 2; ++ap)
         pop[ap][b] = u32x4{w[2 * ap][0], w[2 * ap][1], w[2 * ap + 1][0], w[2 * ap + 1][1]};
     }
-    // ---- values: A operand rows = dims DPL*c16 + nn, k-slots = keys of a pair
+    // ---- values: A operand rows = dims DPL*c16 + nn, k-slots = the lane's
+    // eight keys (keys 32ap + 4G + 0..3 and 32ap + 16 + 4G + 0..3), which
+    // V^T holds contiguously at columns 32ap + 8G .. 32ap + 8G + 7
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap) {
-      uint32_t vr[2][4][DPL / 2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const T* src = v_lds + (16 * (2 * ap + half) + 4 * G + i) * STRIDE + DPL * c16;
-          if constexpr (DPL == 8) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-            vr[half][i][0] = x.x; vr[half][i][1] = x.y; vr[half][i][2] = x.z; vr[half][i][3] = x.w;
-          } else {
-            const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-            vr[half][i][0] = x.x; vr[half][i][1] = x.y;
-          }
-        }
 #pragma unroll
       for (int nn = 0; nn < DPL; ++nn) {
-        const int w = nn >> 1;
-        const uint32_t sel = (nn & 1) ? 0x07060302u : 0x05040100u;
-        const u32x4 va = {perm(vr[0][1][w], vr[0][0][w], sel), perm(vr[0][3][w], vr[0][2][w], sel),
-                          perm(vr[1][1][w], vr[1][0][w], sel), perm(vr[1][3][w], vr[1][2][w], sel)};
+        const u32x4 va = *reinterpret_cast<const u32x4*>(
+            vt_lds + vt_offset<D>(DPL * c16 + nn, 32 * ap + 8 * G));
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[b][nn] = PMma<T>::mma(va, pop[ap][b], acc[b][nn]);
       }
