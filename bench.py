@@ -19,6 +19,9 @@ torch's seeded generator (same distributions).  R batches with separate
 pools are rotated so that no step finds its KV in the 256 MB last-level
 cache.
 
+After the timed region the same steps are also replayed from captured HIP
+graphs (one per batch) and that rate is reported beside the eager one.
+
 Printed: one JSON line with the step rate, a roofline object for the
 dominant kernel (its average duration measured with HIP events on the
 launch stream) and a CPU baseline (the fp64 oracle on a bounded sample, on
@@ -136,6 +139,7 @@ def run_decode_bench(args, dev):
     for i in range(args.warmup):
         step(batches[i % len(batches)])
     torch.cuda.synchronize()
+
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -144,6 +148,27 @@ def run_decode_bench(args, dev):
     elapsed = time.perf_counter() - t0
     attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
     red_ms = [e[1].elapsed_time(e[2]) for e in evs]
+
+    # After the timed region: the same steps replayed from captured HIP graphs
+    # (one graph per batch), as a serving loop replays captured decode steps.
+    graph_ms = None
+    try:
+        graphs = []
+        for b in batches:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(b)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    except RuntimeError as exc:
+        print(f"bench.py: hipGraph replay skipped ({exc})", file=sys.stderr)
     assert not torch.isnan(b0.out).any(), "NaN in decode output"
 
     eff = W.effective_kv_bytes(lay.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
@@ -175,6 +200,8 @@ def run_decode_bench(args, dev):
         "decode_gbps_attention_plus_reduce": round(
             eff / ((attn_avg + float(np.mean(red_ms))) * 1e-3) / 1e9, 1),
         "reduce_avg_ms": round(float(np.mean(red_ms)), 5),
+        "hipgraph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "hipgraph_gbps": None if graph_ms is None else round(eff / (graph_ms * 1e-3) / 1e9, 1),
         "attention_p10_p50_p90_ms": [round(float(x), 5) for x in
                                       np.percentile(attn_ms, [10, 50, 90])],
         "effective_kv_bytes_per_step": eff,
