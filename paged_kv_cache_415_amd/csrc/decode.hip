@@ -5,22 +5,23 @@
 // query attends every cached token of the sequence, whose K/V are found
 // block by block through the block table.
 //
-// Scheduling.  The grid is persistent: as many workgroups (four independent
-// wave64s each) as stay resident on the device.  Every workgroup first reads
-// the batch's lengths into LDS and forms the prefix sum of each sequence's
-// count of 32-token steps ("units").  The units of all (sequence, KV head)
-// pairs, laid end to end, are then cut into one contiguous range per wave, so
-// every wave streams the same number of KV bytes whatever the length mix.  A
-// range that covers a pair partly yields a partial result (o, m, l); a pair
-// covered by one wave gets its output written directly.  The log-sum-exp
-// reduce kernel merges the partials.  Two other cuts exist: fixed partitions
-// of a given length from each sequence's start (items handed out round-robin),
-// and whole pairs (no partials at all).
+// Scheduling.  The grid is persistent: one workgroup per CU, holding as many
+// wave64s as the CU keeps resident at the kernel's register count.  Every
+// workgroup first reads the batch's lengths into LDS and forms the prefix sum
+// of each sequence's count of 32-token steps ("units").  The units of all
+// (sequence, KV head) pairs, laid end to end, are cut into equal chunks (about
+// one per wave), so every wave streams about the same number of KV bytes
+// whatever the length mix.  A chunk that covers a pair partly yields a
+// partial result (o, m, l); a pair inside one chunk gets its output written
+// directly.  The log-sum-exp reduce kernel merges the partials.  Two other
+// cuts exist: fixed partitions of a given length from each sequence's start,
+// and whole pairs (no partials at all).  Each workgroup owns an even share of
+// the chunks (or items); its waves take them from an LDS queue.
 //
 // Within a segment a wave walks 32-token steps; K/V are read with 16-byte
-// non-temporal loads (each byte is used once).  The block-table entries of the segment sit in two registers per lane (a window
-// of 128 consecutive entries); the block id of a tile is read out with
-// v_readlane, so tile addresses are scalar.
+// non-temporal loads (each byte is used once).  Block-table entries are read
+// with scalar loads one step ahead, so tile addresses are scalar and the
+// table reads do not wait on the K/V loads in flight.
 //
 // Matrix cores: all query heads of a KV group are the 16 columns of one
 // MFMA tile (group <= 16; unused columns are zero queries), so each K/V
@@ -60,13 +61,16 @@ struct Mma<_Float16> {
   }
 };
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 32;       // tokens per step (one unit of work)
 constexpr int kMaxPlanSeqs = 8000;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int kChunksPerWave = 1;       // balanced cut: chunks per wave, on average
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Block-table rows are read through the constant address space: uniform
+// indices then become scalar loads (the kernels never write the tables).
+typedef const __attribute__((address_space(4))) int* ctab_ptr;
 
 // ---------------------------------------------------------------------------
 // Plan: clamped lengths and the exclusive prefix sum of per-sequence counts
@@ -79,10 +83,12 @@ __device__ __forceinline__ int plan_count(const DecodeParams& p, int len) {
   return (u + p.chunk - 1) / p.chunk;
 }
 
+template <int NW>
 __device__ void build_plan(const DecodeParams& p, int* lens, int* pre) {
-  __shared__ int wave_sum[kWaves];
+  constexpr int NT = 64 * NW;
+  __shared__ int wave_sum[NW];
   const int S = p.num_seqs;
-  const int per = (S + kThreads - 1) / kThreads;
+  const int per = (S + NT - 1) / NT;
   const int b = min(S, (int)threadIdx.x * per), e = min(S, b + per);
   int sum = 0;
   for (int s = b; s < e; ++s) {
@@ -109,7 +115,7 @@ __device__ void build_plan(const DecodeParams& p, int* lens, int* pre) {
     pre[s] = run;
     run += c;
   }
-  if (threadIdx.x == kThreads - 1) pre[S] = run;
+  if (threadIdx.x == NT - 1) pre[S] = run;
   __syncthreads();
 }
 
@@ -168,27 +174,41 @@ struct MfmaDecode {
   static constexpr int EB = FP8 ? 1 : 2;
   static constexpr int VW = DPL * EB / 4;       // dwords per V row piece
   static constexpr int KL = FP8 ? D / 64 : NC;  // 16-byte K loads per lane and tile
+  static constexpr bool kDoubleBuffer = FP8;
+  // waves per workgroup = waves one CU keeps resident at this register count
+  static constexpr int kWaves = D == 64 ? 16 : (FP8 ? 8 : 12);
 
   struct Buf {
     u32x4 k[2][KL];
     uint32_t v[2][4][VW];
   };
 
-  // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).  A tile
-  // that starts past the end re-reads the last block (its tokens are masked).
-  static __device__ __forceinline__ void load(Buf& buf, TableWindow<BS>& win, const DecodeParams& p,
-                                              int kvh, int j) {
+  // Block ids of the two 16-token tiles of step j, read with scalar loads
+  // (constant address space: they are counted apart from the vector loads in
+  // flight).  A tile that starts past the end takes the last block (its
+  // tokens are masked).
+  struct Ids {
+    int b0, b1;
+  };
+  static __device__ __forceinline__ Ids ids(ctab_ptr row, int nblk, int j) {
+    Ids r;
+    r.b0 = row[min((j * kStep) / BS, nblk - 1)];
+    r.b1 = BS == 32 ? r.b0 : row[min((j * kStep + 16) / BS, nblk - 1)];
+    return r;
+  }
+
+  // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).
+  static __device__ __forceinline__ void load(Buf& buf, Ids id, const DecodeParams& p, int kvh,
+                                              int j) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, c16 = lane & 15;
     const char* kpool = reinterpret_cast<const char*>(p.k_pool);
     const char* vpool = reinterpret_cast<const char*>(p.v_pool);
-    win.ensure(min((j * kStep + kStep - 1) / BS, win.nblk - 1));
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int rel = j * kStep + 16 * tau;
-      const int bi = min(rel / BS, win.nblk - 1);
       const int row0 = rel % BS;
-      const int blk = win.get(bi);
+      const int blk = tau == 0 ? id.b0 : id.b1;
       const int64_t tile = (((int64_t)blk * p.num_kv_heads + kvh) * BS + row0) * D;  // elements
       const char* kt = kpool + (tile + (int64_t)c16 * D) * EB;
       if constexpr (FP8) {
@@ -347,8 +367,8 @@ struct MfmaDecode {
       }
     }
 
-    TableWindow<BS> win;
-    win.init(p.block_tables + (int64_t)s * p.max_blocks, (len + BS - 1) / BS, (j0 * kStep) / BS);
+    const ctab_ptr trow = (ctab_ptr)(p.block_tables + (int64_t)s * p.max_blocks);
+    const int nblk = (len + BS - 1) / BS;
 
     State st;
     st.m = -INFINITY;
@@ -356,13 +376,34 @@ struct MfmaDecode {
 #pragma unroll
     for (int n = 0; n < DPL; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One step's K/V in registers at a time: the register budget then allows
-    // two waves per SIMD, whose loads overlap each other's compute (measured
-    // faster on MI355X than two register buffers at one wave per SIMD).
-    for (int j = j0; j < j1; ++j) {
-      Buf buf;
-      load(buf, win, p, kvh, j);
-      compute(buf, st, qop, p.qk_scale_log2, len, j);
+    // The block ids of the next step are fetched one step ahead.  With
+    // kDoubleBuffer the K/V loads of step j+1 are in flight while step j is
+    // computed (two register buffers); otherwise one buffer keeps the
+    // register count low enough for more waves per SIMD.
+    Ids cur = ids(trow, nblk, j0);
+    if constexpr (kDoubleBuffer) {
+      Buf A, B;
+      Ids nxt = ids(trow, nblk, min(j0 + 1, j1 - 1));
+      load(A, cur, p, kvh, j0);
+      for (int j = j0; j < j1; j += 2) {
+        cur = nxt;
+        nxt = ids(trow, nblk, min(j + 2, j1 - 1));
+        if (j + 1 < j1) load(B, cur, p, kvh, j + 1);
+        compute(A, st, qop, p.qk_scale_log2, len, j);
+        if (j + 1 >= j1) break;
+        cur = nxt;
+        nxt = ids(trow, nblk, min(j + 3, j1 - 1));
+        if (j + 2 < j1) load(A, cur, p, kvh, j + 2);
+        compute(B, st, qop, p.qk_scale_log2, len, j + 1);
+      }
+    } else {
+      for (int j = j0; j < j1; ++j) {
+        const Ids nxt = ids(trow, nblk, min(j + 1, j1 - 1));
+        Buf buf;
+        load(buf, cur, p, kvh, j);
+        compute(buf, st, qop, p.qk_scale_log2, len, j);
+        cur = nxt;
+      }
     }
 
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
@@ -410,6 +451,7 @@ struct MfmaDecode {
 // ---------------------------------------------------------------------------
 template <int D, int BS>
 struct F32Decode {
+  static constexpr int kWaves = D == 64 ? 12 : 8;  // resident waves per CU
   static __device__ void segment(const DecodeParams& p, int s, int kvh, int len, int j0, int j1,
                                  int part, int nparts) {
     constexpr int E = D / 64;
@@ -452,10 +494,9 @@ struct F32Decode {
       }
 #pragma unroll
       for (int k = 0; k < kGroup; ++k) {
-        if (t0 + k >= t_end) break;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if (j < g) {
+          if (j < g && t0 + k < t_end) {
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < E; ++e) dot += qv[j][e] * kv[k][e];
@@ -498,73 +539,108 @@ struct F32Decode {
 };
 
 // ---------------------------------------------------------------------------
-// The persistent kernel: plan, zero outputs of empty sequences, then walk
-// this wave's segments.
+// Work of the balanced cut: chunk k covers units [k*chunk, (k+1)*chunk) of
+// the unit line, i.e. one or more segments.  Chunk boundaries are fixed by
+// the chunk size alone, so the partial index of a segment (its chunk minus
+// the first chunk of its pair) does not depend on which wave runs it.
+// ---------------------------------------------------------------------------
+template <class Seg>
+__device__ __forceinline__ void run_chunk(const DecodeParams& p, const int* lens, const int* pre,
+                                          int T, int chunk, int k) {
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  int u = k * chunk;
+  const int uend = min(T, u + chunk);
+  int s = find_seq(pre, S, u / H);
+  int base = uni(pre[s]);
+  int U = uni(pre[s + 1]) - base;
+  int h = (u - base * H) / U;
+  int j = u - base * H - h * U;
+  while (true) {
+    const int ps = base * H + h * U;  // first unit of the pair
+    const int j1 = min(U, j + (uend - u));
+    const int wf = ps / chunk, wl = (ps + U - 1) / chunk;
+    Seg::segment(p, s, h, uni(lens[s]), j, j1, k - wf, wl - wf + 1);
+    u += j1 - j;
+    if (u >= uend) break;
+    j = 0;
+    if (++h == H) {
+      h = 0;
+      do {
+        ++s;
+      } while (uni(pre[s + 1]) == uni(pre[s]));
+      base = uni(pre[s]);
+      U = uni(pre[s + 1]) - base;
+    }
+  }
+}
+
+// Work item i of the fixed and whole cuts: one partition of one pair.
+template <class Seg>
+__device__ __forceinline__ void run_item(const DecodeParams& p, const int* lens, const int* pre,
+                                         int i) {
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  const int s = find_seq(pre, S, i / H);
+  const int base = uni(pre[s]);
+  const int q = uni(pre[s + 1]) - base;
+  const int rel = i - base * H;
+  const int h = rel / q, part = rel - h * q;
+  const int len = uni(lens[s]);
+  const int U = (len + kStep - 1) / kStep;
+  const int j0 = part * p.chunk;
+  const int j1 = min(U, j0 + p.chunk);
+  Seg::segment(p, s, h, len, j0, j1, part, q);
+}
+
+// Next ticket of the workgroup's queue (LDS counter), the same in all lanes.
+__device__ __forceinline__ int take_ticket(int* counter) {
+  int v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(counter, 1);
+  return __builtin_amdgcn_readlane(v, 0);
+}
+
+// ---------------------------------------------------------------------------
+// The persistent kernel: one workgroup per CU holding all the waves the CU
+// keeps resident.  Plan, zero outputs of empty sequences, then the waves take
+// the workgroup's share of the work list from an LDS queue.
+//
+// Finer chunks (several per wave, so that fast waves could take more of
+// them) were measured slower on MI355X: each extra chunk adds a segment
+// start and a partial, which cost more than the balance gains.  Items of the
+// fixed and whole cuts differ in length, and there the queue does balance.
 // ---------------------------------------------------------------------------
 template <class Seg, typename QT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p) {
+  constexpr int NW = Seg::kWaves, NT = 64 * NW;
   extern __shared__ __align__(16) int plan_lds[];
+  __shared__ int queue;
   const int S = p.num_seqs, H = p.num_kv_heads;
   int* lens = plan_lds;
   int* pre = plan_lds + S;
-  build_plan(p, lens, pre);
+  if (threadIdx.x == 0) queue = 0;
+  build_plan<NW>(p, lens, pre);  // ends with a barrier
 
   // Sequences with no tokens get a zero output.
   for (int s = blockIdx.x; s < S; s += gridDim.x) {
     if (lens[s] == 0) {
       QT* out = reinterpret_cast<QT*>(p.out) + (int64_t)s * p.num_q_heads * p.head_dim;
-      for (int i = threadIdx.x; i < p.num_q_heads * p.head_dim; i += kThreads) out[i] = (QT)0.0f;
+      for (int i = threadIdx.x; i < p.num_q_heads * p.head_dim; i += NT) out[i] = (QT)0.0f;
     }
   }
 
-  const int wave = uni(threadIdx.x >> 6);
-  const int W = gridDim.x * kWaves;
-  const int w = blockIdx.x * kWaves + wave;
-  const int total = uni(pre[S]);
-  const int T = total * H;
-
+  // Work list: chunks of units (balanced cut) or items (fixed / whole cuts).
+  const int T = uni(pre[S]) * H;
+  int chunk = 1, nwork = T;
   if (p.mode == kSplitBalanced) {
-    int chunk = (T + W - 1) / W;
+    const int64_t want = (int64_t)gridDim.x * NW * kChunksPerWave;
+    chunk = (int)((T + want - 1) / want);
     chunk = chunk < p.chunk ? p.chunk : chunk;
-    const int64_t u0 = (int64_t)w * chunk;
-    if (u0 >= T) return;
-    int u = (int)u0;
-    const int uend = min(T, u + chunk);
-    int s = find_seq(pre, S, u / H);
-    int base = uni(pre[s]);
-    int U = uni(pre[s + 1]) - base;
-    int h = (u - base * H) / U;
-    int j = u - base * H - h * U;
-    while (true) {
-      const int ps = base * H + h * U;                 // first unit of the pair
-      const int j1 = min(U, j + (uend - u));
-      const int wf = ps / chunk, wl = (ps + U - 1) / chunk;
-      Seg::segment(p, s, h, uni(lens[s]), j, j1, w - wf, wl - wf + 1);
-      u += j1 - j;
-      if (u >= uend) break;
-      j = 0;
-      if (++h == H) {
-        h = 0;
-        do {
-          ++s;
-        } while (uni(pre[s + 1]) == uni(pre[s]));
-        base = uni(pre[s]);
-        U = uni(pre[s + 1]) - base;
-      }
-    }
-  } else {
-    for (int i = w; i < T; i += W) {
-      const int s = find_seq(pre, S, i / H);
-      const int base = uni(pre[s]);
-      const int q = uni(pre[s + 1]) - base;
-      const int rel = i - base * H;
-      const int h = rel / q, part = rel - h * q;
-      const int len = uni(lens[s]);
-      const int U = (len + kStep - 1) / kStep;
-      const int j0 = part * p.chunk;
-      const int j1 = min(U, j0 + p.chunk);
-      Seg::segment(p, s, h, len, j0, j1, part, q);
-    }
+    nwork = (T + chunk - 1) / chunk;
+  }
+  const int k0 = (int)((int64_t)nwork * blockIdx.x / gridDim.x);
+  const int k1 = (int)((int64_t)nwork * (blockIdx.x + 1) / gridDim.x);
+  for (int k = k0 + take_ticket(&queue); k < k1; k = k0 + take_ticket(&queue)) {
+    if (p.mode == kSplitBalanced) run_chunk<Seg>(p, lens, pre, T, chunk, k);
+    else run_item<Seg>(p, lens, pre, k);
   }
 }
 
@@ -574,26 +650,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 template <typename QT>
 __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
+  __shared__ float s_max[16], s_inv[16];
   const int h = blockIdx.x, s = blockIdx.y;
   int len = p.seq_lens[s];
   len = len < p.max_len ? len : p.max_len;
   if (len <= 0) return;
   const int np = p.nparts[s * p.num_kv_heads + h];
   if (np <= 1) return;
-  const int D = p.head_dim;
-  for (int idx = threadIdx.x; idx < p.group * D; idx += blockDim.x) {
-    const int j = idx / D, d = idx - j * D;
-    const int hq = h * p.group + j;
-    const int64_t b = ((int64_t)s * p.num_q_heads + hq) * p.max_parts;
+  const int D = p.head_dim, g = p.group;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)s * p.num_q_heads + h * g) * p.max_parts;
+  // M and L of each head: one wave per head, lanes over the partials.
+  for (int j = wave; j < g; j += 4) {
+    const float* m = p.part_m + row0 + (int64_t)j * p.max_parts;
+    const float* l = p.part_l + row0 + (int64_t)j * p.max_parts;
     float M = -INFINITY;
-    for (int i = 0; i < np; ++i) M = fmaxf(M, p.part_m[b + i]);
-    float L = 0.f, O = 0.f;
-    for (int i = 0; i < np; ++i) {
-      const float wt = __builtin_amdgcn_exp2f(p.part_m[b + i] - M);
-      L += wt * p.part_l[b + i];
-      O += wt * p.part_o[(b + i) * D + d];
+    for (int i = lane; i < np; i += 64) M = fmaxf(M, m[i]);
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = 0.f;
+    for (int i = lane; i < np; i += 64) L += __builtin_amdgcn_exp2f(m[i] - M) * l[i];
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (lane == 0) {
+      s_max[j] = M;
+      s_inv[j] = p.v_scale / L;
     }
-    reinterpret_cast<QT*>(p.out)[((int64_t)s * p.num_q_heads + hq) * D + d] = (QT)(O / L * p.v_scale);
+  }
+  __syncthreads();
+  // Weighted sum of the partial outputs; the loads of several partials are
+  // issued together (they do not depend on each other).
+  for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
+    const int j = idx / D, d = idx - j * D;
+    const int64_t b = row0 + (int64_t)j * p.max_parts;
+    const float M = s_max[j];
+    float O = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < np; ++i) O += __builtin_amdgcn_exp2f(p.part_m[b + i] - M) * p.part_o[(b + i) * D + d];
+    reinterpret_cast<QT*>(p.out)[((int64_t)s * p.num_q_heads + h * g + j) * D + d] = (QT)(O * s_inv[j]);
   }
 }
 
@@ -632,17 +724,18 @@ int64_t wave_work_bound(const DecodeParams& p) {
 
 template <class Seg, typename QT>
 hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
+  constexpr int NT = 64 * Seg::kWaves;
   const size_t lds = decode_plan_lds_bytes(p.num_seqs);
   auto kernel = decode_kernel<Seg, QT>;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
-                                                   kThreads, lds) != hipSuccess || per_cu <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), NT,
+                                                   lds) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   int64_t grid = (int64_t)cu_count() * per_cu;
-  const int64_t need = (wave_work_bound(p) + kWaves - 1) / kWaves;
+  const int64_t need = (wave_work_bound(p) + Seg::kWaves - 1) / Seg::kWaves;
   if (grid > need) grid = need;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NT), lds, stream, p);
   return hipGetLastError();
 }
 
