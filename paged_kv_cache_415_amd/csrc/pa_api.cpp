@@ -374,8 +374,8 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
     return fail(PA_ERR_INVALID_ARG, "scales must be finite");
   if ((long long)max_blocks_per_seq * block_size > (1 << 30))
     return fail(PA_ERR_UNSUPPORTED, "block table too wide");
-  if ((size_t)max_blocks_per_seq * 4 + 64 * (head_dim + 8) * 2 + (size_t)head_dim * 64 * 2 > 160 * 1024)
-    return fail(PA_ERR_UNSUPPORTED, "block table row does not fit in LDS");
+  if (pa::prefill_smem_bytes(head_dim) > 160 * 1024)
+    return fail(PA_ERR_UNSUPPORTED, "K/V tile stages do not fit in LDS");
   if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return ok();
   if (!out || !q || !query_start_loc || !k_pool || !v_pool || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");

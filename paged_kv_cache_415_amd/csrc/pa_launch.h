@@ -102,6 +102,8 @@ hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// LDS bytes the prefill kernel needs (two stages of a K and a V tile).
+size_t prefill_smem_bytes(int head_dim);
 hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 

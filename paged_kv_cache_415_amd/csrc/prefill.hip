@@ -11,19 +11,52 @@
 // head) run on one XCD.  A tile holds 128 query rows = (128 / group)
 // consecutive chunk positions x the group's query heads, so one staged K/V
 // tile serves every head of the group.  The workgroup walks the context in
-// 64-key tiles: the tile's rows are gathered through the LDS-cached block
-// table with 16-byte loads (the next tile's loads are in flight while the
-// current one is computed) and stored to LDS, then each wave (32 query rows)
-// forms
+// 64-key tiles held in two LDS stages: while tile t is computed, tile t + 1
+// is copied from HBM straight into the other stage by LDS-DMA loads (no
+// registers, no LDS stores); one barrier per tile hands the stages over.
+// Each wave (32 query rows) forms
 //   S^T[key][row] = K[key][:] . Q[row][:]            (v_mfma_f32_16x16x32)
 //   O^T[dim][row] += V^T[dim][key] P^T[key][row]     (v_mfma_f32_16x16x32)
 // with an online softmax per query row.  As in the decode kernel, the score
 // tile's register layout is the value product's B operand, so
-// probabilities stay in their lanes.
+// probabilities stay in their lanes; the value operand V^T is read from the
+// row-major V tile with gfx950's transposing LDS reads (ds_read_b64_tr_b16).
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef const __attribute__((address_space(4))) int* ctab_ptr;   // block table, read-only
+
+// Maximum that propagates NaN (v_maximum3_f32; no operand canonicalisation).
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (lane swaps, no LDS).
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// ds_read_b64_tr_b16 at LDS byte address `addr` + OFF.  Issued as inline
+// assembly: the compiler treats the builtin as possibly aliasing the LDS-DMA
+// copies in flight and would wait for all of them before it.  The result
+// may be used only after lds_wait().
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// Wait for every LDS read issued so far; the values in h are taken as
+// produced here, so no use of them is scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&h)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(h[i]));
+}
 
 template <typename T>
 struct PMma;
@@ -48,45 +81,156 @@ constexpr int kPThreads = 256;
 constexpr int kRowsPerWG = 128;
 constexpr int kKeyTile = 64;
 constexpr float kSlack = 8.0f;   // log2 units
-constexpr int kXcds = 8;
-// Column of key k (0..63) of a tile in the transposed V tile: the key index
-// [ap:1][h:1][G:2][i:2] becomes [ap][G][h][i], so that the keys a lane holds
-// in the probability operand (tiles 2ap and 2ap+1, rows 4G + i) are adjacent.
-__device__ __forceinline__ int vt_col(int k) {
-  return (k & 0x20) | ((k & 0x0C) << 1) | ((k & 0x10) >> 2) | (k & 3);
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// Tiles are stored row-major (one 2D-byte row per key) with the 16-byte
+// chunks of each row XOR-swizzled, so that the LDS reads of the matrix
+// operands hit distinct banks:
+//  - K operand (ds_read_b128): 16 lanes read one chunk of 16 consecutive
+//    rows, so the K swizzle takes a different chunk slot for each of them;
+//  - V^T operand (ds_read_b64_tr_b16): lanes read 8-byte pieces of two
+//    adjacent chunks of 4 rows per 16-lane group, so the V swizzle moves
+//    chunk pairs together (an even XOR) and differs across 8 rows.
+// With D = 64 two rows share one 256-byte bank line, hence the row / RPL.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  constexpr int CPR = D / 8, RPL = 256 / (2 * D);
+  return (row / RPL) & (CPR - 1);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  constexpr int CPR = D / 8, RPL = 256 / (2 * D);
+  return 2 * ((row / RPL) & (CPR / 2 - 1));
 }
 
-// Byte offset of (dimension d, column col) in the transposed V tile: rows of
-// 64 keys (128 B), taken in pairs as 256-byte lines whose sixteen 16-byte
-// chunks are XOR-swizzled by d / (D/16), so that the 16 lanes reading one
-// operand (dimensions (D/16) * c16 + nn) hit 16 different chunks.
-template <int D>
-__device__ __forceinline__ int vt_offset(int d, int col) {
-  const int swz = (d / (D / 16)) & 15;
-  const int chunk = (((d & 1) << 3) | (col >> 3)) ^ swz;
-  return (d >> 1) * 256 + chunk * 16 + (col & 7) * 2;
+// One LDS-DMA load: 16 bytes per lane from `src` to LDS at `dst` + 16 lane.
+// (A plain function: target builtins inside templates make the host pass
+// drop the kernels' launch stubs.)
+__device__ __forceinline__ void dma16(const void* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_char*)dst, 16, 0, 0);
 }
+
+// Where a wave's share of a K/V tile comes from.  Wave w copies key rows
+// [16 w, 16 w + 16) of every tile, which lie in one cache block (the block
+// size is 16 or 32), RPI rows (1 KB) per LDS-DMA instruction.  Lane l lands
+// at byte 16 l of the instruction's 1 KB, i.e. row l / CPR, chunk slot
+// l % CPR, and so fetches the chunk that the swizzle puts there; its byte
+// offset inside the block does not change from tile to tile.
+template <int D, int BS>
+struct TileSrc {
+  static constexpr int CPR = D / 8, RPI = 64 / CPR, NI = 16 / RPI, TILE = kKeyTile * D * 2;
+  const char* kpool;
+  const char* vpool;
+  const int* trow;     // the sequence's block-table row
+  int64_t head_off;    // byte offset of the KV head inside a block
+  int64_t blk_bytes;   // bytes of one block (all heads)
+  int kend, wave, lane;
+  uint32_t koff[NI], voff[NI];   // this lane's byte offsets inside the block
+
+  __device__ void init(const char* kp, const char* vp, const int* tr, int num_kv_heads, int kvh,
+                       int kend_, int wave_, int lane_) {
+    kpool = kp;
+    vpool = vp;
+    trow = tr;
+    blk_bytes = (int64_t)num_kv_heads * BS * D * 2;
+    head_off = (int64_t)kvh * BS * D * 2;
+    kend = kend_;
+    wave = wave_;
+    lane = lane_;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = 16 * wave + RPI * i + lane / CPR;     // row in the tile
+      const int brow = (16 * wave) % BS + RPI * i + lane / CPR;   // row in the block
+      koff[i] = (uint32_t)(brow * D * 2 + 16 * ((lane % CPR) ^ k_swz<D>(row)));
+      voff[i] = (uint32_t)(brow * D * 2 + 16 * ((lane % CPR) ^ v_swz<D>(row)));
+    }
+  }
+
+  // Block id of this wave's rows in tile kt (a scalar load).
+  __device__ __forceinline__ int block_of(int kt) const {
+    const int key0 = min(kt * kKeyTile + 16 * wave, kend - 1);
+    return ((ctab_ptr)trow)[key0 / BS];
+  }
+
+  // Copy this wave's rows of tile kt into a stage (K tile, then V tile);
+  // `blk` = block_of(kt).  Keys past the context re-read the last key
+  // (finite data; their logits are masked).  Completion is counted by vmcnt.
+  __device__ __forceinline__ void copy(int kt, int blk, char* dst) const {
+    char* kd = dst + 16 * wave * D * 2;
+    if (kt * kKeyTile + 16 * wave + 15 < kend) {
+      const char* kb = kpool + blk * blk_bytes + head_off;
+      const char* vb = vpool + blk * blk_bytes + head_off;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        dma16(kb + koff[i], kd + i * 1024);
+        dma16(vb + voff[i], kd + TILE + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = 16 * wave + RPI * i + lane / CPR;
+        const int key = min(kt * kKeyTile + row, kend - 1);
+        const int64_t base = trow[key / BS] * blk_bytes + head_off + (int64_t)(key % BS) * D * 2;
+        dma16(kpool + base + 16 * ((lane % CPR) ^ k_swz<D>(row)), kd + i * 1024);
+        dma16(vpool + base + 16 * ((lane % CPR) ^ v_swz<D>(row)), kd + TILE + i * 1024);
+      }
+    }
+  }
+};
 
 template <typename T> constexpr uint32_t kOnes = 0;                  // two 1.0 values
 template <> constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
-template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;         // MI355X: 8 XCDs, workgroups dispatched round-robin
+template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;
 
-size_t prefill_smem_bytes(int head_dim, int max_blocks) {
-  const int stride = head_dim + 8;  // padded K row, in elements
-  return (size_t)kKeyTile * stride * 2 + (size_t)head_dim * kKeyTile * 2 + (size_t)max_blocks * 4;
+// Value product of one key pair AP (keys 32 AP .. 32 AP + 31) of a stage at
+// LDS address `stage`: acc[b][nb] += V^T(dims 16 nb ..) P^T(keys, rows of b),
+// and the row sums via the all-ones operand.  The A operand of dimension
+// block nb holds, in lane (G, c16), dimension 16 nb + c16 of the lane's eight
+// keys 32 AP + 4 G + 0..3 and 32 AP + 16 + 4 G + 0..3 (the probability
+// operand's keys).  A transposing read returns to lane c16 of a 16-lane group
+// the element (c16 & 3) of the 4-element row addressed by lane 4 t + (c16 >> 2),
+// for t = 0..3; lane s therefore addresses key 4 G + (s >> 2) (+ 16 for the
+// second read), dimensions 16 nb + 4 (s & 3) .. + 3 (voff).
+template <typename T, int D, int AP>
+__device__ __forceinline__ void pv_half(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[2], const u32x4 (&pop)[2],
+                                        uint32_t stage, const uint32_t (&voff)[D / 16]) {
+  constexpr int NB = D / 16;
+  constexpr int NBB = NB < 4 ? NB : 4;    // dimension blocks per batch of reads
+  constexpr int OFF0 = 32 * AP * D * 2, OFF1 = (32 * AP + 16) * D * 2;
+  const u32x4 ones = {kOnes<T>, kOnes<T>, kOnes<T>, kOnes<T>};
+#pragma unroll
+  for (int nb0 = 0; nb0 < NB; nb0 += NBB) {
+    u32x2 h[2 * NBB];
+#pragma unroll
+    for (int j = 0; j < NBB; ++j) {
+      h[2 * j] = lds_read_tr16<OFF0>(stage + voff[nb0 + j]);
+      h[2 * j + 1] = lds_read_tr16<OFF1>(stage + voff[nb0 + j]);
+    }
+    lds_wait(h);
+#pragma unroll
+    for (int j = 0; j < NBB; ++j) {
+      const u32x4 va = {h[2 * j].x, h[2 * j].y, h[2 * j + 1].x, h[2 * j + 1].y};
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b][nb0 + j] = PMma<T>::mma(va, pop[b], acc[b][nb0 + j]);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[b], acc_l[b]);
 }
+
+// Two stages of (K tile, V tile).
+size_t prefill_smem_bytes(int head_dim) { return (size_t)2 * 2 * kKeyTile * head_dim * 2; }
 
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p) {
   extern __shared__ __align__(16) char smem_raw[];
   constexpr int NC = D / 32;
-  constexpr int DPL = D / 16;
-  constexpr int STRIDE = D + 8;             // K row stride in LDS (elements): spreads banks
-  constexpr int VPR = D / 8;                // 16-byte vectors per row
-  constexpr int KPT = kKeyTile * VPR / kPThreads;   // keys per thread in a tile's gather
-  T* k_lds = reinterpret_cast<T*>(smem_raw);
-  char* vt_lds = reinterpret_cast<char*>(k_lds + kKeyTile * STRIDE);   // V^T, D x 64 keys
-  int* tab = reinterpret_cast<int*>(vt_lds + D * kKeyTile * 2);
+  constexpr int NB = D / 16;                 // 16-dimension blocks of the output
+  constexpr int TILE = kKeyTile * D * 2;     // bytes of one K or V tile
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;              // rows per 1 KB DMA instruction
+  // stage t (t = 0, 1) at smem_raw + 2 t TILE: K tile, then V tile
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)smem_raw;
 
   // Workgroup `lin` runs on XCD lin % kXcds.  Each XCD gets a contiguous
   // range of work items (query tile fastest), so the query tiles that read
@@ -112,9 +256,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   const int ctx0 = n - L;                   // position of chunk query 0
   const int last_pos = min(p0 + qpos, L) - 1;
   const int kend = ctx0 + last_pos + 1;     // keys [0, kend) can be visible to this tile
-  const int ntab = (kend + BS - 1) / BS;
   const int* trow = p.block_tables + (int64_t)seq * p.max_blocks;
-  for (int i = threadIdx.x; i < ntab; i += kPThreads) tab[i] = trow[i];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = lane >> 4, c16 = lane & 15;
@@ -152,71 +294,48 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   // value product against an all-ones operand (every row of acc_l holds the
   // column's sum).
   float m_run[2] = {-INFINITY, -INFINITY};
-  f32x4 acc[2][DPL], acc_l[2];
+  f32x4 acc[2][NB], acc_l[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     acc_l[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nn = 0; nn < DPL; ++nn) acc[b][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nn = 0; nn < NB; ++nn) acc[b][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const u32x4 ones = {kOnes<T>, kOnes<T>, kOnes<T>, kOnes<T>};
   // first tile that needs the causal mask: every row sees keys <= ctx0 + p0
   const int min_lim = ctx0 + p0;
 
   const char* kpool = reinterpret_cast<const char*>(p.k_pool);
   const char* vpool = reinterpret_cast<const char*>(p.v_pool);
   const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
-  __syncthreads();   // block-table slice visible
 
-  // The next tile's K/V rows are fetched into registers while the current
-  // tile is computed; they go to LDS between two barriers.  Thread t loads
-  // the 16-byte piece `vec` of KPT consecutive keys (a 16-lane group reads a
-  // whole 256-byte row).  K is stored row-major; V is stored transposed (one
-  // LDS row per dimension) with its keys permuted by vt_col, in the order in
-  // which the probability operand holds them, so a lane's eight keys of one
-  // dimension are 16 contiguous bytes (one ds_read_b128, no byte permutes).
-  const int g_vec = threadIdx.x % VPR, g_kq = threadIdx.x / VPR;
-  u32x4 kx[KPT], vx[KPT];
-  auto gather = [&](int kt) {
+  // LDS byte offsets of this lane's operand pieces inside a stage (the
+  // swizzles depend only on the lane, not on the 16-row block or key pair):
+  // K piece c of row block a at a * 16 rows + koff[c]; V^T dimension block nb
+  // of key pair ap, half hh at (32 ap + 16 hh) rows + voff[nb].
+  uint32_t koff[NC], voff[NB];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = kt * kKeyTile + g_kq * KPT + i;
-      kx[i] = u32x4{0, 0, 0, 0};
-      vx[i] = u32x4{0, 0, 0, 0};
-      if (key < kend) {
-        const int blk = tab[key / BS];
-        const int64_t off = ((((int64_t)blk * p.num_kv_heads + kvh) * BS + key % BS) * D + g_vec * 8) * 2;
-        kx[i] = ld16(kpool + off);
-        vx[i] = ld16(vpool + off);
-      }
-    }
-  };
-  auto stash = [&]() {
+  for (int c = 0; c < NC; ++c) koff[c] = c16 * D * 2 + 16 * ((4 * c + G) ^ k_swz<D>(c16));
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) st16(k_lds + (g_kq * KPT + i) * STRIDE + g_vec * 8, kx[i]);
-    // transpose KPT keys x 8 dims into 8 dims x KPT keys (16-bit lanes)
-    const int col = vt_col(g_kq * KPT);     // KPT consecutive keys stay consecutive
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = g_vec * 8 + e;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      char* dst = vt_lds + vt_offset<D>(d, col);
-      if constexpr (KPT == 4) {
-        const uint32_t w0 = perm(vx[1][e >> 1], vx[0][e >> 1], sel);
-        const uint32_t w1 = perm(vx[3][e >> 1], vx[2][e >> 1], sel);
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = perm(vx[1][e >> 1], vx[0][e >> 1], sel);
-      }
-    }
-  };
-  gather(0);
-  stash();
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = 4 * G + (c16 >> 2);
+    voff[nb] = TILE + row * D * 2 + 16 * ((2 * nb + ((c16 & 3) >> 1)) ^ v_swz<D>(row)) + 8 * (c16 & 1);
+  }
+
+  TileSrc<D, BS> src;
+  src.init(kpool, vpool, trow, p.num_kv_heads, kvh, kend, wave, lane);
+  src.copy(0, src.block_of(0), smem_raw);
+  int blk_next = src.block_of(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
+    const char* k_lds = smem_raw + (kt & 1) * 2 * TILE;
+    const uint32_t v_base = lds_base + (kt & 1) * 2 * TILE;   // LDS address of the stage
     const bool more = kt + 1 < ntiles;     // uniform over the workgroup
-    if (more) gather(kt + 1);
+    if (more) {
+      src.copy(kt + 1, blk_next, smem_raw + ((kt + 1) & 1) * 2 * TILE);
+      blk_next = src.block_of(kt + 2);   // in flight while this tile is computed
+    }
 
     // ---- raw products q.k for 4 key row-tiles x 2 query column-tiles
     const bool diag = kt * kKeyTile + kKeyTile - 1 > min_lim;   // uniform
@@ -226,7 +345,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
       u32x4 ka[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        ka[c] = *reinterpret_cast<const u32x4*>(k_lds + (16 * a + c16) * STRIDE + 32 * c + 8 * G);
+        ka[c] = *reinterpret_cast<const u32x4*>(k_lds + a * 16 * D * 2 + koff[c]);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -249,12 +368,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     u32x4 pop[2][2];   // [key pair][column tile]
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      float mx = fmaxf(fmaxf(fmaxf(s[0][b][0], s[0][b][1]), fmaxf(s[0][b][2], s[0][b][3])),
-                       fmaxf(fmaxf(s[1][b][0], s[1][b][1]), fmaxf(s[1][b][2], s[1][b][3])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[2][b][0], s[2][b][1]), fmaxf(s[2][b][2], s[2][b][3])),
-                           fmaxf(fmaxf(s[3][b][0], s[3][b][1]), fmaxf(s[3][b][2], s[3][b][3]))));
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
+      float mx = s[0][b][0];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (a + i > 0) mx = fmax_nan(mx, s[a][b][i]);
+      mx = max_over_groups(mx);
       mx *= cscale;   // cscale > 0: -inf stays -inf
       // Lazy rescaling (as in decode): the reference max moves only when a
       // row's max exceeds it by more than kSlack, so p <= 2^kSlack.  A row
@@ -265,7 +385,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
         m_run[b] = m_new;
         acc_l[b] = acc_l[b] * alpha;
 #pragma unroll
-        for (int nn = 0; nn < DPL; ++nn) acc[b][nn] = acc[b][nn] * alpha;
+        for (int nn = 0; nn < NB; ++nn) acc[b][nn] = acc[b][nn] * alpha;
       }
       // p = 2^(c * (q.k) - m): one fused multiply-add per score
       const float nm = -m_run[b];
@@ -280,29 +400,24 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
       for (int ap = 0; ap < 2; ++ap)
         pop[ap][b] = u32x4{w[2 * ap][0], w[2 * ap][1], w[2 * ap + 1][0], w[2 * ap + 1][1]};
     }
-    // ---- values: A operand rows = dims DPL*c16 + nn, k-slots = the lane's
-    // eight keys (keys 32ap + 4G + 0..3 and 32ap + 16 + 4G + 0..3), which
-    // V^T holds contiguously at columns 32ap + 8G .. 32ap + 8G + 7
-#pragma unroll
-    for (int ap = 0; ap < 2; ++ap) {
-#pragma unroll
-      for (int nn = 0; nn < DPL; ++nn) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(
-            vt_lds + vt_offset<D>(DPL * c16 + nn, 32 * ap + 8 * G));
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[b][nn] = PMma<T>::mma(va, pop[ap][b], acc[b][nn]);
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[ap][b], acc_l[b]);
-    }
+    // ---- values: the A operand of dimension block nn holds, in lane
+    // (G, c16), dimension 16 nn + c16 of the lane's eight keys 32 ap + 4 G +
+    // 0..3 and 32 ap + 16 + 4 G + 0..3 (the probability operand's keys).  A
+    // transposing read returns to lane c16 of a 16-lane group the element
+    // (c16 & 3) of the 4-element row addressed by lane 4 t + (c16 >> 2),
+    // for t = 0..3; lane s therefore addresses key 4 G + (s >> 2) (+ 16 for
+    // the second read), dimensions 16 nn + 4 (s & 3) .. + 3.
+    pv_half<T, D, 0>(acc, acc_l, pop[0], v_base, voff);
+    pv_half<T, D, 1>(acc, acc_l, pop[1], v_base, voff);
     if (more) {
-      __syncthreads();   // every wave is done with this tile
-      stash();
-      __syncthreads();   // the next tile is visible
+      // this wave's copy of the next tile has landed; after the barrier all
+      // copies have, and every wave is done with this tile's stage
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
   }
 
-  // ---- normalise and store: lane (G, c16) holds dims DPL*(4G+i) + nn of its row
+  // ---- normalise and store: lane (G, c16) holds dims 16 nn + 4 G + i of its row
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (!valid[b]) continue;
@@ -310,16 +425,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     T* orow = reinterpret_cast<T*>(p.out) +
               ((int64_t)(q0 + pos[b]) * p.num_q_heads + kvh * g + head[b]) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t w[DPL / 2];
-#pragma unroll
-      for (int nn = 0; nn < DPL; nn += 2) w[nn / 2] = pack2<T>(acc[b][nn][i] * inv, acc[b][nn + 1][i] * inv);
-      T* dst = orow + DPL * (4 * G + i);
-      if constexpr (DPL == 8) {
-        st16(dst, u32x4{w[0], w[1], w[2], w[3]});
-      } else {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-      }
+    for (int nn = 0; nn < NB; ++nn) {
+      const u32x2 w = {pack2<T>(acc[b][nn][0] * inv, acc[b][nn][1] * inv),
+                       pack2<T>(acc[b][nn][2] * inv, acc[b][nn][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + 16 * nn + 4 * G) = w;
     }
   }
 }
@@ -328,7 +437,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
   const int qpos = kRowsPerWG / p.group;
   const dim3 grid((p.max_q_len + qpos - 1) / qpos, p.num_kv_heads, p.num_seqs);
-  const size_t smem = prefill_smem_bytes(p.head_dim, p.max_blocks);
+  const size_t smem = prefill_smem_bytes(p.head_dim);
 #define PA_PREFILL(T, D, BS) \
   hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS>), grid, dim3(kPThreads), smem, stream, p)
   if (p.q_dtype == kBF16) {
