@@ -49,11 +49,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
-// Wait for every LDS read issued so far; the values in h are taken as
-// produced here, so no use of them is scheduled before the wait.
-template <int N>
+// Wait until at most CNT LDS reads are outstanding (those issued last); the
+// values in h are taken as produced here, so no use of them is scheduled
+// before the wait.  LDS reads complete in order, and between the reads of a
+// batch and this wait no other LDS instruction is issued (the inline
+// assembly is ordered against all memory operations).
+template <int CNT, int N>
 __device__ __forceinline__ void lds_wait(u32x2 (&h)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  static_assert(CNT >= 0 && CNT <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(CNT) : "memory");
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(h[i]));
 }
@@ -182,40 +186,67 @@ template <typename T> constexpr uint32_t kOnes = 0;                  // two 1.0 
 template <> constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
 template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;
 
-// Value product of one key pair AP (keys 32 AP .. 32 AP + 31) of a stage at
-// LDS address `stage`: acc[b][nb] += V^T(dims 16 nb ..) P^T(keys, rows of b),
-// and the row sums via the all-ones operand.  The A operand of dimension
-// block nb holds, in lane (G, c16), dimension 16 nb + c16 of the lane's eight
-// keys 32 AP + 4 G + 0..3 and 32 AP + 16 + 4 G + 0..3 (the probability
-// operand's keys).  A transposing read returns to lane c16 of a 16-lane group
-// the element (c16 & 3) of the 4-element row addressed by lane 4 t + (c16 >> 2),
-// for t = 0..3; lane s therefore addresses key 4 G + (s >> 2) (+ 16 for the
-// second read), dimensions 16 nb + 4 (s & 3) .. + 3 (voff).
-template <typename T, int D, int AP>
-__device__ __forceinline__ void pv_half(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[2], const u32x4 (&pop)[2],
-                                        uint32_t stage, const uint32_t (&voff)[D / 16]) {
-  constexpr int NB = D / 16;
-  constexpr int NBB = NB < 4 ? NB : 4;    // dimension blocks per batch of reads
+// Value product of a tile held in the stage at LDS address `stage`:
+// acc[b][nb] += V^T(dims 16 nb .., keys) P^T(keys, rows of column tile b),
+// and the row sums via the all-ones operand.  For key pair ap (keys 32 ap ..
+// 32 ap + 31) the A operand of dimension block nb holds, in lane (G, c16),
+// dimension 16 nb + c16 of the lane's eight keys 32 ap + 4 G + 0..3 and
+// 32 ap + 16 + 4 G + 0..3 (the probability operand's keys).  A transposing
+// read returns to lane c16 of a 16-lane group the element (c16 & 3) of the
+// 4-element row addressed by lane 4 t + (c16 >> 2), for t = 0..3; lane s
+// therefore addresses key 4 G + (s >> 2) (+ 16 for the second read),
+// dimensions 16 nb + 4 (s & 3) .. + 3 (voff).
+//
+// The reads come in batches of four dimension blocks (eight reads); the
+// next batch is in flight while the current one feeds the matrix cores.
+template <int D, int AP, int NB0>
+__device__ __forceinline__ void pv_read(u32x2 (&h)[8], uint32_t stage, const uint32_t (&voff)[D / 16]) {
   constexpr int OFF0 = 32 * AP * D * 2, OFF1 = (32 * AP + 16) * D * 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[2 * j] = lds_read_tr16<OFF0>(stage + voff[NB0 + j]);
+    h[2 * j + 1] = lds_read_tr16<OFF1>(stage + voff[NB0 + j]);
+  }
+}
+template <typename T, int D, int NB0>
+__device__ __forceinline__ void pv_mma(f32x4 (&acc)[2][D / 16], const u32x2 (&h)[8], const u32x4 (&pop)[2]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 va = {h[2 * j].x, h[2 * j].y, h[2 * j + 1].x, h[2 * j + 1].y};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[b][NB0 + j] = PMma<T>::mma(va, pop[b], acc[b][NB0 + j]);
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void pv_tile(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[2], const u32x4 (&pop)[2][2],
+                                        uint32_t stage, const uint32_t (&voff)[D / 16]) {
   const u32x4 ones = {kOnes<T>, kOnes<T>, kOnes<T>, kOnes<T>};
-#pragma unroll
-  for (int nb0 = 0; nb0 < NB; nb0 += NBB) {
-    u32x2 h[2 * NBB];
-#pragma unroll
-    for (int j = 0; j < NBB; ++j) {
-      h[2 * j] = lds_read_tr16<OFF0>(stage + voff[nb0 + j]);
-      h[2 * j + 1] = lds_read_tr16<OFF1>(stage + voff[nb0 + j]);
-    }
-    lds_wait(h);
-#pragma unroll
-    for (int j = 0; j < NBB; ++j) {
-      const u32x4 va = {h[2 * j].x, h[2 * j].y, h[2 * j + 1].x, h[2 * j + 1].y};
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc[b][nb0 + j] = PMma<T>::mma(va, pop[b], acc[b][nb0 + j]);
-    }
+  u32x2 h0[8], h1[8];
+  if constexpr (D == 128) {
+    pv_read<D, 0, 0>(h0, stage, voff);
+    pv_read<D, 0, 4>(h1, stage, voff);
+    lds_wait<8>(h0);
+    pv_mma<T, D, 0>(acc, h0, pop[0]);
+    pv_read<D, 1, 0>(h0, stage, voff);
+    lds_wait<8>(h1);
+    pv_mma<T, D, 4>(acc, h1, pop[0]);
+    pv_read<D, 1, 4>(h1, stage, voff);
+    lds_wait<8>(h0);
+    pv_mma<T, D, 0>(acc, h0, pop[1]);
+    lds_wait<0>(h1);
+    pv_mma<T, D, 4>(acc, h1, pop[1]);
+  } else {
+    pv_read<D, 0, 0>(h0, stage, voff);
+    pv_read<D, 1, 0>(h1, stage, voff);
+    lds_wait<8>(h0);
+    pv_mma<T, D, 0>(acc, h0, pop[0]);
+    lds_wait<0>(h1);
+    pv_mma<T, D, 0>(acc, h1, pop[1]);
   }
 #pragma unroll
-  for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[b], acc_l[b]);
+  for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[ap][b], acc_l[b]);
 }
 
 // Two stages of (K tile, V tile).
@@ -340,21 +371,29 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     // ---- raw products q.k for 4 key row-tiles x 2 query column-tiles
     const bool diag = kt * kKeyTile + kKeyTile - 1 > min_lim;   // uniform
     float s[4][2][4];
+    // K pieces of all four 16-key blocks are read up front; the products
+    // run c-outermost so that eight independent accumulation chains
+    // interleave on the matrix cores.
+    u32x4 ka[4][NC];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      u32x4 ka[NC];
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        ka[c] = *reinterpret_cast<const u32x4*>(k_lds + a * 16 * D * 2 + koff[c]);
+        ka[a][c] = *reinterpret_cast<const u32x4*>(k_lds + a * 16 * D * 2 + koff[c]);
+    f32x4 sc[4][2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) sc = PMma<T>::mma(ka[c], qop[b][c], sc);
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[a][b][i] = sc[i];
-      }
-    }
+        for (int b = 0; b < 2; ++b)
+          sc[a][b] = PMma<T>::mma(ka[a][c], qop[b][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[a][b]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[a][b][i] = sc[a][b][i];
     if (diag) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -407,8 +446,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     // (c16 & 3) of the 4-element row addressed by lane 4 t + (c16 >> 2),
     // for t = 0..3; lane s therefore addresses key 4 G + (s >> 2) (+ 16 for
     // the second read), dimensions 16 nn + 4 (s & 3) .. + 3.
-    pv_half<T, D, 0>(acc, acc_l, pop[0], v_base, voff);
-    pv_half<T, D, 1>(acc, acc_l, pop[1], v_base, voff);
+    pv_tile<T, D>(acc, acc_l, pop, v_base, voff);
     if (more) {
       // this wave's copy of the next tile has landed; after the barrier all
       // copies have, and every wave is done with this tile's stage
