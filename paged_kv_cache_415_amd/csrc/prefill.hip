@@ -380,6 +380,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         ka[a][c] = *reinterpret_cast<const u32x4*>(k_lds + a * 16 * D * 2 + koff[c]);
+    // MFMA-heavy phases run at raised wave priority, so that on a SIMD shared
+    // with a wave in its softmax phase the matrix core is fed first.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 sc[4][2];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -403,30 +406,41 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
           for (int i = 0; i < 4; ++i)
             if (kt * kKeyTile + 16 * a + 4 * G + i > lim[b]) s[a][b][i] = -INFINITY;
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- online softmax per query row (lane column), probabilities -> operands
-    u32x4 pop[2][2];   // [key pair][column tile]
+    // Both column tiles go through each phase together (two independent
+    // dependency chains), with one rescaling decision for the pair.
+    float mx[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      float mx = s[0][b][0];
+      mx[b] = s[0][b][0];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (a + i > 0) mx = fmax_nan(mx, s[a][b][i]);
-      mx = max_over_groups(mx);
-      mx *= cscale;   // cscale > 0: -inf stays -inf
-      // Lazy rescaling (as in decode): the reference max moves only when a
-      // row's max exceeds it by more than kSlack, so p <= 2^kSlack.  A row
-      // whose keys are all masked in this tile has mx = -inf and keeps it.
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[b] + kSlack) != 0) {
-        const float m_new = fmaxf(m_run[b], mx);
+          if (a + i > 0) mx[b] = fmax_nan(mx[b], s[a][b][i]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) mx[b] = max_over_groups(mx[b]) * cscale;   // cscale > 0: -inf stays -inf
+    // Lazy rescaling (as in decode): the reference max moves only when a
+    // row's max exceeds it by more than kSlack, so p <= 2^kSlack; when it
+    // moves for some row, every row of the wave takes its exact new max.  A
+    // row whose keys are all masked in this tile has mx = -inf and keeps it.
+    if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kSlack || mx[1] > m_run[1] + kSlack) != 0) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float m_new = fmaxf(m_run[b], mx[b]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
         m_run[b] = m_new;
         acc_l[b] = acc_l[b] * alpha;
 #pragma unroll
         for (int nn = 0; nn < NB; ++nn) acc[b][nn] = acc[b][nn] * alpha;
       }
-      // p = 2^(c * (q.k) - m): one fused multiply-add per score
+    }
+    // p = 2^(c * (q.k) - m): one fused multiply-add per score
+    u32x4 pop[2][2];   // [key pair][column tile]
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
       const float nm = -m_run[b];
       uint32_t w[4][2];
 #pragma unroll
@@ -439,14 +453,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
       for (int ap = 0; ap < 2; ++ap)
         pop[ap][b] = u32x4{w[2 * ap][0], w[2 * ap][1], w[2 * ap + 1][0], w[2 * ap + 1][1]};
     }
-    // ---- values: the A operand of dimension block nn holds, in lane
-    // (G, c16), dimension 16 nn + c16 of the lane's eight keys 32 ap + 4 G +
-    // 0..3 and 32 ap + 16 + 4 G + 0..3 (the probability operand's keys).  A
-    // transposing read returns to lane c16 of a 16-lane group the element
-    // (c16 & 3) of the 4-element row addressed by lane 4 t + (c16 >> 2),
-    // for t = 0..3; lane s therefore addresses key 4 G + (s >> 2) (+ 16 for
-    // the second read), dimensions 16 nn + 4 (s & 3) .. + 3.
+    __builtin_amdgcn_s_setprio(1);
     pv_tile<T, D>(acc, acc_l, pop, v_base, voff);
+    __builtin_amdgcn_s_setprio(0);
     if (more) {
       // this wave's copy of the next tile has landed; after the barrier all
       // copies have, and every wave is done with this tile's stage
