@@ -289,6 +289,72 @@ def run_mixed_bench(args, dev):
     }
 
 
+def run_block_ops_bench(dev, iters: int = 20) -> dict:
+    """Rates of the block-management copies beside the mixed step: token-
+    granular copy-on-write, one block copy applied to 32 layers, and swapping
+    blocks out to pinned host memory and back (shapes of the mixed workload:
+    8 KV heads x 32 tokens x 128 dims, bf16 = 64 KB per block and pool)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_415_amd as pa
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4151)
+    hkv, bs, d = 8, 32, 128
+    blk_bytes = hkv * bs * d * 2
+
+    def pool(n, device=dev):
+        return torch.randn((n, hkv, bs, d), generator=gen, device=dev, dtype=torch.float32).to(
+            torch.bfloat16).to(device)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    rng = np.random.default_rng(4152)
+    out = {}
+    # token-granular CoW: 1,024 forks inside a block, n ~ U[1, 31] rows each
+    kp, vp = pool(4096), pool(4096)
+    ids = rng.permutation(4096)
+    counts = rng.integers(1, bs, size=1024)
+    triples = torch.from_numpy(np.stack([ids[:1024], ids[1024:2048], counts], 1).astype(np.int64)).to(dev)
+    ms = timed(lambda: pa.pa_copy_blocks_partial(kp, vp, triples))
+    moved = int(counts.sum()) * hkv * d * 2 * 2 * 2          # rows x (K, V) x (read, write)
+    out["copy_partial"] = {"pairs": 1024, "bytes_moved": moved, "ms": round(ms, 5),
+                           "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    del kp, vp
+    # one fork across 32 layers: 15 block copies per layer, one launch
+    layers = 32
+    kps, vps = [pool(64) for _ in range(layers)], [pool(64) for _ in range(layers)]
+    pairs = torch.from_numpy(np.stack([np.arange(15), np.arange(32, 47)], 1).astype(np.int64)).to(dev)
+    kptr, vptr = pa.layer_pool_pointers(kps, dev), pa.layer_pool_pointers(vps, dev)
+    ms = timed(lambda: pa.pa_copy_blocks_layers(kptr, vptr, pairs, block_bytes=blk_bytes))
+    moved = layers * 15 * blk_bytes * 2 * 2
+    out["copy_layers"] = {"layers": layers, "pairs": 15, "bytes_moved": moved, "ms": round(ms, 5),
+                          "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    del kps, vps
+    # swap 512 blocks (32 MB) of one pool out to pinned host memory and back
+    dp = pool(2048)
+    hp = torch.empty((512, hkv, bs, d), dtype=torch.bfloat16).pin_memory()
+    dev_ids = torch.from_numpy(rng.permutation(2048)[:512].astype(np.int64))
+    out_pairs = torch.stack([dev_ids, torch.arange(512)], 1).to(dev)
+    in_pairs = torch.stack([torch.arange(512), dev_ids], 1).to(dev)
+    ms_out = timed(lambda: pa.pa_swap_blocks(hp, dp, out_pairs))
+    ms_in = timed(lambda: pa.pa_swap_blocks(dp, hp, in_pairs))
+    moved = 512 * blk_bytes
+    out["swap"] = {"blocks": 512, "bytes_each_way": moved,
+                   "out_ms": round(ms_out, 5), "out_gbps": round(moved / (ms_out * 1e-3) / 1e9, 1),
+                   "in_ms": round(ms_in, 5), "in_gbps": round(moved / (ms_in * 1e-3) / 1e9, 1)}
+    return out
+
+
 # ---------------------------------------------------------------------------
 # HBM traffic of the decode kernel from committed rocprofv3 counter runs
 # ---------------------------------------------------------------------------
@@ -406,6 +472,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.config == "mixed_prefix_bf16":
         res = run_mixed_bench(args, dev)
+        res["block_ops"] = run_block_ops_bench(dev)
     else:
         res = run_decode_bench(args, dev)
     res["probe_read_gbps"] = round(probe_read_gbps(dev), 1)

@@ -116,6 +116,55 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs,
                          int64_t block_bytes, void* stream);
 
 /*
+ * pa_copy_blocks_partial — copy-on-write of partly filled blocks.
+ *
+ * [bogosort] §17 Parallel Sampling: sequences forked from one prompt share
+ * its blocks and write what follows the fork into blocks of their own; when
+ * the fork falls inside a block, the new block needs only the tokens that
+ * precede the fork.  For each triple p of block_triples (int64
+ * [num_pairs][3] = src, dst, n in device memory), rows [0, n) of every KV
+ * head of block dst of k_pool and of v_pool become those of block src; the
+ * other rows of dst are left as they are.  n is clamped to
+ * [0, block_size].  Pools are [blocks][num_kv_heads][block_size][row] with
+ * row_bytes = head_dim * element bytes (a multiple of 16).  Destinations
+ * must be distinct and never a source in the same call.  num_pairs == 0 is
+ * a no-op.
+ */
+pa_status pa_copy_blocks_partial(void* k_pool, void* v_pool, const int64_t* block_triples, int32_t num_pairs,
+                                 int32_t num_kv_heads, int32_t block_size, int64_t row_bytes, void* stream);
+
+/*
+ * pa_copy_blocks_layers — the same whole-block copies in every layer.
+ *
+ * [ybb] §2.2 Copy-on-Write: a fork duplicates a shared block in each
+ * layer's cache.  k_pools and v_pools are device arrays of num_layers
+ * device pointers (one K and one V pool per layer, all with the same block
+ * size block_bytes, a multiple of 16); for each (src, dst) pair of
+ * block_pairs (int64 [num_pairs][2], device memory) and each layer, block
+ * dst becomes a copy of block src.  One launch covers all layers.
+ */
+pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                                const int64_t* block_pairs, int32_t num_pairs, int64_t block_bytes,
+                                void* stream);
+
+/*
+ * pa_swap_blocks — move blocks between two pools, e.g. to and from CPU
+ * memory.
+ *
+ * [ybb] §三 Continuous Batching, the preemption bullet: when memory runs
+ * short, the block manager swaps blocks out to CPU memory (and back in
+ * later).  For each (src, dst) pair of block_pairs (int64 [num_pairs][2]),
+ * block dst of dst_pool becomes a copy of block src of src_pool
+ * (block_bytes each, a multiple of 16).  Each of dst_pool, src_pool and
+ * block_pairs is device memory or pinned host memory (hipHostMalloc, or a
+ * pinned torch tensor), reached by the kernel through its device mapping;
+ * pageable host memory is rejected with PA_ERR_INVALID_ARG.  Call it once
+ * for the K pools and once for the V pools.  The pools must not overlap.
+ */
+pa_status pa_swap_blocks(void* dst_pool, const void* src_pool, const int64_t* block_pairs, int32_t num_pairs,
+                         int64_t block_bytes, void* stream);
+
+/*
  * Split-KV planning for decode.  The decode kernel is persistent: each of
  * its waves processes one or more segments, a segment being a run of
  * 32-token steps of one (sequence, KV head) pair.  A pair whose context is

@@ -39,6 +39,9 @@ from .paged import (
     prefill_chunk_attention,
     reshape_and_cache,
     copy_blocks,
+    copy_block_rows,
+    copy_blocks_layers,
+    swap_blocks,
 )
 
 __all__ = [
@@ -54,4 +57,7 @@ __all__ = [
     "prefill_chunk_attention",
     "reshape_and_cache",
     "copy_blocks",
+    "copy_block_rows",
+    "copy_blocks_layers",
+    "swap_blocks",
 ]

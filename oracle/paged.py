@@ -242,3 +242,52 @@ def copy_blocks(k_pool, v_pool, pairs):
         k_new[dst] = k_pool[src]
         v_new[dst] = v_pool[src]
     return k_new, v_new
+
+
+def copy_block_rows(k_pool, v_pool, triples):
+    """Copy-on-write of partly filled blocks; returns new (k_pool, v_pool).
+
+    bogosort page "五十三：vLLM-PagedAttention" §17 Parallel Sampling: forked
+    sequences share the prompt's blocks and write what follows the fork into
+    blocks of their own.  When the fork falls inside a block, only the tokens
+    before it are carried over: for each (src, dst, n) triple, rows [0, n)
+    of every KV head of block dst become those of block src, with n clamped
+    to [0, block_size]; every other row keeps its contents.
+    """
+    k_new = np.array(k_pool, copy=True)
+    v_new = np.array(v_pool, copy=True)
+    block_size = k_pool.shape[2]
+    for src, dst, n in np.asarray(triples, dtype=np.int64).reshape(-1, 3):
+        n = min(max(int(n), 0), block_size)
+        k_new[dst, :, :n, :] = k_pool[src, :, :n, :]
+        v_new[dst, :, :n, :] = v_pool[src, :, :n, :]
+    return k_new, v_new
+
+
+def copy_blocks_layers(k_pools, v_pools, pairs):
+    """The same copy-on-write block copies applied in every layer's pools.
+
+    ybb.press page §2.2 "Copy-on-Write 与共享前缀": a fork duplicates each
+    shared block, and a model keeps one K and one V cache per layer, so the
+    copy is repeated layer by layer.  Returns lists of new pools.
+    """
+    out_k, out_v = [], []
+    for kp, vp in zip(k_pools, v_pools):
+        nk, nv = copy_blocks(kp, vp, pairs)
+        out_k.append(nk)
+        out_v.append(nv)
+    return out_k, out_v
+
+
+def swap_blocks(dst_pool, src_pool, pairs):
+    """Block moves between two pools (swap out to CPU memory and back in).
+
+    ybb.press page §三 (Continuous Batching), the preemption bullet: under
+    memory pressure the block manager moves blocks to CPU memory and later
+    back.  For each (src, dst) pair block dst of a copy of dst_pool becomes
+    block src of src_pool.
+    """
+    out = np.array(dst_pool, copy=True)
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        out[dst] = src_pool[src]
+    return out

@@ -52,6 +52,9 @@ def _load() -> ctypes.CDLL:
     lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32,
                                          i32, f32, f32, vp]
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i64, vp]
+    lib.pa_copy_blocks_partial.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp]
+    lib.pa_copy_blocks_layers.argtypes = [vp, vp, i32, vp, i32, i64, vp]
+    lib.pa_swap_blocks.argtypes = [vp, vp, vp, i32, i64, vp]
     lib.pa_decode_partition_size.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_partition_size.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -69,7 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_probe_read.argtypes = [vp, sz, vp, vp]
     lib.pa_probe_copy.argtypes = [vp, vp, sz, vp]
-    for name in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_prefill_chunk", "pa_probe_read",
+    for name in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_copy_blocks_partial",
+                 "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_probe_read",
                  "pa_probe_copy"):
         getattr(lib, name).restype = i32
     return lib
@@ -87,14 +91,16 @@ def _check(status: int) -> None:
         raise PagedAttentionError(status, _lib.pa_last_error().decode())
 
 
-def _ptr(t, contiguous: bool = True):
+def _ptr(t, contiguous: bool = True, host_ok: bool = False):
+    """Data pointer of a GPU tensor (or, with host_ok, of a CPU tensor: the
+    library itself accepts only pinned host memory there)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError("expected a torch tensor")
     if contiguous and not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
-    if t.device.type != "cuda":
+    if t.device.type != "cuda" and not (host_ok and t.device.type == "cpu"):
         raise ValueError("tensors must be on the GPU")
     return t.data_ptr()
 
@@ -138,6 +144,71 @@ def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
         raise TypeError("block_pairs must be int64")
     block_bytes = k_pool[0].numel() * k_pool.element_size()
     _check(_lib.pa_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(block_pairs),
+                               block_pairs.shape[0], block_bytes, _stream(stream)))
+
+
+def pa_copy_blocks_partial(k_pool, v_pool, block_triples, stream=None) -> None:
+    """Copy rows [0, n) of every KV head of block src into block dst, for each
+    (src, dst, n) triple, in both pools (see pa.h)."""
+    if block_triples.dtype != torch.int64:
+        raise TypeError("block_triples must be int64")
+    _, hkv, bs, d = k_pool.shape
+    _check(_lib.pa_copy_blocks_partial(_ptr(k_pool), _ptr(v_pool), _ptr(block_triples),
+                                       block_triples.shape[0], hkv, bs, d * k_pool.element_size(),
+                                       _stream(stream)))
+
+
+def layer_pool_pointers(pools, device) -> torch.Tensor:
+    """Device array of the pools' addresses, as pa_copy_blocks_layers takes them
+    (build it once for a fixed set of layer caches)."""
+    shape, dtype = pools[0].shape, pools[0].dtype
+    for t in pools:
+        if t.shape != shape or t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("every pool must be a contiguous GPU tensor of one shape and dtype")
+    return torch.tensor([t.data_ptr() for t in pools], dtype=torch.int64, device=device)
+
+
+def pa_copy_blocks_layers(k_pools, v_pools, block_pairs, stream=None, block_bytes=None) -> None:
+    """Apply the same whole-block (src, dst) copies to the K and V pools of
+    every layer in one launch (see pa.h).  k_pools, v_pools: lists of pools of
+    one shape and dtype, or address arrays from layer_pool_pointers (then
+    block_bytes, the bytes of one block of one pool, is required)."""
+    if block_pairs.dtype != torch.int64:
+        raise TypeError("block_pairs must be int64")
+    if isinstance(k_pools, torch.Tensor):
+        if not isinstance(v_pools, torch.Tensor) or k_pools.dtype != torch.int64 or block_bytes is None:
+            raise ValueError("address arrays need int64 tensors for both pools and block_bytes")
+        kp, vp = k_pools, v_pools
+    else:
+        if len(k_pools) != len(v_pools):
+            raise ValueError("k_pools and v_pools differ in length")
+        if not k_pools:
+            return
+        kp = layer_pool_pointers(k_pools, block_pairs.device)
+        vp = layer_pool_pointers(v_pools, block_pairs.device)
+        if k_pools[0].shape != v_pools[0].shape or k_pools[0].dtype != v_pools[0].dtype:
+            raise ValueError("K and V pools differ in shape or dtype")
+        block_bytes = k_pools[0][0].numel() * k_pools[0].element_size()
+    if kp.numel() != vp.numel():
+        raise ValueError("k_pools and v_pools differ in length")
+    _check(_lib.pa_copy_blocks_layers(_ptr(kp), _ptr(vp), kp.numel(), _ptr(block_pairs),
+                                      block_pairs.shape[0], block_bytes, _stream(stream)))
+    if stream is not None:
+        # the address arrays may be freed when this call returns: keep them
+        # alive for the launch on a stream other than the allocator's
+        kp.record_stream(stream)
+        vp.record_stream(stream)
+
+
+def pa_swap_blocks(dst_pool, src_pool, block_pairs, stream=None) -> None:
+    """Block dst of dst_pool = block src of src_pool for each (src, dst) pair;
+    either pool may be a pinned CPU tensor (see pa.h)."""
+    if block_pairs.dtype != torch.int64:
+        raise TypeError("block_pairs must be int64")
+    if dst_pool.dtype != src_pool.dtype or dst_pool.shape[1:] != src_pool.shape[1:]:
+        raise ValueError("pools must have the same dtype and block shape")
+    block_bytes = dst_pool[0].numel() * dst_pool.element_size()
+    _check(_lib.pa_swap_blocks(_ptr(dst_pool, host_ok=True), _ptr(src_pool, host_ok=True), _ptr(block_pairs),
                                block_pairs.shape[0], block_bytes, _stream(stream)))
 
 
@@ -225,7 +296,9 @@ def pa_probe_copy(dst, src, stream=None) -> None:
 
 
 __all__ = [
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_decode_attention",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
+    "layer_pool_pointers",
+    "pa_swap_blocks", "pa_decode", "pa_decode_attention",
     "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",
     "pa_decode_workspace_bytes", "decode_workspace", "pa_probe_read", "pa_probe_copy",
     "PagedAttentionError", "library", "LIB_PATH",

@@ -1,5 +1,6 @@
-// Slot scatter (reshape_and_cache), whole-block copy (copy-on-write) and
-// the HBM probe kernels.
+// Slot scatter (reshape_and_cache), block copies (whole-block and
+// partial-block copy-on-write, one layer or many), block moves between pools
+// (swapping to host memory) and the HBM probe kernels.
 //
 // The scatter follows the datawhalechina page "17. vLLM PagedAttention"
 // (Step 3 item 3 / Step 4: each generated token's K/V goes into the
@@ -81,19 +82,86 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterParams p) {
   }
 }
 
+// Copy nvec 16-byte vectors with the workgroups of grid dimension x; each
+// thread keeps four loads in flight.
+__device__ __forceinline__ void copy_vecs(char* dst, const char* src, int64_t nvec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const u32x4 a = ld16(src + i * 16), b = ld16(src + (i + stride) * 16);
+    const u32x4 c = ld16(src + (i + 2 * stride) * 16), d = ld16(src + (i + 3 * stride) * 16);
+    st16(dst + i * 16, a);
+    st16(dst + (i + stride) * 16, b);
+    st16(dst + (i + 2 * stride) * 16, c);
+    st16(dst + (i + 3 * stride) * 16, d);
+  }
+  for (; i < nvec; i += stride) st16(dst + i * 16, ld16(src + i * 16));
+}
+
+// Workgroups along x for a copy of nvec vectors: four vectors per thread.
+inline int copy_chunks(int64_t nvec) {
+  int64_t c = (nvec + 1023) / 1024;
+  return (int)(c < 1 ? 1 : (c > 64 ? 64 : c));
+}
+
 // One workgroup per (pair, chunk of the block); K and V pools both copied.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p) {
   const int pair = blockIdx.y;
   const int64_t src = p.pairs[2 * pair];
   const int64_t dst = p.pairs[2 * pair + 1];
   const int64_t nvec = p.block_bytes / 16;
+  char* k = static_cast<char*>(p.k_pool);
+  char* v = static_cast<char*>(p.v_pool);
+  copy_vecs(k + dst * p.block_bytes, k + src * p.block_bytes, nvec);
+  copy_vecs(v + dst * p.block_bytes, v + src * p.block_bytes, nvec);
+}
+
+// Copy-on-write of a partly filled block (bogosort page "五十三：
+// vLLM-PagedAttention" §17 Parallel Sampling: after a fork each sequence
+// writes into its own blocks): only the rows [0, n) that hold tokens are
+// copied, head by head (each head's rows are contiguous in a block).  n is
+// clamped to [0, block_size].
+__global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsParams p) {
+  const int pair = blockIdx.y;
+  const int64_t src = p.triples[3 * pair];
+  const int64_t dst = p.triples[3 * pair + 1];
+  int64_t n = p.triples[3 * pair + 2];
+  n = n < 0 ? 0 : (n > p.block_size ? p.block_size : n);
+  const int64_t head_bytes = (int64_t)p.block_size * p.row_bytes;
+  const int64_t vph = n * p.row_bytes / 16;            // 16-byte vectors per head
+  const int64_t nvec = vph * p.num_kv_heads;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t so = src * p.block_bytes + i * 16;
-    const int64_t d = dst * p.block_bytes + i * 16;
+    const int64_t h = i / vph, v = i - h * vph;
+    const int64_t so = (src * p.num_kv_heads + h) * head_bytes + v * 16;
+    const int64_t d = (dst * p.num_kv_heads + h) * head_bytes + v * 16;
     st16((char*)p.k_pool + d, ld16((const char*)p.k_pool + so));
     st16((char*)p.v_pool + d, ld16((const char*)p.v_pool + so));
   }
+}
+
+// The same whole-block copies in the pools of every layer (one launch for a
+// fork across the model: ybb.press page §2.2 Copy-on-Write 与共享前缀).
+__global__ __launch_bounds__(256) void copy_layers_kernel(CopyLayersParams p) {
+  const int pair = blockIdx.y, layer = blockIdx.z;
+  const int64_t src = p.pairs[2 * pair];
+  const int64_t dst = p.pairs[2 * pair + 1];
+  char* k = static_cast<char*>(p.k_pools[layer]);
+  char* v = static_cast<char*>(p.v_pools[layer]);
+  const int64_t nvec = p.block_bytes / 16;
+  copy_vecs(k + dst * p.block_bytes, k + src * p.block_bytes, nvec);
+  copy_vecs(v + dst * p.block_bytes, v + src * p.block_bytes, nvec);
+}
+
+// Block moves between two pools (ybb.press page §三, the preemption bullet:
+// blocks are swapped out to CPU memory and back).  Host memory is reached
+// through its device mapping, so one launch moves any set of blocks.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(SwapParams p) {
+  const int pair = blockIdx.y;
+  const int64_t src = p.pairs[2 * pair];
+  const int64_t dst = p.pairs[2 * pair + 1];
+  copy_vecs(static_cast<char*>(p.dst) + dst * p.block_bytes,
+            static_cast<const char*>(p.src) + src * p.block_bytes, p.block_bytes / 16);
 }
 
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream) {
@@ -113,11 +181,31 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream) {
 
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream) {
   if (p.num_pairs == 0) return hipSuccess;
-  const int64_t nvec = p.block_bytes / 16;
+  dim3 grid(copy_chunks(p.block_bytes / 16), p.num_pairs), block(256);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const CopyRowsParams& p, hipStream_t stream) {
+  if (p.num_pairs == 0) return hipSuccess;
+  const int64_t nvec = (int64_t)p.num_kv_heads * p.block_size * p.row_bytes / 16;
   int chunks = (int)((nvec + 255) / 256);
   if (chunks > 64) chunks = 64;
-  dim3 grid(chunks, p.num_pairs), block(256);
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, p);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(chunks, p.num_pairs), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_layers(const CopyLayersParams& p, hipStream_t stream) {
+  if (p.num_pairs == 0 || p.num_layers == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_layers_kernel, dim3(copy_chunks(p.block_bytes / 16), p.num_pairs, p.num_layers),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const SwapParams& p, hipStream_t stream) {
+  if (p.num_pairs == 0) return hipSuccess;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(copy_chunks(p.block_bytes / 16), p.num_pairs), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -294,6 +294,93 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs,
   return hip_status(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "copy launch");
 }
 
+pa_status pa_copy_blocks_partial(void* k_pool, void* v_pool, const int64_t* block_triples, int32_t num_pairs,
+                                 int32_t num_kv_heads, int32_t block_size, int64_t row_bytes, void* stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs < 0");
+  if (num_pairs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_pairs > 65535");
+  if (num_kv_heads <= 0 || block_size <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads and block_size must be > 0");
+  if (row_bytes <= 0 || row_bytes % 16)
+    return fail(PA_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !block_triples) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_triples, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  pa::CopyRowsParams p{};
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.triples = block_triples;
+  p.row_bytes = row_bytes;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.num_pairs = num_pairs;
+  return hip_status(pa::launch_copy_rows(p, static_cast<hipStream_t>(stream)), "partial copy launch");
+}
+
+pa_status pa_copy_blocks_layers(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                                const int64_t* block_pairs, int32_t num_pairs, int64_t block_bytes,
+                                void* stream) {
+  if (num_pairs < 0 || num_layers < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs or num_layers < 0");
+  if (num_pairs > 65535 || num_layers > 65535) return fail(PA_ERR_UNSUPPORTED, "num_pairs or num_layers > 65535");
+  if (block_bytes <= 0 || block_bytes % 16)
+    return fail(PA_ERR_INVALID_ARG, "block_bytes must be a positive multiple of 16");
+  if (num_pairs == 0 || num_layers == 0) return ok();
+  if (!k_pools || !v_pools || !block_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(k_pools, 8) || !aligned(v_pools, 8) || !aligned(block_pairs, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  pa::CopyLayersParams p{};
+  p.k_pools = k_pools;
+  p.v_pools = v_pools;
+  p.pairs = block_pairs;
+  p.block_bytes = block_bytes;
+  p.num_pairs = num_pairs;
+  p.num_layers = num_layers;
+  return hip_status(pa::launch_copy_layers(p, static_cast<hipStream_t>(stream)), "layer copy launch");
+}
+
+namespace {
+// Address at which kernels reach `ptr`: device memory as it is, pinned host
+// memory through its device mapping; pageable host memory is rejected.
+bool device_address(const void* ptr, const void** out) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged || a.type == hipMemoryTypeUnified) {
+    *out = ptr;
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer) {
+    *out = static_cast<const char*>(a.devicePointer) +
+           (static_cast<const char*>(ptr) - static_cast<const char*>(a.hostPointer));
+    return true;
+  }
+  return false;
+}
+}  // namespace
+
+pa_status pa_swap_blocks(void* dst_pool, const void* src_pool, const int64_t* block_pairs, int32_t num_pairs,
+                         int64_t block_bytes, void* stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs < 0");
+  if (num_pairs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_pairs > 65535");
+  if (block_bytes <= 0 || block_bytes % 16)
+    return fail(PA_ERR_INVALID_ARG, "block_bytes must be a positive multiple of 16");
+  if (num_pairs == 0) return ok();
+  if (!dst_pool || !src_pool || !block_pairs) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(dst_pool, 16) || !aligned(src_pool, 16) || !aligned(block_pairs, 8))
+    return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
+  const void *d = nullptr, *s = nullptr, *pr = nullptr;
+  if (!device_address(dst_pool, &d) || !device_address(src_pool, &s) || !device_address(block_pairs, &pr))
+    return fail(PA_ERR_INVALID_ARG, "pools and pairs must be device memory or pinned host memory");
+  pa::SwapParams p{};
+  p.dst = const_cast<void*>(d);
+  p.src = s;
+  p.pairs = static_cast<const int64_t*>(pr);
+  p.block_bytes = block_bytes;
+  p.num_pairs = num_pairs;
+  return hip_status(pa::launch_swap_blocks(p, static_cast<hipStream_t>(stream)), "swap launch");
+}
+
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                  int32_t max_seq_len, int32_t partition_size) {
   (void)num_seqs;

@@ -39,6 +39,39 @@ struct CopyParams {
   int num_pairs;
 };
 
+// Copy of the first rows of blocks: for each triple (src, dst, n), rows
+// [0, n) of every KV head of block dst become those of block src.
+struct CopyRowsParams {
+  void* k_pool;
+  void* v_pool;
+  const int64_t* triples;
+  int64_t row_bytes;
+  int num_kv_heads;
+  int block_size;
+  int num_pairs;
+};
+
+// Whole-block copies applied to the K and V pools of several layers; the
+// pool pointers are device arrays of num_layers entries.
+struct CopyLayersParams {
+  void* const* k_pools;
+  void* const* v_pools;
+  const int64_t* pairs;
+  int64_t block_bytes;
+  int num_pairs;
+  int num_layers;
+};
+
+// Block moves from one pool to another (either may be host memory mapped
+// for device access): block pairs[2p + 1] of dst = block pairs[2p] of src.
+struct SwapParams {
+  void* dst;
+  const void* src;
+  const int64_t* pairs;
+  int64_t block_bytes;
+  int num_pairs;
+};
+
 // How a decode call cuts each (sequence, KV head) pair's context into the
 // segments that single waves process.  Units are 32-token steps.
 enum : int {
@@ -99,6 +132,9 @@ struct PrefillParams {
 
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
+hipError_t launch_copy_rows(const CopyRowsParams& p, hipStream_t stream);
+hipError_t launch_copy_layers(const CopyLayersParams& p, hipStream_t stream);
+hipError_t launch_swap_blocks(const SwapParams& p, hipStream_t stream);
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

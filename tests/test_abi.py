@@ -148,6 +148,27 @@ def test_scatter_and_copy_empty_are_ok(lib):
     assert lib.pa_copy_blocks(None, None, None, 2, 4096, None) == INVALID
 
 
+def test_partial_layer_and_swap_copies_check_arguments(lib):
+    # partial copy: (k, v, triples, pairs, heads, block_size, row_bytes, stream)
+    assert lib.pa_copy_blocks_partial(None, None, None, 0, 8, 16, 256, None) == OK
+    assert lib.pa_copy_blocks_partial(None, None, None, -1, 8, 16, 256, None) == INVALID
+    assert lib.pa_copy_blocks_partial(None, None, None, 2, 8, 16, 250, None) == INVALID
+    assert lib.pa_copy_blocks_partial(None, None, None, 2, 0, 16, 256, None) == INVALID
+    assert lib.pa_copy_blocks_partial(None, None, None, 2, 8, 16, 256, None) == INVALID   # nulls
+    assert lib.pa_copy_blocks_partial(None, None, None, 70000, 8, 16, 256, None) == UNSUPPORTED
+    # layers: (k_pools, v_pools, layers, pairs, num_pairs, block_bytes, stream)
+    assert lib.pa_copy_blocks_layers(None, None, 0, None, 3, 4096, None) == OK
+    assert lib.pa_copy_blocks_layers(None, None, 4, None, 0, 4096, None) == OK
+    assert lib.pa_copy_blocks_layers(None, None, -1, None, 3, 4096, None) == INVALID
+    assert lib.pa_copy_blocks_layers(None, None, 4, None, 3, 4100, None) == INVALID
+    assert lib.pa_copy_blocks_layers(None, None, 4, None, 3, 4096, None) == INVALID      # nulls
+    # swap: (dst, src, pairs, num_pairs, block_bytes, stream)
+    assert lib.pa_swap_blocks(None, None, None, 0, 4096, None) == OK
+    assert lib.pa_swap_blocks(None, None, None, 2, 4104, None) == INVALID
+    assert lib.pa_swap_blocks(None, None, None, 2, 4096, None) == INVALID                # nulls
+    assert lib.pa_swap_blocks(None, None, None, -5, 4096, None) == INVALID
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(hq=12, hkv=4), UNSUPPORTED),            # group 3: not a power of two
     (dict(qdt=BF16, cdt=FP8), UNSUPPORTED),

@@ -126,3 +126,93 @@ def test_empty_calls_are_noops():
     pa.pa_copy_blocks(gk, gk, up_int(np.zeros((0, 2), np.int64)))
     torch.cuda.synchronize()
     assert torch.equal(gk, before)
+
+
+@pytest.mark.parametrize("dtype,hkv,bs,d", [("bf16", 8, 32, 128), ("fp8_e4m3", 8, 16, 128),
+                                            ("f32", 2, 16, 64), ("f16", 3, 32, 64)])
+def test_copy_blocks_partial_bytes(dtype, hkv, bs, d):
+    """Token-granular copy-on-write: counts 0, 1, mid, whole block, beyond the
+    block and negative (clamped), whole pools compared byte for byte."""
+    rng = np.random.default_rng(5)
+    nb = 48
+    kp, _ = _pools(nb, hkv, bs, d, dtype, rng)
+    vp, _ = _pools(nb, hkv, bs, d, dtype, rng)
+    ids = rng.permutation(nb)
+    counts = np.array([0, 1, bs // 2, bs - 1, bs, bs + 7, -4, 3, bs // 3, 2, 5, bs], dtype=np.int64)
+    triples = np.stack([ids[:12], ids[12:24], counts], axis=1).astype(np.int64)
+    okp, ovp = oracle.copy_block_rows(kp, vp, triples)
+    gk, gv = up(kp, dtype), up(vp, dtype)
+    lib().pa_copy_blocks_partial(gk, gv, up_int(triples))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(gk, dtype), okp)
+    assert np.array_equal(W.torch_to_bits(gv, dtype), ovp)
+
+
+@pytest.mark.parametrize("form", ["lists", "addresses"])
+def test_copy_blocks_layers_bytes(form):
+    """One launch applies the block copies to the K and V pools of 5 layers."""
+    rng = np.random.default_rng(6)
+    nb, hkv, bs, d, layers = 40, 8, 32, 128, 5
+    kps = [_pools(nb, hkv, bs, d, "bf16", rng)[0] for _ in range(layers)]
+    vps = [_pools(nb, hkv, bs, d, "bf16", rng)[0] for _ in range(layers)]
+    ids = rng.permutation(nb)
+    pairs = np.stack([ids[:9], ids[9:18]], axis=1).astype(np.int64)
+    oks, ovs = oracle.copy_blocks_layers(kps, vps, pairs)
+    gks, gvs = [up(k, "bf16") for k in kps], [up(v, "bf16") for v in vps]
+    pa = lib()
+    if form == "lists":
+        pa.pa_copy_blocks_layers(gks, gvs, up_int(pairs))
+    else:
+        kp = pa.layer_pool_pointers(gks, gks[0].device)
+        vp = pa.layer_pool_pointers(gvs, gvs[0].device)
+        pa.pa_copy_blocks_layers(kp, vp, up_int(pairs), block_bytes=hkv * bs * d * 2)
+    torch.cuda.synchronize()
+    for gk, gv, ok, ov in zip(gks, gvs, oks, ovs):
+        assert np.array_equal(W.torch_to_bits(gk, "bf16"), ok)
+        assert np.array_equal(W.torch_to_bits(gv, "bf16"), ov)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_swap_blocks_out_to_pinned_host_and_back(dtype):
+    """Swap-out from the device pool into a pinned host pool, then swap-in into
+    other device blocks; both steps match the oracle byte for byte."""
+    rng = np.random.default_rng(7)
+    nb, nh, hkv, bs, d = 64, 24, 8, 16, 128
+    dev_bits, _ = _pools(nb, hkv, bs, d, dtype, rng)
+    host_bits, _ = _pools(nh, hkv, bs, d, dtype, rng)
+    ids = rng.permutation(nb)
+    out_pairs = np.stack([ids[:20], rng.permutation(nh)[:20]], axis=1).astype(np.int64)
+    want_host = oracle.swap_blocks(host_bits, dev_bits, out_pairs)
+    g = up(dev_bits, dtype)
+    h = W.bits_to_torch(host_bits, dtype).pin_memory()
+    pa = lib()
+    pa.pa_swap_blocks(h, g, up_int(out_pairs))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(h, dtype), want_host)
+    in_pairs = np.stack([out_pairs[:, 1], ids[20:40]], axis=1).astype(np.int64)
+    want_dev = oracle.swap_blocks(dev_bits, want_host, in_pairs)
+    pa.pa_swap_blocks(g, h, up_int(in_pairs))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(g, dtype), want_dev)
+
+
+def test_swap_blocks_device_to_device():
+    rng = np.random.default_rng(8)
+    a_bits, _ = _pools(30, 4, 32, 64, "f16", rng)
+    b_bits, _ = _pools(20, 4, 32, 64, "f16", rng)
+    pairs = np.stack([rng.permutation(30)[:11], rng.permutation(20)[:11]], axis=1).astype(np.int64)
+    want = oracle.swap_blocks(b_bits, a_bits, pairs)
+    ga, gb = up(a_bits, "f16"), up(b_bits, "f16")
+    lib().pa_swap_blocks(gb, ga, up_int(pairs))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(gb, "f16"), want)
+    assert np.array_equal(W.torch_to_bits(ga, "f16"), a_bits)
+
+
+def test_swap_blocks_rejects_pageable_host_memory():
+    """A pageable host pool is refused before any launch."""
+    pa = lib()
+    g = up(np.zeros((4, 1, 16, 64), np.uint16), "bf16")
+    pageable = torch.zeros((4, 1, 16, 64), dtype=torch.bfloat16)
+    with pytest.raises(pa.PagedAttentionError):
+        pa.pa_swap_blocks(pageable, g, up_int(np.array([[0, 1]], np.int64)))

@@ -379,6 +379,93 @@ def test_copy_on_write_is_transparent():
     assert not np.isnan(a).any()
 
 
+def _random_pools(rng, nb, hkv, bs, d):
+    kp = rng.integers(0, 2 ** 16, size=(nb, hkv, bs, d), dtype=np.uint64).astype(np.uint16)
+    vp = rng.integers(0, 2 ** 16, size=(nb, hkv, bs, d), dtype=np.uint64).astype(np.uint16)
+    return kp, vp
+
+
+def test_copy_block_rows_brute_force():
+    """Element by element: row r of head h of block b changes only when b is a
+    destination and r < the clamped count, and then takes the source's row."""
+    rng = np.random.default_rng(11)
+    nb, hkv, bs, d = 10, 2, 4, 3
+    kp, vp = _random_pools(rng, nb, hkv, bs, d)
+    triples = np.array([[0, 5, 2], [1, 6, 0], [2, 7, 4], [3, 8, 9], [4, 9, -3]], dtype=np.int64)
+    k2, v2 = oracle.copy_block_rows(kp, vp, triples)
+    dst_of = {int(t[1]): (int(t[0]), int(t[2])) for t in triples}
+    for b in range(nb):
+        for h in range(hkv):
+            for r in range(bs):
+                for e in range(d):
+                    want_k, want_v = kp[b, h, r, e], vp[b, h, r, e]
+                    if b in dst_of:
+                        src, n = dst_of[b]
+                        if r < max(0, min(n, bs)):
+                            want_k, want_v = kp[src, h, r, e], vp[src, h, r, e]
+                    assert k2[b, h, r, e] == want_k and v2[b, h, r, e] == want_v
+
+
+def test_copy_block_rows_whole_block_equals_copy_blocks():
+    rng = np.random.default_rng(12)
+    kp, vp = _random_pools(rng, 6, 3, 8, 4)
+    pairs = np.array([[0, 3], [1, 4], [2, 5]], dtype=np.int64)
+    full_k, full_v = oracle.copy_blocks(kp, vp, pairs)
+    for n in (8, 50):   # the block size and beyond it (clamped)
+        triples = np.concatenate([pairs, np.full((3, 1), n, dtype=np.int64)], axis=1)
+        k2, v2 = oracle.copy_block_rows(kp, vp, triples)
+        assert np.array_equal(k2, full_k) and np.array_equal(v2, full_v)
+    k0, v0 = oracle.copy_block_rows(kp, vp, np.concatenate([pairs, np.zeros((3, 1), np.int64)], axis=1))
+    assert np.array_equal(k0, kp) and np.array_equal(v0, vp)
+
+
+def test_partial_fork_is_transparent():
+    """A sequence forked inside a block reads the same attention through the
+    partial copy of that block as through the shared block."""
+    rng = np.random.default_rng(13)
+    nb, hkv, hq, bs, d, length = 12, 2, 4, 16, 64, 37     # 37 = 2 blocks + 5 rows
+    kp = W.to_bits(rng.standard_normal((nb, hkv, bs, d)).astype(np.float32), "bf16")
+    vp = W.to_bits(rng.standard_normal((nb, hkv, bs, d)).astype(np.float32), "bf16")
+    q = W.to_bits(rng.standard_normal((1, hq, d)).astype(np.float32), "bf16")
+    parent = np.array([[3, 7, 1]], dtype=np.int32)
+    child = np.array([[3, 7, 10]], dtype=np.int32)        # tail block 1 copied into 10
+    k2, v2 = oracle.copy_block_rows(kp, vp, [[1, 10, length % bs]])
+    lens = np.array([length], dtype=np.int32)
+    a = oracle.decode_attention(q, "bf16", kp, vp, "bf16", parent, lens, 0.125, bs, hkv)
+    b = oracle.decode_attention(q, "bf16", k2, v2, "bf16", child, lens, 0.125, bs, hkv)
+    assert np.array_equal(a, b)
+
+
+def test_copy_blocks_layers_brute_force():
+    rng = np.random.default_rng(14)
+    layers = [_random_pools(rng, 5, 2, 4, 2) for _ in range(3)]
+    pairs = np.array([[0, 2], [4, 1]], dtype=np.int64)
+    ks, vs = oracle.copy_blocks_layers([l[0] for l in layers], [l[1] for l in layers], pairs)
+    for (kp, vp), k2, v2 in zip(layers, ks, vs):
+        for b in range(5):
+            src = {2: 0, 1: 4}.get(b, b)
+            assert np.array_equal(k2[b], kp[src]) and np.array_equal(v2[b], vp[src])
+
+
+def test_swap_out_and_back_in_restores_blocks():
+    """Swapping blocks out to a (smaller) host pool and back into freed slots
+    of the device pool gives back the same bytes at the new places."""
+    rng = np.random.default_rng(15)
+    dev, _ = _random_pools(rng, 10, 2, 4, 3)
+    host = np.zeros((4, 2, 4, 3), dtype=np.uint16)
+    out_pairs = np.array([[7, 0], [2, 3], [5, 1]], dtype=np.int64)     # device -> host slot
+    host2 = oracle.swap_blocks(host, dev, out_pairs)
+    for src, dst in out_pairs:
+        assert np.array_equal(host2[dst], dev[src])
+    assert not host2[2].any()                                          # untouched slot
+    in_pairs = np.array([[0, 9], [3, 8], [1, 0]], dtype=np.int64)      # host slot -> new device block
+    dev2 = oracle.swap_blocks(dev, host2, in_pairs)
+    assert np.array_equal(dev2[9], dev[7]) and np.array_equal(dev2[8], dev[2])
+    assert np.array_equal(dev2[0], dev[5])
+    for b in range(1, 8):
+        assert np.array_equal(dev2[b], dev[b])
+
+
 # ------------------------------------------------------------ byte accounting
 
 def test_effective_bytes_match_llama2_7b_figure(golden_dir):
