@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size override (default: the workload's)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="decode workloads: run with this block size (8, 16, 32, 64) instead; a "
+                         "fixed pool keeps its token capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline")
@@ -113,6 +116,14 @@ def run_decode_bench(args, dev):
     import workloads as W
 
     spec = W.DECODE_SPECS[args.config]
+    if args.block_size is not None and args.block_size != spec.block_size:
+        import dataclasses
+        pool = spec.pool
+        if pool[0] == "fixed":
+            pool = ("fixed", max(1, pool[1] * spec.block_size // args.block_size))
+        # the same name keeps the same seeded lengths
+        spec = dataclasses.replace(spec, block_size=args.block_size, pool=pool,
+                                   description=f"{spec.description}; block size {args.block_size}")
     lay = W.make_decode_layout(spec, rep=0)
     max_len = int(lay.seq_lens.max())
     part = spec.partition_size if args.partition is None else args.partition
@@ -191,7 +202,8 @@ def run_decode_bench(args, dev):
                      else "decode_kernel<F32Decode>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": decode_traffic_bytes() if spec.name == "llama2_7b_mha_f16" else None,
+                     "traffic": (decode_traffic_bytes()
+                                 if spec.name == "llama2_7b_mha_f16" and spec.block_size == 16 else None),
                      "traffic_unit": "bytes per launch",
                      "algorithmic_bytes_per_launch": eff,
                      "avg_launch_ms": round(attn_avg, 5)},

@@ -27,7 +27,7 @@
  *   (f16,fp8).  Outputs have the query's type.  For an fp8 cache the stored
  *   code times the per-tensor k_scale / v_scale is the value; the scales are
  *   applied the same way for other cache types (pass 1.0f).
- * Shapes.  head_dim is 64 or 128; block_size is 16 or 32; num_q_heads is a
+ * Shapes.  head_dim is 64 or 128; block_size is 8, 16, 32 or 64; num_q_heads is a
  *   multiple of num_kv_heads with at most 16 query heads per KV head.  Query
  *   head h uses KV head h / (num_q_heads / num_kv_heads).
  * Memory.  Every pointer is device memory owned by the caller, dense, and

@@ -183,17 +183,19 @@ struct MfmaDecode {
     uint32_t v[2][4][VW];
   };
 
-  // Block ids of the two 16-token tiles of step j, read with scalar loads
-  // (constant address space: they are counted apart from the vector loads in
-  // flight).  A tile that starts past the end takes the last block (its
-  // tokens are masked).
+  // Block ids of step j, read with scalar loads (constant address space:
+  // they are counted apart from the vector loads in flight): b[tau] holds
+  // the block of 16-token tile tau, or, for 8-token blocks, b[2 tau + half]
+  // that of each half tile.  A block past the end is replaced by the last one
+  // (its tokens are masked).
+  static constexpr int NID = BS < 16 ? 4 : 2;
   struct Ids {
-    int b0, b1;
+    int b[NID];
   };
   static __device__ __forceinline__ Ids ids(ctab_ptr row, int nblk, int j) {
     Ids r;
-    r.b0 = row[min((j * kStep) / BS, nblk - 1)];
-    r.b1 = BS == 32 ? r.b0 : row[min((j * kStep + 16) / BS, nblk - 1)];
+#pragma unroll
+    for (int q = 0; q < NID; ++q) r.b[q] = row[min((j * kStep + (kStep / NID) * q) / BS, nblk - 1)];
     return r;
   }
 
@@ -206,11 +208,21 @@ struct MfmaDecode {
     const char* vpool = reinterpret_cast<const char*>(p.v_pool);
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int rel = j * kStep + 16 * tau;
-      const int row0 = rel % BS;
-      const int blk = tau == 0 ? id.b0 : id.b1;
-      const int64_t tile = (((int64_t)blk * p.num_kv_heads + kvh) * BS + row0) * D;  // elements
-      const char* kt = kpool + (tile + (int64_t)c16 * D) * EB;
+      // element offsets of this lane's K row and of its first V row
+      int64_t krow, vrow;
+      if constexpr (BS < 16) {
+        // 8-token blocks: rows 0-7 and 8-15 of the tile lie in two blocks
+        const int kb = c16 < 8 ? id.b[2 * tau] : id.b[2 * tau + 1];
+        const int vb = G < 2 ? id.b[2 * tau] : id.b[2 * tau + 1];
+        krow = (((int64_t)kb * p.num_kv_heads + kvh) * BS + (c16 & 7)) * D;
+        vrow = (((int64_t)vb * p.num_kv_heads + kvh) * BS + 4 * (G & 1)) * D;
+      } else {
+        const int row0 = (j * kStep + 16 * tau) % BS;
+        const int64_t tile = (((int64_t)id.b[tau] * p.num_kv_heads + kvh) * BS + row0) * D;  // elements
+        krow = tile + (int64_t)c16 * D;
+        vrow = tile + (int64_t)(4 * G) * D;
+      }
+      const char* kt = kpool + krow * EB;
       if constexpr (FP8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16_nt(kt + 64 * h + 16 * G);
@@ -218,7 +230,7 @@ struct MfmaDecode {
 #pragma unroll
         for (int c = 0; c < KL; ++c) buf.k[tau][c] = ld16_nt(kt + (32 * c + 8 * G) * 2);
       }
-      const char* vt = vpool + (tile + (int64_t)(4 * G) * D + DPL * c16) * EB;
+      const char* vt = vpool + (vrow + DPL * c16) * EB;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const char* src = vt + (int64_t)i * D * EB;
@@ -741,8 +753,22 @@ hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
 
 template <typename QT, bool FP8, int D>
 hipError_t launch_mfma_bs(const DecodeParams& p, hipStream_t s) {
-  if (p.block_size == 16) return launch_persistent<MfmaDecode<QT, FP8, D, 16>, QT>(p, s);
-  return launch_persistent<MfmaDecode<QT, FP8, D, 32>, QT>(p, s);
+  switch (p.block_size) {
+    case 8: return launch_persistent<MfmaDecode<QT, FP8, D, 8>, QT>(p, s);
+    case 16: return launch_persistent<MfmaDecode<QT, FP8, D, 16>, QT>(p, s);
+    case 32: return launch_persistent<MfmaDecode<QT, FP8, D, 32>, QT>(p, s);
+    default: return launch_persistent<MfmaDecode<QT, FP8, D, 64>, QT>(p, s);
+  }
+}
+
+template <int D>
+hipError_t launch_f32_bs(const DecodeParams& p, hipStream_t s) {
+  switch (p.block_size) {
+    case 8: return launch_persistent<F32Decode<D, 8>, float>(p, s);
+    case 16: return launch_persistent<F32Decode<D, 16>, float>(p, s);
+    case 32: return launch_persistent<F32Decode<D, 32>, float>(p, s);
+    default: return launch_persistent<F32Decode<D, 64>, float>(p, s);
+  }
 }
 
 template <typename QT, bool FP8>
@@ -755,14 +781,7 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
-  if (p.cache_dtype == kF32) {
-    if (p.head_dim == 128) {
-      if (p.block_size == 16) return launch_persistent<F32Decode<128, 16>, float>(p, stream);
-      return launch_persistent<F32Decode<128, 32>, float>(p, stream);
-    }
-    if (p.block_size == 16) return launch_persistent<F32Decode<64, 16>, float>(p, stream);
-    return launch_persistent<F32Decode<64, 32>, float>(p, stream);
-  }
+  if (p.cache_dtype == kF32) return p.head_dim == 128 ? launch_f32_bs<128>(p, stream) : launch_f32_bs<64>(p, stream);
   const bool fp8 = p.cache_dtype == kFP8;
   if (p.q_dtype == kBF16) return fp8 ? launch_mfma<__bf16, true>(p, stream) : launch_mfma<__bf16, false>(p, stream);
   return fp8 ? launch_mfma<_Float16, true>(p, stream) : launch_mfma<_Float16, false>(p, stream);

@@ -59,8 +59,8 @@ pa_status check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim,
   if (num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "too many KV heads");
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
-  if (block_size != 16 && block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64)", block_size);
   if (elem_bytes(q_dtype) == 0 || elem_bytes(cache_dtype) == 0)
     return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
   const bool same = q_dtype == cache_dtype && q_dtype != PA_DTYPE_FP8_E4M3;
@@ -233,8 +233,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool,
     return fail(PA_ERR_INVALID_ARG, "negative size or non-positive heads/block_size");
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
-  if (block_size != 16 && block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", block_size);
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64)", block_size);
   const int seb = elem_bytes(src_dtype), ceb = elem_bytes(cache_dtype);
   if (seb == 0 || ceb == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
   const bool same = src_dtype == cache_dtype;
@@ -385,7 +385,8 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t
                                  int32_t max_seq_len, int32_t partition_size) {
   (void)num_seqs;
   (void)num_kv_heads;
-  if (max_seq_len <= 0 || (block_size != 16 && block_size != 32)) return -1;
+  if (max_seq_len <= 0 || (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64))
+    return -1;
   if (!valid_request(partition_size, block_size)) return -1;
   if (partition_size == -1) return (max_seq_len + kUnit - 1) / kUnit * kUnit;
   return partition_size;

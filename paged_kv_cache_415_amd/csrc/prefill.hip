@@ -144,28 +144,38 @@ struct TileSrc {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = 16 * wave + RPI * i + lane / CPR;     // row in the tile
-      const int brow = (16 * wave) % BS + RPI * i + lane / CPR;   // row in the block
+      // row in its block (8-token blocks: the wave's rows lie in two blocks)
+      const int brow = BS < 16 ? (RPI * i + lane / CPR) % BS : (16 * wave) % BS + RPI * i + lane / CPR;
       koff[i] = (uint32_t)(brow * D * 2 + 16 * ((lane % CPR) ^ k_swz<D>(row)));
       voff[i] = (uint32_t)(brow * D * 2 + 16 * ((lane % CPR) ^ v_swz<D>(row)));
     }
   }
 
-  // Block id of this wave's rows in tile kt (a scalar load).
-  __device__ __forceinline__ int block_of(int kt) const {
+  // Block ids of this wave's rows in tile kt (scalar loads): rows 0-7 of the
+  // wave's 16 in block a, rows 8-15 in block b (the same block unless the
+  // block size is 8).
+  struct Blk {
+    int a, b;
+  };
+  __device__ __forceinline__ Blk block_of(int kt) const {
     const int key0 = min(kt * kKeyTile + 16 * wave, kend - 1);
-    return ((ctab_ptr)trow)[key0 / BS];
+    Blk r;
+    r.a = ((ctab_ptr)trow)[key0 / BS];
+    r.b = BS < 16 ? ((ctab_ptr)trow)[min(key0 + 8, kend - 1) / BS] : r.a;
+    return r;
   }
 
   // Copy this wave's rows of tile kt into a stage (K tile, then V tile);
   // `blk` = block_of(kt).  Keys past the context re-read the last key
   // (finite data; their logits are masked).  Completion is counted by vmcnt.
-  __device__ __forceinline__ void copy(int kt, int blk, char* dst) const {
+  __device__ __forceinline__ void copy(int kt, Blk blk, char* dst) const {
     char* kd = dst + 16 * wave * D * 2;
     if (kt * kKeyTile + 16 * wave + 15 < kend) {
-      const char* kb = kpool + blk * blk_bytes + head_off;
-      const char* vb = vpool + blk * blk_bytes + head_off;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
+        const int bi = (BS < 16 && RPI * i >= 8) ? blk.b : blk.a;   // one block per instruction
+        const char* kb = kpool + bi * blk_bytes + head_off;
+        const char* vb = vpool + bi * blk_bytes + head_off;
         dma16(kb + koff[i], kd + i * 1024);
         dma16(vb + voff[i], kd + TILE + i * 1024);
       }
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   TileSrc<D, BS> src;
   src.init(kpool, vpool, trow, p.num_kv_heads, kvh, kend, wave, lane);
   src.copy(0, src.block_of(0), smem_raw);
-  int blk_next = src.block_of(1);
+  auto blk_next = src.block_of(1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -487,19 +497,19 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const size_t smem = prefill_smem_bytes(p.head_dim);
 #define PA_PREFILL(T, D, BS) \
   hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS>), grid, dim3(kPThreads), smem, stream, p)
-  if (p.q_dtype == kBF16) {
-    if (p.head_dim == 128) {
-      if (p.block_size == 16) PA_PREFILL(__bf16, 128, 16); else PA_PREFILL(__bf16, 128, 32);
-    } else {
-      if (p.block_size == 16) PA_PREFILL(__bf16, 64, 16); else PA_PREFILL(__bf16, 64, 32);
-    }
-  } else {
-    if (p.head_dim == 128) {
-      if (p.block_size == 16) PA_PREFILL(_Float16, 128, 16); else PA_PREFILL(_Float16, 128, 32);
-    } else {
-      if (p.block_size == 16) PA_PREFILL(_Float16, 64, 16); else PA_PREFILL(_Float16, 64, 32);
-    }
+#define PA_PREFILL_BS(T, D)                      \
+  switch (p.block_size) {                        \
+    case 8: PA_PREFILL(T, D, 8); break;          \
+    case 16: PA_PREFILL(T, D, 16); break;        \
+    case 32: PA_PREFILL(T, D, 32); break;        \
+    default: PA_PREFILL(T, D, 64); break;        \
   }
+  if (p.q_dtype == kBF16) {
+    if (p.head_dim == 128) { PA_PREFILL_BS(__bf16, 128) } else { PA_PREFILL_BS(__bf16, 64) }
+  } else {
+    if (p.head_dim == 128) { PA_PREFILL_BS(_Float16, 128) } else { PA_PREFILL_BS(_Float16, 64) }
+  }
+#undef PA_PREFILL_BS
 #undef PA_PREFILL
   return hipGetLastError();
 }

@@ -65,7 +65,8 @@ def _decode(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), UNSUPPORTED),
     (dict(bs=24), UNSUPPORTED),
-    (dict(bs=8), UNSUPPORTED),
+    (dict(bs=128), UNSUPPORTED),
+    (dict(bs=4), UNSUPPORTED),
     (dict(hq=6, hkv=4), INVALID),
     (dict(hq=64, hkv=2), UNSUPPORTED),            # 32 query heads per KV head
     (dict(qdt=F32, cdt=BF16), UNSUPPORTED),

@@ -160,6 +160,14 @@ SWEEP = [
     ("bf16", "fp8_e4m3", 64, 8, 128, 32),
     ("f32", "f32", 4, 1, 128, 32),
     ("f32", "f32", 5, 5, 64, 16),
+    # 8- and 64-token blocks
+    ("bf16", "bf16", 8, 2, 128, 8),
+    ("f16", "f16", 4, 4, 64, 64),
+    ("bf16", "fp8_e4m3", 16, 2, 128, 8),
+    ("bf16", "fp8_e4m3", 8, 8, 64, 64),
+    ("f16", "f16", 32, 32, 128, 64),
+    ("f32", "f32", 4, 2, 64, 8),
+    ("f32", "f32", 2, 1, 128, 64),
 ]
 LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 600, 1031]
 

@@ -45,6 +45,11 @@ CASES = [
     ([130], [131], 16, 1, 128, 16, "f16"),
     ([17, 50], [60, 99], 2, 2, 64, 16, "f16"),
     ([40], [555], 8, 1, 64, 32, "bf16"),
+    # 8- and 64-token blocks
+    ([20, 9], [85, 9], 8, 2, 128, 8, "bf16"),
+    ([70], [300], 4, 4, 64, 64, "f16"),
+    ([33], [77], 16, 1, 128, 64, "bf16"),
+    ([100], [130], 4, 1, 64, 8, "bf16"),
 ]
 
 
