@@ -115,8 +115,8 @@ __device__ __forceinline__ void dma16(const void* src, char* dst) {
 }
 
 // Where a wave's share of a K/V tile comes from.  Wave w copies key rows
-// [16 w, 16 w + 16) of every tile, which lie in one cache block (the block
-// size is 16 or 32), RPI rows (1 KB) per LDS-DMA instruction.  Lane l lands
+// [16 w, 16 w + 16) of every tile, which lie in one cache block (two for
+// 8-token blocks), RPI rows (1 KB) per LDS-DMA instruction.  Lane l lands
 // at byte 16 l of the instruction's 1 KB, i.e. row l / CPR, chunk slot
 // l % CPR, and so fetches the chunk that the swizzle puts there; its byte
 // offset inside the block does not change from tile to tile.
