@@ -247,9 +247,18 @@ def run_mixed_bench(args, dev):
     max_len = int(case.decode_lens.max())
     ws = pa.decode_workspace(qd, kp, max_len)
 
-    def step(ev=None):
+    def step(ev=None, side=None):
         pa.pa_copy_blocks(kp, vp, pairs)
         pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
+        if side is not None:
+            # prefill chunks and decodes on two streams (joined at the end)
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+                pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
+            torch.cuda.current_stream().wait_stream(side)
+            return
         if ev is not None:
             ev[0].record()
         pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
@@ -269,6 +278,20 @@ def run_mixed_bench(args, dev):
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the same step captured as one HIP graph with the prefill and the decode
+    # on forked streams (timed after the eager measurement above)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(side=side)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step = elapsed * 1e3 / args.steps
@@ -297,6 +320,7 @@ def run_mixed_bench(args, dev):
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                             "algorithmic_bytes_per_launch": eff, "avg_launch_ms": round(dec_ms, 5)},
         "prefill_tokens_per_s": round(int(case.query_start_loc[-1]) / (pre_ms * 1e-3), 1),
+        "hipgraph_two_stream_ms_per_step": round(graph_ms, 5),
         "decode_tokens_per_s_per_layer": round(len(case.decode_lens) / (ms_step * 1e-3), 1),
     }
 

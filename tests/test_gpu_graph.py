@@ -70,3 +70,61 @@ def test_prefill_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(graphed.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
+def test_mixed_step_graph_with_two_streams_matches_eager():
+    """The whole mixed step captured as one graph: copy-on-write and scatter,
+    then the prefill chunks on the capturing stream and the decodes (attention
+    and reduce) on a forked stream, joined at the end.  Every replay matches
+    the eager, single-stream step bit for bit."""
+    pa = lib()
+    case = W.make_mixed_case(num_forks=4, prefix_len=256, chunk_len=120, num_decode=6,
+                             decode_lens=[40, 300, 900, 17, 2000, 64])
+    s = case.spec
+    dt = s.dtype
+    base_k, base_v = up(case.k_pool, dt), up(case.v_pool, dt)
+    pairs, slots = up_int(case.cow_pairs), up_int(case.slot_mapping)
+    nk, nv = up(case.new_k, dt), up(case.new_v, dt)
+    qc, qd = up(case.q_chunk, dt), up(case.q_decode, dt)
+    qsl, ptab, plen = up_int(case.query_start_loc), up_int(case.prefill_tables), up_int(case.prefill_lens)
+    dtab, dlen = up_int(case.decode_tables), up_int(case.decode_lens)
+    max_q = int(np.diff(case.query_start_loc).max())
+    max_len = int(case.decode_lens.max())
+    ws = pa.decode_workspace(qd, base_k, max_len)
+
+    def step(kp, vp, out_c, out_d, side=None):
+        pa.pa_copy_blocks(kp, vp, pairs)
+        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
+        if side is not None:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+                pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
+            torch.cuda.current_stream().wait_stream(side)
+        else:
+            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
+            pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+            pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+
+    ek, ev = base_k.clone(), base_v.clone()
+    e_c, e_d = torch.empty_like(qc), torch.empty_like(qd)
+    step(ek, ev, e_c, e_d)
+    torch.cuda.synchronize()
+    gk, gv = base_k.clone(), base_v.clone()
+    g_c, g_d = torch.empty_like(qc), torch.empty_like(qd)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(gk, gv, g_c, g_d, side)
+    bits = torch.int16
+    for rep in range(3):
+        gk.copy_(base_k)                      # eager work between replays
+        gv.copy_(base_v)
+        g_c.zero_()
+        g_d.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_c.view(bits), e_c.view(bits)), f"prefill, replay {rep}"
+        assert torch.equal(g_d.view(bits), e_d.view(bits)), f"decode, replay {rep}"
+        assert torch.equal(gk.view(bits), ek.view(bits)) and torch.equal(gv.view(bits), ev.view(bits))
