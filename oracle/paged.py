@@ -97,7 +97,7 @@ def softmax_attention(q_rows: np.ndarray, keys: np.ndarray, values: np.ndarray,
 def decode_attention(q_bits, q_dtype: str, k_pool, v_pool, cache_dtype: str,
                      block_tables, seq_lens, scale: float, block_size: int,
                      num_kv_heads: int, k_scale: float = 1.0,
-                     v_scale: float = 1.0) -> np.ndarray:
+                     v_scale: float = 1.0, v_cache_dtype: str | None = None) -> np.ndarray:
     """Paged decode attention: one query token per sequence.
 
     bogosort page §8 (the attention kernel finds each sequence's past K/V
@@ -109,7 +109,9 @@ def decode_attention(q_bits, q_dtype: str, k_pool, v_pool, cache_dtype: str,
     h // (Hq / Hkv).  Stored fp8 codes are multiplied by the per-tensor
     k_scale / v_scale; for other element types the scales are applied the
     same way (1.0 leaves them unchanged).  A sequence of length <= 0 yields a
-    zero output.
+    zero output.  v_cache_dtype names the V pool's element type when it
+    differs from the K pool's (the intelliparadigm page §6.1 pairs an fp8 K
+    cache with a bf16 V cache); by default both pools hold cache_dtype.
 
     q_bits [S][Hq][D]; pools [NB][Hkv][bs][D]; block_tables [S][MB];
     seq_lens [S].  Returns float64 [S][Hq][D].
@@ -125,7 +127,8 @@ def decode_attention(q_bits, q_dtype: str, k_pool, v_pool, cache_dtype: str,
         if n <= 0:
             continue
         keys = gather_sequence(k_pool, cache_dtype, block_tables[s], n, block_size) * float(k_scale)
-        vals = gather_sequence(v_pool, cache_dtype, block_tables[s], n, block_size) * float(v_scale)
+        vals = gather_sequence(v_pool, v_cache_dtype or cache_dtype, block_tables[s], n,
+                               block_size) * float(v_scale)
         for h in range(num_q_heads):
             kv = h // group
             out[s, h] = softmax_attention(q[s, h][None, :], keys[kv], vals[kv], scale)[0]
@@ -193,7 +196,8 @@ def prefill_chunk_attention(q_bits, q_dtype: str, query_start_loc, k_pool, v_poo
 
 def reshape_and_cache(k_pool, v_pool, cache_dtype: str, key_bits, value_bits,
                       src_dtype: str, slot_mapping, block_size: int,
-                      k_scale: float = 1.0, v_scale: float = 1.0):
+                      k_scale: float = 1.0, v_scale: float = 1.0,
+                      v_cache_dtype: str | None = None):
     """Write new tokens' K/V into their pool slots; returns new (k_pool, v_pool).
 
     datawhalechina page, Step 3 item 3 and Step 4: physical block indices are
@@ -204,27 +208,30 @@ def reshape_and_cache(k_pool, v_pool, cache_dtype: str, key_bits, value_bits,
     cache holds the same element type as the source, the bits are copied
     unchanged.  An fp8 cache stores e4m3(float32(x) / float32(scale)) — the
     division done once in float32, as the ybb.press page's §6.2 (FP8 KV cache)
-    leaves the arithmetic open.  Slots are assumed distinct.
+    leaves the arithmetic open.  Slots are assumed distinct.  v_cache_dtype
+    names the V pool's element type when it differs from the K pool's
+    (intelliparadigm page §6.1: fp8 K cache, bf16 V cache).
 
     key_bits/value_bits [T][Hkv][D]; slot_mapping [T] int64.
     """
     k_new = np.array(k_pool, copy=True)
     v_new = np.array(v_pool, copy=True)
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    for src, dst, scale in ((key_bits, k_new, k_scale), (value_bits, v_new, v_scale)):
+    for src, dst, scale, pool_dtype in ((key_bits, k_new, k_scale, cache_dtype),
+                                        (value_bits, v_new, v_scale, v_cache_dtype or cache_dtype)):
         src = np.asarray(src)
         for t, slot in enumerate(slots):
             if slot < 0:
                 continue
             blk, row = int(slot // block_size), int(slot % block_size)
-            if cache_dtype == src_dtype:
+            if pool_dtype == src_dtype:
                 dst[blk, :, row, :] = src[t]
-            elif cache_dtype == "fp8_e4m3":
+            elif pool_dtype == "fp8_e4m3":
                 x32 = decode_elements(src[t], src_dtype).astype(np.float32)
                 q32 = x32 / np.float32(scale)
                 dst[blk, :, row, :] = e4m3_encode(q32)
             else:
-                raise ValueError(f"unsupported conversion {src_dtype} -> {cache_dtype}")
+                raise ValueError(f"unsupported conversion {src_dtype} -> {pool_dtype}")
     return k_new, v_new
 
 

@@ -246,6 +246,75 @@ def test_decode_scales_multiply_stored_values():
     np.testing.assert_allclose(got[0], ref, rtol=0, atol=1e-12)
 
 
+
+# ------------------------------------------------------------ fp8 K beside a bf16 V pool
+
+def _mixed_pools(rng, lens, hkv, d, bs):
+    """An fp8 K pool and a bf16 V pool with the given lengths, plus float32
+    pools holding exactly the same values (both formats are exact in float32)."""
+    need = [-(-n // bs) for n in lens]
+    nb = sum(need) + 2
+    ids = rng.permutation(nb)
+    k8 = rng.integers(0, 256, (nb, hkv, bs, d)).astype(np.uint8)
+    k8[(k8 & 0x7F) == 0x7F] = 0x3C             # no NaN codes
+    vb = W.to_bits(rng.standard_normal((nb, hkv, bs, d)).astype(np.float32), "bf16")
+    kf = oracle.decode_elements(k8, "fp8_e4m3").astype(np.float32)
+    vf = oracle.decode_elements(vb, "bf16").astype(np.float32)
+    tables = np.full((len(lens), max(need)), nb - 1, np.int32)
+    cur = 0
+    for s, n in enumerate(lens):
+        tables[s, :need[s]] = ids[cur:cur + need[s]]
+        cur += need[s]
+    return k8, vb, _f32_bits(kf), _f32_bits(vf), tables
+
+
+def test_mixed_pools_equal_float32_pools_of_the_same_values():
+    # intelliparadigm page §6.1: fp8 K cache, bf16 V cache.  Reading each pool
+    # in its own format must give the attention over the decoded values, which
+    # float32 pools hold exactly; decoding V as fp8 (or K as bf16) would not.
+    rng = np.random.default_rng(21)
+    lens = [1, 17, 40]
+    k8, vb, kf, vf, tables = _mixed_pools(rng, lens, 2, 16, 8)
+    q = W.to_bits(rng.standard_normal((3, 4, 16)).astype(np.float32), "bf16")
+    got = oracle.decode_attention(q, "bf16", k8, vb, "fp8_e4m3", tables, lens, 0.3, 8, 2,
+                                  k_scale=0.05, v_scale=1.5, v_cache_dtype="bf16")
+    ref = oracle.decode_attention(q, "bf16", kf, vf, "f32", tables, lens, 0.3, 8, 2,
+                                  k_scale=0.05, v_scale=1.5)
+    assert np.array_equal(got, ref)
+
+
+def test_mixed_length_one_returns_its_scaled_bf16_value():
+    rng = np.random.default_rng(22)
+    k8, vb, _, _, tables = _mixed_pools(rng, [1], 1, 8, 16)
+    q = W.to_bits(rng.standard_normal((1, 2, 8)).astype(np.float32), "bf16")
+    out = oracle.decode_attention(q, "bf16", k8, vb, "fp8_e4m3", tables, [1], 0.5, 16, 1,
+                                  k_scale=3.0, v_scale=0.5, v_cache_dtype="bf16")
+    blk = tables[0, 0]
+    v = oracle.decode_elements(vb[blk, 0, 0], "bf16") * 0.5
+    for h in range(2):
+        assert np.array_equal(out[0, h], v)
+
+
+def test_mixed_scatter_is_fp8_k_and_copied_v():
+    rng = np.random.default_rng(23)
+    key = W.to_bits(rng.standard_normal((5, 2, 16)).astype(np.float32) * 30, "bf16")
+    val = W.to_bits(rng.standard_normal((5, 2, 16)).astype(np.float32), "bf16")
+    slots = np.array([3, -1, 0, 9, 6], np.int64)
+    k0 = np.zeros((3, 2, 4, 16), np.uint8)
+    v0 = np.zeros((3, 2, 4, 16), np.uint16)
+    km, vm = oracle.reshape_and_cache(k0, v0, "fp8_e4m3", key, val, "bf16", slots, 4,
+                                      k_scale=0.25, v_scale=7.0, v_cache_dtype="bf16")
+    k8, _ = oracle.reshape_and_cache(k0, k0, "fp8_e4m3", key, val, "bf16", slots, 4,
+                                     k_scale=0.25, v_scale=7.0)
+    _, v16 = oracle.reshape_and_cache(v0, v0, "bf16", key, val, "bf16", slots, 4)
+    assert np.array_equal(km, k8) and np.array_equal(vm, v16)
+    # the copied V rows are the source bits (slot = block * 4 + row); rows no
+    # slot names, like the skipped token's, keep their old contents
+    assert np.array_equal(vm[0, :, 3], val[0]) and np.array_equal(vm[2, :, 1], val[3])
+    assert np.array_equal(vm[1, :, 2], val[4]) and np.array_equal(vm[0, :, 0], val[2])
+    assert not vm[1, :, 0].any() and not vm[2, :, 0].any()
+
+
 # ------------------------------------------------------------ prefill chunk
 
 def _bottom_right_mask(rows, n):
