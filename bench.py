@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama2_7b_mha_f16",
-                    help="llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | tiny_f32 "
+                    help="llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
+                         "| tiny_f32 "
                          "| mixed_prefix_bf16")
     ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
     ap.add_argument("--partition", type=int, default=None,
@@ -97,7 +98,7 @@ class DecodeBatch:
         gen.manual_seed(seed)
         shape = (lay.num_blocks, s.num_kv_heads, s.block_size, s.head_dim)
         self.k_pool, self.k_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.cache_dtype)
-        self.v_pool, self.v_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.cache_dtype)
+        self.v_pool, self.v_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.v_dtype)
         S = len(lay.seq_lens)
         qdt = W.TORCH_DTYPE[s.q_dtype]
         self.q = _randn((S, s.num_q_heads, s.head_dim), gen, dev, s.value_std).to(qdt)
@@ -134,16 +135,21 @@ def run_decode_bench(args, dev):
                                            max_len, part)
     ws = pa.decode_workspace(b0.q, b0.k_pool, max_len, part)
 
+    mixed = spec.v_dtype != spec.cache_dtype     # fp8 K beside a 16-bit V pool
+    scatter = pa.pa_reshape_and_cache_kv if mixed else pa.pa_reshape_and_cache
+    attention = pa.pa_decode_attention_kv if mixed else pa.pa_decode_attention
+    reduce = pa.pa_decode_reduce_kv if mixed else pa.pa_decode_reduce
+
     def step(b, ev=None):
-        pa.pa_reshape_and_cache(b.new_k, b.new_v, b.k_pool, b.v_pool, b.slots, b.k_scale, b.v_scale)
+        scatter(b.new_k, b.new_v, b.k_pool, b.v_pool, b.slots, b.k_scale, b.v_scale)
         if ev is not None:
             ev[0].record()
-        pa.pa_decode_attention(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
-                               max_len, b.k_scale, b.v_scale, part, ws)
+        attention(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
+                  max_len, b.k_scale, b.v_scale, part, ws)
         if ev is not None:
             ev[1].record()
-        pa.pa_decode_reduce(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
-                            max_len, b.k_scale, b.v_scale, part, ws)
+        reduce(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
+               max_len, b.k_scale, b.v_scale, part, ws)
         if ev is not None:
             ev[2].record()
 
@@ -182,7 +188,8 @@ def run_decode_bench(args, dev):
         print(f"bench.py: hipGraph replay skipped ({exc})", file=sys.stderr)
     assert not torch.isnan(b0.out).any(), "NaN in decode output"
 
-    eff = W.effective_kv_bytes(lay.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
+    eff = W.effective_kv_bytes(lay.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
+                               spec.v_dtype)
     ms_step = elapsed * 1e3 / args.steps
     attn_avg = float(np.mean(attn_ms))
     S = len(lay.seq_lens)
@@ -191,8 +198,9 @@ def run_decode_bench(args, dev):
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
         "ms_per_step": round(ms_step, 5),
-        "dtype": spec.cache_dtype if spec.cache_dtype == spec.q_dtype else
-        f"{spec.q_dtype}+{spec.cache_dtype}",
+        "dtype": spec.cache_dtype if spec.cache_dtype == spec.q_dtype == spec.v_dtype else
+        f"{spec.q_dtype}+{spec.cache_dtype}" if spec.v_dtype == spec.cache_dtype else
+        f"{spec.q_dtype}+K {spec.cache_dtype}+V {spec.v_dtype}",
         "config": {"workload": spec.description, "name": spec.name, "num_seqs": S,
                    "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
                    "head_dim": spec.head_dim, "block_size": spec.block_size,
@@ -476,7 +484,8 @@ def cpu_baseline(args):
     spec = W.DECODE_SPECS[name]
     nseq = 16
     case = W.make_decode_case(spec, rep=0, num_seqs=nseq)
-    eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
+    eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
+                               spec.v_dtype)
     passes, spent = 0, 0.0
     with threadpool_limits(1):
         while spent < args.cpu_seconds or passes == 0:
@@ -484,7 +493,7 @@ def cpu_baseline(args):
             oracle.decode_attention(case.q, spec.q_dtype, case.k_pool, case.v_pool,
                                     spec.cache_dtype, case.block_tables, case.seq_lens,
                                     spec.scale, spec.block_size, spec.num_kv_heads,
-                                    case.k_scale, case.v_scale)
+                                    case.k_scale, case.v_scale, v_cache_dtype=spec.v_dtype)
             spent += time.perf_counter() - t0
             passes += 1
     return {"value": round(eff * passes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,

@@ -100,6 +100,23 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool,
                                float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_reshape_and_cache_kv — pa_reshape_and_cache with separate K and V pool
+ * element types, for the mixed-precision cache of [intelli] §6.1 (an fp8 K
+ * cache beside a bf16 V cache: 3 bytes per K/V element pair instead of 4).
+ * K follows the pa_reshape_and_cache rules with cache_dtype = k_cache_dtype;
+ * v_cache_dtype equals k_cache_dtype (then the call equals
+ * pa_reshape_and_cache), or k_cache_dtype is fp8 and v_cache_dtype equals
+ * src_dtype (V bits copied unchanged; v_scale unused for V).  Any other pair
+ * returns PA_ERR_UNSUPPORTED.
+ */
+pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_pool, void* v_pool,
+                                  const int64_t* slot_mapping, int32_t num_tokens,
+                                  int64_t key_token_stride, int64_t value_token_stride,
+                                  int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, pa_dtype src_dtype, pa_dtype k_cache_dtype,
+                                  pa_dtype v_cache_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_copy_blocks — copy whole blocks for copy-on-write.
  *
  * [ybb] §2.2 Copy-on-Write: when several sequences reference one block, a
@@ -257,6 +274,44 @@ pa_status pa_decode_reduce(void* out, const void* q, const void* k_pool, const v
                            int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
                            float k_scale, float v_scale, int32_t partition_size, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_kv — pa_decode with separate K and V pool element types
+ * ([intelli] §6.1: fp8 K cache, bf16 V cache, bf16 activations).  The
+ * result is the pa_decode formula with K read as k_cache_dtype and V as
+ * v_cache_dtype (fp8 codes decoded exactly, then scaled by k_scale /
+ * v_scale; 16-bit pools use the scales the same way).  Supported: the pairs
+ * of pa_decode with v_cache_dtype == k_cache_dtype, and k_cache_dtype fp8
+ * with v_cache_dtype == q_dtype (bf16 or f16).  Other pairs return
+ * PA_ERR_UNSUPPORTED.  Workspace and partition rules are those of
+ * pa_decode (pa_decode_workspace_bytes does not depend on the pool types).
+ */
+pa_status pa_decode_kv(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                       int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                       int32_t max_seq_len, pa_dtype q_dtype, pa_dtype k_cache_dtype,
+                       pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       void* stream);
+/* The two stages of pa_decode_kv (as pa_decode_attention / pa_decode_reduce
+ * are for pa_decode), taking exactly its arguments. */
+pa_status pa_decode_attention_kv(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                                 int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t max_seq_len, pa_dtype q_dtype, pa_dtype k_cache_dtype,
+                                 pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+pa_status pa_decode_reduce_kv(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, pa_dtype q_dtype, pa_dtype k_cache_dtype,
+                              pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * pa_prefill_chunk — causal attention of one prefill chunk per sequence

@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
     i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32,
                                          i32, f32, f32, vp]
+    lib.pa_reshape_and_cache_kv.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32,
+                                            i32, i32, i32, f32, f32, vp]
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i64, vp]
     lib.pa_copy_blocks_partial.argtypes = [vp, vp, vp, i32, i32, i32, i64, vp]
     lib.pa_copy_blocks_layers.argtypes = [vp, vp, i32, vp, i32, i64, vp]
@@ -64,6 +66,9 @@ def _load() -> ctypes.CDLL:
     for name in ("pa_decode", "pa_decode_attention", "pa_decode_reduce"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = i32
+    for name in ("pa_decode_kv", "pa_decode_attention_kv", "pa_decode_reduce_kv"):
+        getattr(lib, name).argtypes = dec[:16] + [i32] + dec[16:]
+        getattr(lib, name).restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, f32, vp]
     lib.pa_status_string.argtypes = [i32]
@@ -72,7 +77,7 @@ def _load() -> ctypes.CDLL:
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_probe_read.argtypes = [vp, sz, vp, vp]
     lib.pa_probe_copy.argtypes = [vp, vp, sz, vp]
-    for name in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_copy_blocks_partial",
+    for name in ("pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_copy_blocks", "pa_copy_blocks_partial",
                  "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_probe_read",
                  "pa_probe_copy"):
         getattr(lib, name).restype = i32
@@ -123,6 +128,21 @@ def _stream(stream) -> int:
 def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, k_scale: float = 1.0,
                          v_scale: float = 1.0, stream=None) -> None:
     """Scatter key/value [T][Hkv][D] into pool slots (see pa.h)."""
+    _scatter(_lib.pa_reshape_and_cache, key, value, k_pool, v_pool, slot_mapping, k_scale, v_scale,
+             stream, mixed=False)
+
+
+def pa_reshape_and_cache_kv(key, value, k_pool, v_pool, slot_mapping, k_scale: float = 1.0,
+                            v_scale: float = 1.0, stream=None) -> None:
+    """pa_reshape_and_cache with the K and V pool types taken apart (fp8 K
+    cache beside a V cache of the source type; see pa.h)."""
+    _scatter(_lib.pa_reshape_and_cache_kv, key, value, k_pool, v_pool, slot_mapping, k_scale,
+             v_scale, stream, mixed=True)
+
+
+def _scatter(fn, key, value, k_pool, v_pool, slot_mapping, k_scale, v_scale, stream, mixed):
+    if not mixed and _dtype(k_pool) != _dtype(v_pool):
+        raise ValueError("K and V pools of different types need pa_reshape_and_cache_kv")
     if slot_mapping.dtype != torch.int64:
         raise TypeError("slot_mapping must be int64")
     nb, hkv, bs, d = k_pool.shape
@@ -132,10 +152,12 @@ def pa_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, k_scale: floa
             raise ValueError("key/value must be [T][num_kv_heads][head_dim] with dense rows")
     key_stride = key.stride(0) if t > 0 else 0
     value_stride = value.stride(0) if t > 0 else 0
-    _check(_lib.pa_reshape_and_cache(_ptr(key, False), _ptr(value, False), _ptr(k_pool), _ptr(v_pool),
-                                     _ptr(slot_mapping), t, key_stride, value_stride, nb, hkv, d,
-                                     bs, _dtype(key), _dtype(k_pool), k_scale, v_scale,
-                                     _stream(stream)))
+    if v_pool.shape[1:] != k_pool.shape[1:] or v_pool.shape[0] < nb:
+        raise ValueError("V pool shape does not match the K pool")
+    types = [_dtype(k_pool), _dtype(v_pool)] if mixed else [_dtype(k_pool)]
+    _check(fn(_ptr(key, False), _ptr(value, False), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping),
+              t, key_stride, value_stride, nb, hkv, d, bs, _dtype(key), *types, k_scale, v_scale,
+              _stream(stream)))
 
 
 def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
@@ -235,15 +257,20 @@ def decode_workspace(q, k_pool, max_seq_len: int, partition_size: int = 0):
 
 
 def _decode_call(fn, out, q, k_pool, v_pool, block_tables, seq_lens, scale, max_seq_len,
-                 k_scale, v_scale, partition_size, workspace, stream):
+                 k_scale, v_scale, partition_size, workspace, stream, mixed=False):
     s, hq, d = q.shape
     _, hkv, bs, _ = k_pool.shape
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_tables and seq_lens must be int32")
+    if v_pool.shape[1:] != k_pool.shape[1:]:
+        raise ValueError("V pool shape does not match the K pool")
+    if not mixed and _dtype(k_pool) != _dtype(v_pool):
+        raise ValueError("K and V pools of different types need pa_decode_kv")
+    types = [_dtype(k_pool), _dtype(v_pool)] if mixed else [_dtype(k_pool)]
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fn(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens),
               float(scale), bs, s, hq, hkv, d, block_tables.shape[1], int(max_seq_len),
-              _dtype(q), _dtype(k_pool), float(k_scale), float(v_scale), int(partition_size),
+              _dtype(q), *types, float(k_scale), float(v_scale), int(partition_size),
               _ptr(workspace), wbytes, _stream(stream)))
 
 
@@ -253,6 +280,31 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_
     """Decode attention of one query per sequence over its paged context (see pa.h)."""
     _decode_call(_lib.pa_decode, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
                  max_seq_len, k_scale, v_scale, partition_size, workspace, stream)
+
+
+def pa_decode_kv(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int = 0,
+                 k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                 workspace=None, stream=None) -> None:
+    """pa_decode with the K and V pool types taken apart (fp8 K cache beside
+    a V cache of the query type; see pa.h)."""
+    _decode_call(_lib.pa_decode_kv, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                 max_seq_len, k_scale, v_scale, partition_size, workspace, stream, mixed=True)
+
+
+def pa_decode_attention_kv(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                           max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                           partition_size: int = 0, workspace=None, stream=None) -> None:
+    """First stage of pa_decode_kv (attention kernel only)."""
+    _decode_call(_lib.pa_decode_attention_kv, out, q, k_pool, v_pool, block_tables, seq_lens,
+                 scale, max_seq_len, k_scale, v_scale, partition_size, workspace, stream, mixed=True)
+
+
+def pa_decode_reduce_kv(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                        max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                        partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Second stage of pa_decode_kv."""
+    _decode_call(_lib.pa_decode_reduce_kv, out, q, k_pool, v_pool, block_tables, seq_lens,
+                 scale, max_seq_len, k_scale, v_scale, partition_size, workspace, stream, mixed=True)
 
 
 def pa_decode_attention(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
@@ -296,7 +348,8 @@ def pa_probe_copy(dst, src, stream=None) -> None:
 
 
 __all__ = [
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
+    "pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_decode_kv", "pa_decode_attention_kv",
+    "pa_decode_reduce_kv", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
     "layer_pool_pointers",
     "pa_swap_blocks", "pa_decode", "pa_decode_attention",
     "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",

@@ -44,8 +44,10 @@ __device__ __forceinline__ float src_elem(const char* base, int i) {
 }
 
 // Quantising scatter into an fp8 E4M3 pool: each thread turns 16 source
-// elements into 16 codes (one 16-byte store).
-template <typename SrcT>
+// elements into 16 codes (one 16-byte store).  With VQ false only K is
+// quantised and the V elements are copied unchanged (fp8 K cache beside a
+// 16-bit V cache).
+template <typename SrcT, bool VQ>
 __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterParams p) {
   const int t = blockIdx.x;
   const int64_t slot = p.slot_mapping[t];
@@ -61,8 +63,14 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterParams p) {
     const int c = i - h * groups_per_head;
     const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 16;
     const int64_t src = (int64_t)h * p.head_dim + c * 16;
+    if constexpr (!VQ) {
+      const char* vs = reinterpret_cast<const char*>(vsrc + src);
+      char* vd = (char*)p.v_pool + dst * (int64_t)sizeof(SrcT);
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
+      for (int q = 0; q < (int)sizeof(SrcT); ++q) st16(vd + 16 * q, ld16(vs + 16 * q));
+    }
+#pragma unroll
+    for (int which = 0; which < (VQ ? 2 : 1); ++which) {
       const SrcT* s = which ? vsrc : ksrc;
       const float scale = which ? p.v_scale : p.k_scale;
       uint32_t w[4];
@@ -167,14 +175,18 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(SwapParams p) {
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream) {
   if (p.num_tokens == 0) return hipSuccess;
   dim3 grid(p.num_tokens), block(256);
+  const bool vq = p.v_cache_dtype != p.src_dtype;   // V quantised too
   if (p.cache_dtype == p.src_dtype) {
     hipLaunchKernelGGL(scatter_copy_kernel<void>, grid, block, 0, stream, p);
   } else if (p.src_dtype == kBF16) {
-    hipLaunchKernelGGL(scatter_fp8_kernel<__bf16>, grid, block, 0, stream, p);
+    if (vq) hipLaunchKernelGGL((scatter_fp8_kernel<__bf16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((scatter_fp8_kernel<__bf16, false>), grid, block, 0, stream, p);
   } else if (p.src_dtype == kF16) {
-    hipLaunchKernelGGL(scatter_fp8_kernel<_Float16>, grid, block, 0, stream, p);
+    if (vq) hipLaunchKernelGGL((scatter_fp8_kernel<_Float16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((scatter_fp8_kernel<_Float16, false>), grid, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL(scatter_fp8_kernel<float>, grid, block, 0, stream, p);
+    if (vq) hipLaunchKernelGGL((scatter_fp8_kernel<float, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((scatter_fp8_kernel<float, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

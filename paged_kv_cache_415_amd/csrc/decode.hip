@@ -165,18 +165,20 @@ struct TableWindow {
 // ---------------------------------------------------------------------------
 // MFMA segment for 16-bit and fp8 caches.
 //   QT: query / output / MFMA operand type (__bf16 or _Float16)
-//   FP8: cache holds E4M3 codes (decoded exactly to QT)
+//   KF8, VF8: the K / V pool holds E4M3 codes (decoded exactly to QT);
+//   otherwise it holds QT.  K fp8 with V in QT is the mixed format of the
+//   intelligence-ai page §6.1 (fp8 K cache, bf16 V cache).
 // ---------------------------------------------------------------------------
-template <typename QT, bool FP8, int D, int BS>
+template <typename QT, bool KF8, bool VF8, int D, int BS>
 struct MfmaDecode {
   static constexpr int NC = D / 32;             // QK MFMAs per 16-token tile
   static constexpr int DPL = D / 16;            // value dims per lane = PV MFMAs per step
-  static constexpr int EB = FP8 ? 1 : 2;
-  static constexpr int VW = DPL * EB / 4;       // dwords per V row piece
-  static constexpr int KL = FP8 ? D / 64 : NC;  // 16-byte K loads per lane and tile
-  static constexpr bool kDoubleBuffer = FP8;
+  static constexpr int KEB = KF8 ? 1 : 2, VEB = VF8 ? 1 : 2;
+  static constexpr int VW = DPL * VEB / 4;      // dwords per V row piece
+  static constexpr int KL = KF8 ? D / 64 : NC;  // 16-byte K loads per lane and tile
+  static constexpr bool kDoubleBuffer = KF8 && VF8;
   // waves per workgroup = waves one CU keeps resident at this register count
-  static constexpr int kWaves = D == 64 ? 16 : (FP8 ? 8 : 12);
+  static constexpr int kWaves = D == 64 ? 16 : (KF8 && VF8 ? 8 : 12);
 
   struct Buf {
     u32x4 k[2][KL];
@@ -222,18 +224,18 @@ struct MfmaDecode {
         krow = tile + (int64_t)c16 * D;
         vrow = tile + (int64_t)(4 * G) * D;
       }
-      const char* kt = kpool + krow * EB;
-      if constexpr (FP8) {
+      const char* kt = kpool + krow * KEB;
+      if constexpr (KF8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16_nt(kt + 64 * h + 16 * G);
       } else {
 #pragma unroll
         for (int c = 0; c < KL; ++c) buf.k[tau][c] = ld16_nt(kt + (32 * c + 8 * G) * 2);
       }
-      const char* vt = vpool + (vrow + DPL * c16) * EB;
+      const char* vt = vpool + (vrow + DPL * c16) * VEB;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const char* src = vt + (int64_t)i * D * EB;
+        const char* src = vt + (int64_t)i * D * VEB;
         if constexpr (VW == 4) {
           const u32x4 x = ld16_nt(src);
           buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y; buf.v[tau][i][2] = x.z; buf.v[tau][i][3] = x.w;
@@ -274,7 +276,7 @@ struct MfmaDecode {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       u32x4 ka[NC];
-      if constexpr (FP8) {
+      if constexpr (KF8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) {
           const u32x4 raw = buf.k[tau][h];
@@ -334,7 +336,7 @@ struct MfmaDecode {
 #pragma unroll
     for (int n = 0; n < DPL; ++n) {
       u32x4 a;
-      if constexpr (FP8) {
+      if constexpr (VF8) {
         const int w = n >> 2, k = n & 3;
         uint32_t x[2];
 #pragma unroll
@@ -374,7 +376,7 @@ struct MfmaDecode {
                        ((int64_t)s * p.num_q_heads + kvh * g + c16) * D;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int d0 = FP8 ? (64 * (c >> 1) + 16 * G + 8 * (c & 1)) : (32 * c + 8 * G);
+        const int d0 = KF8 ? (64 * (c >> 1) + 16 * G + 8 * (c & 1)) : (32 * c + 8 * G);
         qop[c] = (c16 < g) ? ld16(qrow + d0) : u32x4{0, 0, 0, 0};
       }
     }
@@ -751,13 +753,13 @@ hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename QT, bool FP8, int D>
+template <typename QT, bool KF8, bool VF8, int D>
 hipError_t launch_mfma_bs(const DecodeParams& p, hipStream_t s) {
   switch (p.block_size) {
-    case 8: return launch_persistent<MfmaDecode<QT, FP8, D, 8>, QT>(p, s);
-    case 16: return launch_persistent<MfmaDecode<QT, FP8, D, 16>, QT>(p, s);
-    case 32: return launch_persistent<MfmaDecode<QT, FP8, D, 32>, QT>(p, s);
-    default: return launch_persistent<MfmaDecode<QT, FP8, D, 64>, QT>(p, s);
+    case 8: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 8>, QT>(p, s);
+    case 16: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 16>, QT>(p, s);
+    case 32: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 32>, QT>(p, s);
+    default: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 64>, QT>(p, s);
   }
 }
 
@@ -771,10 +773,18 @@ hipError_t launch_f32_bs(const DecodeParams& p, hipStream_t s) {
   }
 }
 
-template <typename QT, bool FP8>
+template <typename QT, bool KF8, bool VF8>
 hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
-  if (p.head_dim == 128) return launch_mfma_bs<QT, FP8, 128>(p, s);
-  return launch_mfma_bs<QT, FP8, 64>(p, s);
+  if (p.head_dim == 128) return launch_mfma_bs<QT, KF8, VF8, 128>(p, s);
+  return launch_mfma_bs<QT, KF8, VF8, 64>(p, s);
+}
+
+template <typename QT>
+hipError_t launch_mfma_formats(const DecodeParams& p, hipStream_t s) {
+  const bool kf8 = p.cache_dtype == kFP8, vf8 = p.v_cache_dtype == kFP8;
+  if (kf8 && vf8) return launch_mfma<QT, true, true>(p, s);
+  if (kf8) return launch_mfma<QT, true, false>(p, s);
+  return launch_mfma<QT, false, false>(p, s);
 }
 
 }  // namespace
@@ -782,9 +792,8 @@ hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
   if (p.cache_dtype == kF32) return p.head_dim == 128 ? launch_f32_bs<128>(p, stream) : launch_f32_bs<64>(p, stream);
-  const bool fp8 = p.cache_dtype == kFP8;
-  if (p.q_dtype == kBF16) return fp8 ? launch_mfma<__bf16, true>(p, stream) : launch_mfma<__bf16, false>(p, stream);
-  return fp8 ? launch_mfma<_Float16, true>(p, stream) : launch_mfma<_Float16, false>(p, stream);
+  if (p.q_dtype == kBF16) return launch_mfma_formats<__bf16>(p, stream);
+  return launch_mfma_formats<_Float16>(p, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {

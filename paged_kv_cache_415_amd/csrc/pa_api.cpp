@@ -48,7 +48,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Shape / type checks shared by decode and prefill.
 pa_status check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                                int max_blocks, pa_dtype q_dtype, pa_dtype cache_dtype) {
+                                int max_blocks, pa_dtype q_dtype, pa_dtype cache_dtype,
+                                pa_dtype v_cache_dtype) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "head counts and max_blocks_per_seq must be positive");
   if (num_q_heads % num_kv_heads)
@@ -61,12 +62,15 @@ pa_status check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim,
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
   if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64)", block_size);
-  if (elem_bytes(q_dtype) == 0 || elem_bytes(cache_dtype) == 0)
+  if (elem_bytes(q_dtype) == 0 || elem_bytes(cache_dtype) == 0 || elem_bytes(v_cache_dtype) == 0)
     return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
   const bool same = q_dtype == cache_dtype && q_dtype != PA_DTYPE_FP8_E4M3;
   const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3 &&
                    (q_dtype == PA_DTYPE_BF16 || q_dtype == PA_DTYPE_F16);
   if (!same && !fp8) return fail(PA_ERR_UNSUPPORTED, "unsupported (q, cache) dtype pair");
+  // V: the K format, or (beside an fp8 K pool) the query type
+  if (v_cache_dtype != cache_dtype && !(fp8 && v_cache_dtype == q_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "unsupported (K cache, V cache) dtype pair");
   return PA_OK;
 }
 
@@ -148,13 +152,14 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                       float scale, int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
-                      int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
-                      float v_scale, int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                      pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
-                                       max_blocks_per_seq, q_dtype, cache_dtype);
+                                       max_blocks_per_seq, q_dtype, cache_dtype, v_cache_dtype);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_INVALID_ARG, "scale, k_scale and v_scale must be finite");
@@ -207,6 +212,7 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   p.max_parts = plan.max_parts;
   p.q_dtype = q_dtype;
   p.cache_dtype = cache_dtype;
+  p.v_cache_dtype = v_cache_dtype;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stage != Stage::kReduce) {
     hipError_t e = pa::launch_decode_attention(p, s);
@@ -223,12 +229,13 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
 
 extern "C" {
 
-pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
-                               const int64_t* slot_mapping, int32_t num_tokens,
-                               int64_t key_token_stride, int64_t value_token_stride,
-                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
-                               float k_scale, float v_scale, void* stream) {
+pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_pool, void* v_pool,
+                                  const int64_t* slot_mapping, int32_t num_tokens,
+                                  int64_t key_token_stride, int64_t value_token_stride,
+                                  int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, pa_dtype src_dtype, pa_dtype k_cache_dtype,
+                                  pa_dtype v_cache_dtype, float k_scale, float v_scale, void* stream) {
+  const pa_dtype cache_dtype = k_cache_dtype;
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || block_size <= 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or non-positive heads/block_size");
   if (head_dim != 64 && head_dim != 128)
@@ -236,10 +243,14 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool,
   if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64)
     return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64)", block_size);
   const int seb = elem_bytes(src_dtype), ceb = elem_bytes(cache_dtype);
-  if (seb == 0 || ceb == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
+  if (seb == 0 || ceb == 0 || elem_bytes(v_cache_dtype) == 0)
+    return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
   const bool same = src_dtype == cache_dtype;
   const bool quant = cache_dtype == PA_DTYPE_FP8_E4M3 && src_dtype != PA_DTYPE_FP8_E4M3;
   if (!same && !quant) return fail(PA_ERR_UNSUPPORTED, "unsupported (src, cache) dtype pair");
+  // V: the K format, or (beside an fp8 K pool) the source type
+  if (v_cache_dtype != cache_dtype && !(quant && v_cache_dtype == src_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "unsupported (K cache, V cache) dtype pair");
   if (quant && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0 && v_scale > 0))
     return fail(PA_ERR_INVALID_ARG, "fp8 scales must be finite and positive");
   const int64_t dense = (int64_t)num_kv_heads * head_dim;
@@ -269,10 +280,23 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool,
   p.block_size = block_size;
   p.src_dtype = src_dtype;
   p.cache_dtype = cache_dtype;
+  p.v_cache_dtype = v_cache_dtype;
   p.src_elem_bytes = seb;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   return hip_status(pa::launch_scatter(p, static_cast<hipStream_t>(stream)), "scatter launch");
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
+                               float k_scale, float v_scale, void* stream) {
+  return pa_reshape_and_cache_kv(key, value, k_pool, v_pool, slot_mapping, num_tokens,
+                                 key_token_stride, value_token_stride, num_blocks, num_kv_heads,
+                                 head_dim, block_size, src_dtype, cache_dtype, cache_dtype, k_scale,
+                                 v_scale, stream);
 }
 
 pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* block_pairs, int32_t num_pairs,
@@ -411,8 +435,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_
                     size_t workspace_bytes, void* stream) {
   return decode_impl(Stage::kBoth, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
                      block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, k_scale, v_scale,
-                     partition_size, workspace, workspace_bytes, stream);
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -424,8 +448,8 @@ pa_status pa_decode_attention(void* out, const void* q, const void* k_pool, cons
                               void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(Stage::kAttention, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
                      block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, k_scale, v_scale,
-                     partition_size, workspace, workspace_bytes, stream);
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_reduce(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -437,8 +461,50 @@ pa_status pa_decode_reduce(void* out, const void* q, const void* k_pool, const v
                            size_t workspace_bytes, void* stream) {
   return decode_impl(Stage::kReduce, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
                      block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, k_scale, v_scale,
-                     partition_size, workspace, workspace_bytes, stream);
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_kv(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                       int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                       int32_t max_seq_len, pa_dtype q_dtype, pa_dtype k_cache_dtype,
+                       pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return decode_impl(Stage::kBoth, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, k_cache_dtype, v_cache_dtype,
+                     k_scale, v_scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_attention_kv(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                                 int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t max_seq_len, pa_dtype q_dtype, pa_dtype k_cache_dtype,
+                                 pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return decode_impl(Stage::kAttention, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, k_cache_dtype, v_cache_dtype,
+                     k_scale, v_scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_reduce_kv(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_seq_len, pa_dtype q_dtype, pa_dtype k_cache_dtype,
+                              pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                              int32_t partition_size, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return decode_impl(Stage::kReduce, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, k_cache_dtype, v_cache_dtype,
+                     k_scale, v_scale, partition_size, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
@@ -452,7 +518,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
     return fail(PA_ERR_INVALID_ARG, "negative size");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
-                                       max_blocks_per_seq, q_dtype, cache_dtype);
+                                       max_blocks_per_seq, q_dtype, cache_dtype, cache_dtype);
   if (st != PA_OK) return st;
   if (cache_dtype != q_dtype || q_dtype == PA_DTYPE_F32)
     return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16/f16 queries with a cache of the same type");

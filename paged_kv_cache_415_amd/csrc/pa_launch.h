@@ -25,7 +25,8 @@ struct ScatterParams {
   int head_dim;
   int block_size;
   int src_dtype;
-  int cache_dtype;
+  int cache_dtype;     // K pool element type
+  int v_cache_dtype;   // V pool element type
   int src_elem_bytes;
   float k_scale;
   float v_scale;
@@ -105,7 +106,8 @@ struct DecodeParams {
   int chunk;           // units: fixed partition length, or the shortest balanced range
   int max_parts;       // partial slots per (sequence, query head)
   int q_dtype;
-  int cache_dtype;
+  int cache_dtype;     // K pool element type
+  int v_cache_dtype;   // V pool element type (the same, or QT beside an fp8 K pool)
 };
 
 struct PrefillParams {

@@ -49,7 +49,8 @@ class DecodeRun:
         s = case.spec
         self.q = up(case.q, s.q_dtype)
         self.k_pool = up(case.k_pool, s.cache_dtype)
-        self.v_pool = up(case.v_pool, s.cache_dtype)
+        self.v_pool = up(case.v_pool, s.v_dtype)
+        self.mixed = s.v_dtype != s.cache_dtype
         self.new_k = up(case.new_k, case.src_dtype)
         self.new_v = up(case.new_v, case.src_dtype)
         self.tables = up_int(case.block_tables)
@@ -58,8 +59,10 @@ class DecodeRun:
         self.max_len = int(case.seq_lens.max()) if len(case.seq_lens) else 1
 
     def scatter(self):
-        lib().pa_reshape_and_cache(self.new_k, self.new_v, self.k_pool, self.v_pool, self.slots,
-                                   self.case.k_scale, self.case.v_scale)
+        pa = lib()
+        fn = pa.pa_reshape_and_cache_kv if self.mixed else pa.pa_reshape_and_cache
+        fn(self.new_k, self.new_v, self.k_pool, self.v_pool, self.slots, self.case.k_scale,
+           self.case.v_scale)
 
     def decode(self, partition_size=None, stages=False, max_seq_len=None):
         pa = lib()
@@ -70,7 +73,13 @@ class DecodeRun:
         out = torch.empty_like(self.q)
         args = (out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, s.scale, msl,
                 self.case.k_scale, self.case.v_scale, ps, ws)
-        if stages:
+        if self.mixed:
+            if stages:
+                pa.pa_decode_attention_kv(*args)
+                pa.pa_decode_reduce_kv(*args)
+            else:
+                pa.pa_decode_kv(*args)
+        elif stages:
             pa.pa_decode_attention(*args)
             pa.pa_decode_reduce(*args)
         else:
@@ -84,14 +93,15 @@ def oracle_step(case: W.DecodeCase):
     s = case.spec
     kp, vp = oracle.reshape_and_cache(case.k_pool, case.v_pool, s.cache_dtype, case.new_k,
                                       case.new_v, case.src_dtype, case.slot_mapping, s.block_size,
-                                      case.k_scale, case.v_scale)
+                                      case.k_scale, case.v_scale, v_cache_dtype=s.v_dtype)
     out = oracle.decode_attention(case.q, s.q_dtype, kp, vp, s.cache_dtype, case.block_tables,
                                   case.seq_lens, s.scale, s.block_size, s.num_kv_heads,
-                                  case.k_scale, case.v_scale)
+                                  case.k_scale, case.v_scale, v_cache_dtype=s.v_dtype)
     return out, kp, vp
 
 
-def custom_spec(name, hq, hkv, d, bs, q_dtype, cache_dtype):
+def custom_spec(name, hq, hkv, d, bs, q_dtype, cache_dtype, v_cache_dtype=None):
     return W.DecodeSpec(name, 1, hq, hkv, d, bs, q_dtype, cache_dtype, ("fixed", (1,)),
                         ("factor", 1.3), 1.0, 8192, 0,
-                        per_tensor_fp8_scale=(cache_dtype == "fp8_e4m3"))
+                        per_tensor_fp8_scale=(cache_dtype == "fp8_e4m3"),
+                        v_cache_dtype=v_cache_dtype)

@@ -141,6 +141,36 @@ def test_scatter_rejects_before_launch(lib, kw, code):
     assert st == code
 
 
+@pytest.mark.parametrize("qdt,kdt,vdt,code", [
+    (BF16, FP8, BF16, INVALID),        # supported pair: fails only on the null pointers
+    (F16, FP8, F16, INVALID),
+    (BF16, BF16, BF16, INVALID),
+    (BF16, FP8, F16, UNSUPPORTED),     # V must be the query type beside an fp8 K pool
+    (BF16, BF16, FP8, UNSUPPORTED),    # fp8 V beside a 16-bit K pool is not offered
+    (F32, FP8, F32, UNSUPPORTED),
+    (BF16, FP8, 9, INVALID),
+])
+def test_decode_kv_checks_the_format_pair(lib, qdt, kdt, vdt, code):
+    st = lib.pa_decode_kv(None, None, None, None, None, None, 0.1, 16, 4, 8, 2, 128, 8, 128, qdt,
+                          kdt, vdt, 1.0, 1.0, 0, None, 0, None)
+    assert st == code
+    assert lib.pa_decode_kv(None, None, None, None, None, None, 0.1, 16, 0, 8, 2, 128, 8, 128,
+                            BF16, FP8, BF16, 1.0, 1.0, 0, None, 0, None) == OK
+
+
+@pytest.mark.parametrize("src,kdt,vdt,code", [
+    (BF16, FP8, BF16, INVALID),        # supported pair: fails only on the null pointers
+    (F32, FP8, F32, INVALID),
+    (BF16, FP8, F16, UNSUPPORTED),
+    (BF16, BF16, FP8, UNSUPPORTED),
+    (BF16, FP8, 7, INVALID),
+])
+def test_scatter_kv_checks_the_format_pair(lib, src, kdt, vdt, code):
+    st = lib.pa_reshape_and_cache_kv(None, None, None, None, None, 5, 0, 0, 4, 2, 128, 16, src, kdt,
+                                     vdt, 1.0, 1.0, None)
+    assert st == code
+
+
 def test_scatter_and_copy_empty_are_ok(lib):
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 0, 0, 4, 2, 128, 16, BF16,
                                     BF16, 1.0, 1.0, None) == OK

@@ -15,7 +15,8 @@ from gpu_cases import TOL, DecodeRun, as_f64, custom_spec, lib, max_abs, oracle_
 
 pytestmark = pytest.mark.gpu
 
-FULL_CONFIGS = ["tiny_f32", "llama2_7b_mha_f16", "llama3_8b_gqa_bf16", "llama3_70b_fp8kv"]
+FULL_CONFIGS = ["tiny_f32", "llama2_7b_mha_f16", "llama3_8b_gqa_bf16", "llama3_70b_fp8kv",
+                "llama3_8b_kfp8_vbf16"]
 
 
 @pytest.fixture(scope="module")
@@ -39,9 +40,9 @@ def test_full_config_scatter_and_decode(name, full_cases):
     run = DecodeRun(case)
     run.scatter()
     torch.cuda.synchronize()
-    dt = case.spec.cache_dtype
+    dt, vdt = case.spec.cache_dtype, case.spec.v_dtype
     assert np.array_equal(W.torch_to_bits(run.k_pool, dt), okp), "K pool differs after scatter"
-    assert np.array_equal(W.torch_to_bits(run.v_pool, dt), ovp), "V pool differs after scatter"
+    assert np.array_equal(W.torch_to_bits(run.v_pool, vdt), ovp), "V pool differs after scatter"
     out = run.decode()
     err = max_abs(out, ref)
     print(f"[decode parity] {name}: max-abs {err:.3e}", flush=True)
@@ -186,6 +187,51 @@ def test_shape_sweep(q_dt, c_dt, hq, hkv, d, bs, partition):
     assert np.array_equal(W.torch_to_bits(run.k_pool, c_dt), okp)
     out = run.decode(partition_size=partition)
     assert max_abs(out, ref) <= TOL[q_dt]
+
+
+MIXED = [
+    # fp8 K beside a V pool of the query type: (q, Hq, Hkv, D, bs)
+    ("bf16", 8, 8, 128, 16),
+    ("bf16", 32, 8, 128, 32),
+    ("f16", 12, 3, 128, 16),
+    ("bf16", 8, 1, 64, 16),
+    ("f16", 4, 4, 64, 32),
+    ("bf16", 16, 2, 128, 8),
+    ("bf16", 8, 8, 64, 64),
+]
+
+
+@pytest.mark.parametrize("q_dt,hq,hkv,d,bs", MIXED)
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_mixed_k_fp8_v_16bit_sweep(q_dt, hq, hkv, d, bs, partition):
+    """intelliparadigm page §6.1: fp8 K cache, 16-bit V cache (scatter byte-exact in both pools)."""
+    if partition > 0 and partition % bs:
+        pytest.skip("partition must be a multiple of block_size")
+    spec = custom_spec(f"mixed_{q_dt}_{hq}_{hkv}_{d}_{bs}", hq, hkv, d, bs, q_dt, "fp8_e4m3",
+                       v_cache_dtype=q_dt)
+    case = W.make_decode_case(spec, lens=LENS)
+    ref, okp, ovp = oracle_step(case)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(run.k_pool, "fp8_e4m3"), okp)
+    assert np.array_equal(W.torch_to_bits(run.v_pool, q_dt), ovp)
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL[q_dt]
+    if partition == 64:
+        staged = run.decode(partition_size=partition, stages=True)
+        assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+
+
+def test_mixed_length_one_returns_its_value_row():
+    spec = custom_spec("len1_mixed", 8, 2, 128, 16, "bf16", "fp8_e4m3", v_cache_dtype="bf16")
+    case = W.make_decode_case(spec, lens=[1, 1, 1])
+    ref, _, _ = oracle_step(case)
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode()
+    exp = torch.from_numpy(ref).to(out.dtype)
+    assert torch.equal(out.cpu().view(torch.int16), exp.view(torch.int16))
 
 
 def _rewrite_k_dim0(case, values_per_seq, k_scale=None):

@@ -155,6 +155,11 @@ class DecodeSpec:
     partition_size: int = 0   # 0 = library's choice
     per_tensor_fp8_scale: bool = False
     description: str = ""
+    v_cache_dtype: str | None = None   # V pool type when it differs from the K pool's
+
+    @property
+    def v_dtype(self) -> str:
+        return self.v_cache_dtype or self.cache_dtype
 
     @property
     def group(self) -> int:
@@ -192,6 +197,13 @@ DECODE_SPECS = {
         description="70B-shaped layer on one GPU: 128 sequences, 64/8 heads, head_dim 128, block 16, "
                     "lens lognormal(median 1500, sigma 0.8) in [16,8192], fp8 e4m3 KV with "
                     "per-tensor scales, bf16 q, 512-token split-KV partitions"),
+    "llama3_8b_kfp8_vbf16": DecodeSpec(
+        "llama3_8b_kfp8_vbf16", 256, 32, 8, 128, 16, "bf16", "fp8_e4m3",
+        ("lognormal", 1200.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
+        per_tensor_fp8_scale=True, v_cache_dtype="bf16",
+        description="Llama-3-8B-shaped GQA layer with the mixed-precision cache (fp8 e4m3 K with "
+                    "a per-tensor scale, bf16 V, bf16 q): batch 256, 32/8 heads, head_dim 128, "
+                    "block 16, lens lognormal(median 1200, sigma 0.8) in [16,8192], pool 1.1x"),
 }
 
 
@@ -302,7 +314,7 @@ def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None 
     H, Hq, D, bs = spec.num_kv_heads, spec.num_q_heads, spec.head_dim, spec.block_size
     nb, poison_block = lay.num_blocks, lay.poison_block
 
-    cache_dt, q_dt = spec.cache_dtype, spec.q_dtype
+    cache_dt, v_dt, q_dt = spec.cache_dtype, spec.v_dtype, spec.q_dtype
     src_dt = q_dt                                  # new K/V arrive in the activation dtype
     std = np.float32(spec.value_std)
 
@@ -332,17 +344,20 @@ def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None 
                     m = max(m, float(np.abs(flat).max()))
             from_new = np.abs(bits_to_torch(new_bits, src_dt).float().numpy()).max() if S else 0.0
             return max(m, float(from_new))
-        k_scale = float(np.float32(amax(k_vals, new_k) / FP8_MAX))
-        v_scale = float(np.float32(amax(v_vals, new_v) / FP8_MAX))
+        if cache_dt == "fp8_e4m3":
+            k_scale = float(np.float32(amax(k_vals, new_k) / FP8_MAX))
+        if v_dt == "fp8_e4m3":
+            v_scale = float(np.float32(amax(v_vals, new_v) / FP8_MAX))
 
-    nan = NAN_BITS[cache_dt]
-    k_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[cache_dt])
-    v_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[cache_dt])
+    k_pool = np.full((nb, H, bs, D), NAN_BITS[cache_dt], dtype=BITS_DTYPE[cache_dt])
+    v_pool = np.full((nb, H, bs, D), NAN_BITS[v_dt], dtype=BITS_DTYPE[v_dt])
     for s, n in enumerate(seq_lens):
         n = int(n)
         ids = np.asarray(tables[s], dtype=np.int64)
-        for vals, pool, sc in ((k_vals[s], k_pool, k_scale), (v_vals[s], v_pool, v_scale)):
-            stored = to_bits(vals / np.float32(sc) if cache_dt == "fp8_e4m3" else vals, cache_dt)
+        for vals, pool, sc, dt in ((k_vals[s], k_pool, k_scale, cache_dt),
+                                   (v_vals[s], v_pool, v_scale, v_dt)):
+            nan = NAN_BITS[dt]
+            stored = to_bits(vals / np.float32(sc) if dt == "fp8_e4m3" else vals, dt)
             # poison every slot from the newest token on (the newest is written by the scatter)
             flat = stored.transpose(1, 0, 2, 3).reshape(H, -1, D)
             flat[:, n - 1:, :] = nan
@@ -512,11 +527,12 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
 # Byte accounting used by the benchmark
 # ---------------------------------------------------------------------------
 
-def effective_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int, cache_dtype: str) -> int:
+def effective_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int, cache_dtype: str,
+                       v_cache_dtype: str | None = None) -> int:
     """K and V bytes a decode step must read: sum_s len_s * Hkv * D * (eb_K + eb_V).
 
     For a Llama-2-7B-shaped fp16 layer (32 KV heads, head_dim 128) this is
     16 KiB per token, the per-layer figure the ybb.press page gives in §一.
     """
-    eb = ELEM_BYTES[cache_dtype]
-    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * num_kv_heads * head_dim * 2 * eb
+    eb = ELEM_BYTES[cache_dtype] + ELEM_BYTES[v_cache_dtype or cache_dtype]
+    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * num_kv_heads * head_dim * eb
