@@ -65,7 +65,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, ... */
   PA_ERR_UNSUPPORTED = 2, /* valid but not implemented: dtype pair, shape */
   PA_ERR_WORKSPACE = 3,   /* split decode needs a larger workspace */
-  PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+  PA_ERR_HIP = 4,         /* the HIP runtime reported an error */
+  PA_ERR_OUT_OF_BLOCKS = 5 /* host block manager: not enough free blocks (nothing changed) */
 } pa_status;
 
 /*

@@ -33,7 +33,7 @@ PA_DTYPE = {
     torch.float8_e4m3fn: 3,
 }
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
-          4: "PA_ERR_HIP"}
+          4: "PA_ERR_HIP", 5: "PA_ERR_OUT_OF_BLOCKS"}
 
 
 class PagedAttentionError(RuntimeError):
@@ -356,3 +356,7 @@ __all__ = [
     "pa_decode_workspace_bytes", "decode_workspace", "pa_probe_read", "pa_probe_copy",
     "PagedAttentionError", "library", "LIB_PATH",
 ]
+
+from .blocks import BlockManager, OutOfBlocks  # noqa: E402  (needs the names above)
+
+__all__ += ["BlockManager", "OutOfBlocks"]

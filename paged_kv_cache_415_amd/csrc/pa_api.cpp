@@ -227,6 +227,14 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
 
 }  // namespace
 
+namespace pa {
+// Status with a message for pa_last_error(), for the other host-side files.
+pa_status report(pa_status code, const char* message) {
+  if (code == PA_OK) return ok();
+  return fail(code, "%s", message);
+}
+}  // namespace pa
+
 extern "C" {
 
 pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_pool, void* v_pool,
@@ -568,6 +576,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS";
     default: return "PA_ERR_UNKNOWN";
   }
 }

@@ -8,7 +8,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", f) for f in ("pa.h", "pa_probe.h")]
+HEADERS = [os.path.join(ROOT, "include", f) for f in ("pa.h", "pa_probe.h", "pa_blocks.h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 F32, F16, BF16, FP8 = 0, 1, 2, 3
@@ -49,6 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.pa_status_string(0) == b"PA_OK"
     assert lib.pa_status_string(3) == b"PA_ERR_WORKSPACE"
+    assert lib.pa_status_string(5) == b"PA_ERR_OUT_OF_BLOCKS"
     assert lib.pa_status_string(77) == b"PA_ERR_UNKNOWN"
 
 
