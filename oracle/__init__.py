@@ -29,6 +29,7 @@ from .elements import (
     decode_elements,
     e4m3_value_table,
     e4m3_encode,
+    int8_encode,
 )
 from .paged import (
     num_blocks,
@@ -49,6 +50,7 @@ __all__ = [
     "decode_elements",
     "e4m3_value_table",
     "e4m3_encode",
+    "int8_encode",
     "num_blocks",
     "locate_token",
     "gather_sequence",

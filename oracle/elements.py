@@ -12,6 +12,7 @@ f32        uint32       IEEE binary32
 f16        uint16       IEEE binary16
 bf16       uint16       the upper 16 bits of an IEEE binary32
 fp8_e4m3   uint8        OCP 8-bit float E4M3FN (no infinities)
+int8       int8         two's-complement integer code (scaled per block)
 =========  ===========  ==================================================
 
 Every value of these formats is exactly representable in float64, so the
@@ -26,6 +27,12 @@ infinities saturate to the largest finite magnitude 448, NaN keeps its sign and
 becomes the NaN code.  The saturation rule is a convention the pages do not fix
 ("parity unpinned" for inputs beyond 448 in magnitude); everything else is
 pinned by the tests against closed forms and torch's CPU cast.
+
+INT8 (the same ybb.press §6.2 sentence): the pages fix no scale granularity or
+rounding.  The reading taken: symmetric codes in [-127, 127], one float32
+scale per (block, KV head) for K and one for V, code = round-half-even of
+float32(x) / float32(scale) (one correctly rounded float32 division), clamped
+to [-127, 127]; NaN stores 0.  The value of a code is code * scale.
 """
 
 from __future__ import annotations
@@ -37,6 +44,7 @@ STORAGE_DTYPES = {
     "f16": np.uint16,
     "bf16": np.uint16,
     "fp8_e4m3": np.uint8,
+    "int8": np.int8,
 }
 
 
@@ -113,4 +121,15 @@ def decode_elements(bits: np.ndarray, dtype: str) -> np.ndarray:
         return widened.view(np.float32).astype(np.float64)
     if dtype == "fp8_e4m3":
         return _E4M3[bits.astype(np.uint8)]
+    if dtype == "int8":
+        return bits.astype(np.uint8).view(np.int8).astype(np.float64)
     raise ValueError(f"unknown element type {dtype!r}")
+
+
+def int8_encode(x_f32: np.ndarray, scale_f32) -> np.ndarray:
+    """Symmetric INT8 code of float32 values under a float32 scale (see the
+    module docstring): round half to even of x / scale, clamped to ±127, NaN -> 0."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    q = x / np.asarray(scale_f32, dtype=np.float32)        # one float32 division
+    q = np.where(np.isnan(q), np.float32(0), q)
+    return np.clip(np.rint(q), -127, 127).astype(np.int8)

@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .elements import decode_elements, e4m3_encode
+from .elements import decode_elements, e4m3_encode, int8_encode
 
 
 def num_blocks(seq_len: int, block_size: int) -> int:
@@ -54,7 +54,7 @@ def locate_token(block_table_row, position: int, block_size: int):
 
 
 def gather_sequence(pool_bits, dtype: str, block_table_row, seq_len: int,
-                    block_size: int) -> np.ndarray:
+                    block_size: int, block_scales=None) -> np.ndarray:
     """Gather one sequence's cache from the pool into a contiguous array.
 
     datawhalechina page, Step 2 and "参考代码与解析" TODO 5: take the physical
@@ -62,11 +62,17 @@ def gather_sequence(pool_bits, dtype: str, block_table_row, seq_len: int,
     axis into one logically contiguous cache, and keep only the first
     seq_len tokens because the last block may be only partly filled.
 
+    With ``block_scales`` ([num_blocks][num_kv_heads], the int8 cache's
+    per-block scales) each block's values are its codes times its scale.
+
     Returns float64 [num_kv_heads][seq_len][head_dim].
     """
     nb = num_blocks(seq_len, block_size)
     ids = np.asarray(block_table_row[:nb], dtype=np.int64)
     blocks = decode_elements(pool_bits[ids], dtype)        # [nb][H][bs][D]
+    if block_scales is not None:
+        sc = np.asarray(block_scales, dtype=np.float32).astype(np.float64)[ids]
+        blocks = blocks * sc[:, :, None, None]
     heads = blocks.shape[1]
     dim = blocks.shape[3]
     joined = blocks.transpose(1, 0, 2, 3).reshape(heads, nb * block_size, dim)
@@ -97,7 +103,8 @@ def softmax_attention(q_rows: np.ndarray, keys: np.ndarray, values: np.ndarray,
 def decode_attention(q_bits, q_dtype: str, k_pool, v_pool, cache_dtype: str,
                      block_tables, seq_lens, scale: float, block_size: int,
                      num_kv_heads: int, k_scale: float = 1.0,
-                     v_scale: float = 1.0, v_cache_dtype: str | None = None) -> np.ndarray:
+                     v_scale: float = 1.0, v_cache_dtype: str | None = None,
+                     k_block_scales=None, v_block_scales=None) -> np.ndarray:
     """Paged decode attention: one query token per sequence.
 
     bogosort page §8 (the attention kernel finds each sequence's past K/V
@@ -112,6 +119,9 @@ def decode_attention(q_bits, q_dtype: str, k_pool, v_pool, cache_dtype: str,
     zero output.  v_cache_dtype names the V pool's element type when it
     differs from the K pool's (the intelliparadigm page §6.1 pairs an fp8 K
     cache with a bf16 V cache); by default both pools hold cache_dtype.
+    k_block_scales / v_block_scales ([num_blocks][num_kv_heads]) give the int8
+    cache's per-block scales (ybb.press §6.2, INT8 KV cache), applied before
+    k_scale / v_scale.
 
     q_bits [S][Hq][D]; pools [NB][Hkv][bs][D]; block_tables [S][MB];
     seq_lens [S].  Returns float64 [S][Hq][D].
@@ -126,9 +136,10 @@ def decode_attention(q_bits, q_dtype: str, k_pool, v_pool, cache_dtype: str,
         n = int(seq_lens[s])
         if n <= 0:
             continue
-        keys = gather_sequence(k_pool, cache_dtype, block_tables[s], n, block_size) * float(k_scale)
+        keys = gather_sequence(k_pool, cache_dtype, block_tables[s], n, block_size,
+                               k_block_scales) * float(k_scale)
         vals = gather_sequence(v_pool, v_cache_dtype or cache_dtype, block_tables[s], n,
-                               block_size) * float(v_scale)
+                               block_size, v_block_scales) * float(v_scale)
         for h in range(num_q_heads):
             kv = h // group
             out[s, h] = softmax_attention(q[s, h][None, :], keys[kv], vals[kv], scale)[0]
@@ -197,7 +208,8 @@ def prefill_chunk_attention(q_bits, q_dtype: str, query_start_loc, k_pool, v_poo
 def reshape_and_cache(k_pool, v_pool, cache_dtype: str, key_bits, value_bits,
                       src_dtype: str, slot_mapping, block_size: int,
                       k_scale: float = 1.0, v_scale: float = 1.0,
-                      v_cache_dtype: str | None = None):
+                      v_cache_dtype: str | None = None, k_block_scales=None,
+                      v_block_scales=None):
     """Write new tokens' K/V into their pool slots; returns new (k_pool, v_pool).
 
     datawhalechina page, Step 3 item 3 and Step 4: physical block indices are
@@ -210,15 +222,18 @@ def reshape_and_cache(k_pool, v_pool, cache_dtype: str, key_bits, value_bits,
     division done once in float32, as the ybb.press page's §6.2 (FP8 KV cache)
     leaves the arithmetic open.  Slots are assumed distinct.  v_cache_dtype
     names the V pool's element type when it differs from the K pool's
-    (intelliparadigm page §6.1: fp8 K cache, bf16 V cache).
+    (intelliparadigm page §6.1: fp8 K cache, bf16 V cache).  An int8 cache
+    stores int8_encode(x, scale[block][head]) with the per-block scales
+    k_block_scales / v_block_scales ([num_blocks][num_kv_heads] float32).
 
     key_bits/value_bits [T][Hkv][D]; slot_mapping [T] int64.
     """
     k_new = np.array(k_pool, copy=True)
     v_new = np.array(v_pool, copy=True)
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    for src, dst, scale, pool_dtype in ((key_bits, k_new, k_scale, cache_dtype),
-                                        (value_bits, v_new, v_scale, v_cache_dtype or cache_dtype)):
+    for src, dst, scale, pool_dtype, bsc in ((key_bits, k_new, k_scale, cache_dtype, k_block_scales),
+                                             (value_bits, v_new, v_scale, v_cache_dtype or cache_dtype,
+                                              v_block_scales)):
         src = np.asarray(src)
         for t, slot in enumerate(slots):
             if slot < 0:
@@ -226,6 +241,10 @@ def reshape_and_cache(k_pool, v_pool, cache_dtype: str, key_bits, value_bits,
             blk, row = int(slot // block_size), int(slot % block_size)
             if pool_dtype == src_dtype:
                 dst[blk, :, row, :] = src[t]
+            elif pool_dtype == "int8":
+                x32 = decode_elements(src[t], src_dtype).astype(np.float32)   # [H][D]
+                sc = np.asarray(bsc, dtype=np.float32)[blk]                  # [H]
+                dst[blk, :, row, :] = int8_encode(x32, sc[:, None])
             elif pool_dtype == "fp8_e4m3":
                 x32 = decode_elements(src[t], src_dtype).astype(np.float32)
                 q32 = x32 / np.float32(scale)

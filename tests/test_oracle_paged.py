@@ -315,6 +315,90 @@ def test_mixed_scatter_is_fp8_k_and_copied_v():
     assert not vm[1, :, 0].any() and not vm[2, :, 0].any()
 
 
+
+# ------------------------------------------------------------ int8 cache with per-block scales
+
+def test_int8_codec_hand_values():
+    x = np.array([2.5, 3.5, -2.5, -3.5, 126.7, 127.5, 1000.0, -1000.0, np.nan, np.inf, 0.49,
+                  -0.5, 1.0000001], np.float32)
+    got = oracle.int8_encode(x, np.float32(1.0))
+    assert list(got) == [2, 4, -2, -4, 127, 127, 127, -127, 0, 127, 0, 0, 1]
+    # one float32 division, then round half to even
+    assert oracle.int8_encode(np.float32(0.3), np.float32(0.1)) == 3
+    assert oracle.int8_encode(np.float32(-7.0), np.float32(2.0)) == -4      # -3.5 -> -4 (even)
+
+
+def _int8_pools(rng, lens, hkv, d, bs):
+    need = [-(-n // bs) for n in lens]
+    nb = sum(need) + 2
+    ids = rng.permutation(nb)
+    kc = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+    vc = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+    ks = (rng.uniform(0.5, 2.0, (nb, hkv)) / 127).astype(np.float32)
+    vs = (rng.uniform(0.5, 2.0, (nb, hkv)) / 127).astype(np.float32)
+    tables = np.full((len(lens), max(need)), nb - 1, np.int32)
+    cur = 0
+    for s, n in enumerate(lens):
+        tables[s, :need[s]] = ids[cur:cur + need[s]]
+        cur += need[s]
+    return kc, vc, ks, vs, tables
+
+
+def test_int8_uniform_scales_equal_the_per_tensor_path():
+    # every block with the same scale: the per-block path must equal codes held
+    # exactly in float32 pools with that scale applied per tensor
+    rng = np.random.default_rng(31)
+    lens = [1, 9, 40]
+    kc, vc, _, _, tables = _int8_pools(rng, lens, 2, 16, 8)
+    nb = kc.shape[0]
+    ks = np.full((nb, 2), np.float32(0.013), np.float32)
+    vs = np.full((nb, 2), np.float32(0.021), np.float32)
+    q = W.to_bits(rng.standard_normal((3, 4, 16)).astype(np.float32), "bf16")
+    got = oracle.decode_attention(q, "bf16", kc.view(np.uint8), vc.view(np.uint8), "int8", tables,
+                                  lens, 0.25, 8, 2, k_block_scales=ks, v_block_scales=vs)
+    ref = oracle.decode_attention(q, "bf16", _f32_bits(kc.astype(np.float32)),
+                                  _f32_bits(vc.astype(np.float32)), "f32", tables, lens, 0.25, 8, 2,
+                                  k_scale=float(np.float32(0.013)), v_scale=float(np.float32(0.021)))
+    assert np.array_equal(got, ref)
+
+
+def test_int8_per_block_scales_match_sdpa_of_dequantised_cache():
+    rng = np.random.default_rng(32)
+    lens = [23, 50]
+    bs, hkv, d = 8, 2, 16
+    kc, vc, ks, vs, tables = _int8_pools(rng, lens, hkv, d, bs)
+    qf = rng.standard_normal((2, 4, d)).astype(np.float32)
+    got = oracle.decode_attention(_f32_bits(qf), "f32", kc.view(np.uint8), vc.view(np.uint8), "int8",
+                                  tables, lens, 0.3, bs, hkv, k_block_scales=ks, v_block_scales=vs)
+    for s, n in enumerate(lens):
+        keys = np.zeros((hkv, n, d))
+        vals = np.zeros((hkv, n, d))
+        for p in range(n):                       # token by token, through the block table
+            b = tables[s, p // bs]
+            for h in range(hkv):
+                keys[h, p] = kc[b, h, p % bs].astype(np.float64) * np.float64(ks[b, h])
+                vals[h, p] = vc[b, h, p % bs].astype(np.float64) * np.float64(vs[b, h])
+        ref = _sdpa(qf[s][:, None, :], keys, vals, 0.3)[:, 0, :]
+        np.testing.assert_allclose(got[s], ref, rtol=0, atol=1e-12)
+
+
+def test_int8_scatter_uses_each_blocks_scale():
+    key = np.array([[[1.0, -2.0, 0.3, 100.0]], [[0.5, 0.25, -0.75, 3.0]]], np.float32)
+    pool = np.zeros((3, 1, 2, 4), np.uint8)
+    ks = np.array([[0.5], [0.25], [1.0]], np.float32)
+    vs = np.array([[1.0], [1.0], [0.1]], np.float32)
+    slots = np.array([5, 0], np.int64)              # token 0 -> block 2 row 1, token 1 -> block 0 row 0
+    kp, vp = oracle.reshape_and_cache(pool, pool, "int8", _f32_bits(key), _f32_bits(key), "f32",
+                                      slots, 2, k_block_scales=ks, v_block_scales=vs)
+    k = kp.view(np.int8)
+    v = vp.view(np.int8)
+    assert list(k[2, 0, 1]) == [1, -2, 0, 100]       # scale 1.0
+    assert list(k[0, 0, 0]) == [1, 0, -2, 6]         # scale 0.5: 1, 0.5 -> 0, -1.5 -> -2, 6
+    assert list(v[2, 0, 1]) == [10, -20, 3, 127]     # scale 0.1 (100 / 0.1 saturates)
+    assert list(v[0, 0, 0]) == [0, 0, -1, 3]         # scale 1.0: 0.5 -> 0, 0.25 -> 0, -0.75 -> -1
+    assert not k[1].any() and not v[1].any()
+
+
 # ------------------------------------------------------------ prefill chunk
 
 def _bottom_right_mask(rows, n):
