@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama2_7b_mha_f16",
                     help="llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
+                         "| llama3_8b_int8kv "
                          "| tiny_f32 "
                          "| mixed_prefix_bf16")
     ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
@@ -87,6 +88,15 @@ def _to_cache(x, dtype: str):
     return x.to(W.TORCH_DTYPE[dtype]), 1.0
 
 
+def _to_int8_blocks(x):
+    """float32 pool -> int8 codes with one scale per (block, KV head): amax / 127."""
+    import torch
+    amax = x.abs().amax(dim=(2, 3))
+    scales = torch.where(amax > 0, amax / 127.0, torch.ones_like(amax)).float().contiguous()
+    codes = (x / scales[:, :, None, None]).round_().clamp_(-127, 127).to(torch.int8)
+    return codes, scales
+
+
 class DecodeBatch:
     """One decode batch resident in HBM (values drawn on the device)."""
 
@@ -97,8 +107,13 @@ class DecodeBatch:
         gen = torch.Generator(device=dev)
         gen.manual_seed(seed)
         shape = (lay.num_blocks, s.num_kv_heads, s.block_size, s.head_dim)
-        self.k_pool, self.k_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.cache_dtype)
-        self.v_pool, self.v_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.v_dtype)
+        if s.cache_dtype == "int8":
+            self.k_pool, self.k_scales = _to_int8_blocks(_randn(shape, gen, dev, s.value_std))
+            self.v_pool, self.v_scales = _to_int8_blocks(_randn(shape, gen, dev, s.value_std))
+            self.k_scale = self.v_scale = 1.0
+        else:
+            self.k_pool, self.k_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.cache_dtype)
+            self.v_pool, self.v_scale = _to_cache(_randn(shape, gen, dev, s.value_std), s.v_dtype)
         S = len(lay.seq_lens)
         qdt = W.TORCH_DTYPE[s.q_dtype]
         self.q = _randn((S, s.num_q_heads, s.head_dim), gen, dev, s.value_std).to(qdt)
@@ -136,20 +151,33 @@ def run_decode_bench(args, dev):
     ws = pa.decode_workspace(b0.q, b0.k_pool, max_len, part)
 
     mixed = spec.v_dtype != spec.cache_dtype     # fp8 K beside a 16-bit V pool
+    int8 = spec.cache_dtype == "int8"            # per-(block, KV head) scales
     scatter = pa.pa_reshape_and_cache_kv if mixed else pa.pa_reshape_and_cache
     attention = pa.pa_decode_attention_kv if mixed else pa.pa_decode_attention
     reduce = pa.pa_decode_reduce_kv if mixed else pa.pa_decode_reduce
 
     def step(b, ev=None):
-        scatter(b.new_k, b.new_v, b.k_pool, b.v_pool, b.slots, b.k_scale, b.v_scale)
+        if int8:
+            pa.pa_reshape_and_cache_int8(b.new_k, b.new_v, b.k_pool, b.v_pool, b.k_scales,
+                                         b.v_scales, b.slots)
+        else:
+            scatter(b.new_k, b.new_v, b.k_pool, b.v_pool, b.slots, b.k_scale, b.v_scale)
         if ev is not None:
             ev[0].record()
-        attention(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
-                  max_len, b.k_scale, b.v_scale, part, ws)
+        if int8:
+            pa.pa_decode_attention_int8(b.out, b.q, b.k_pool, b.v_pool, b.k_scales, b.v_scales,
+                                        b.tables, b.lens, spec.scale, max_len, part, ws)
+        else:
+            attention(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
+                      max_len, b.k_scale, b.v_scale, part, ws)
         if ev is not None:
             ev[1].record()
-        reduce(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
-               max_len, b.k_scale, b.v_scale, part, ws)
+        if int8:
+            pa.pa_decode_reduce_int8(b.out, b.q, b.k_pool, b.v_pool, b.k_scales, b.v_scales,
+                                     b.tables, b.lens, spec.scale, max_len, part, ws)
+        else:
+            reduce(b.out, b.q, b.k_pool, b.v_pool, b.tables, b.lens, spec.scale,
+                   max_len, b.k_scale, b.v_scale, part, ws)
         if ev is not None:
             ev[2].record()
 
@@ -190,6 +218,8 @@ def run_decode_bench(args, dev):
 
     eff = W.effective_kv_bytes(lay.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
                                spec.v_dtype)
+    if spec.cache_dtype == "int8":
+        eff += W.block_scale_bytes(lay.seq_lens, spec.num_kv_heads, spec.block_size)
     ms_step = elapsed * 1e3 / args.steps
     attn_avg = float(np.mean(attn_ms))
     S = len(lay.seq_lens)
@@ -509,6 +539,8 @@ def cpu_baseline(args):
     case = W.make_decode_case(spec, rep=0, num_seqs=nseq)
     eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
                                spec.v_dtype)
+    if spec.cache_dtype == "int8":
+        eff += W.block_scale_bytes(case.seq_lens, spec.num_kv_heads, spec.block_size)
     passes, spent = 0, 0.0
     with threadpool_limits(1):
         while spent < args.cpu_seconds or passes == 0:
@@ -516,7 +548,9 @@ def cpu_baseline(args):
             oracle.decode_attention(case.q, spec.q_dtype, case.k_pool, case.v_pool,
                                     spec.cache_dtype, case.block_tables, case.seq_lens,
                                     spec.scale, spec.block_size, spec.num_kv_heads,
-                                    case.k_scale, case.v_scale, v_cache_dtype=spec.v_dtype)
+                                    case.k_scale, case.v_scale, v_cache_dtype=spec.v_dtype,
+                                    k_block_scales=case.k_block_scales,
+                                    v_block_scales=case.v_block_scales)
             spent += time.perf_counter() - t0
             passes += 1
     return {"value": round(eff * passes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,

@@ -22,11 +22,14 @@
  *   [num_blocks][num_kv_heads][block_size][head_dim]   (row-major)
  *   so one (block, KV head) tile of block_size x head_dim elements is
  *   contiguous.  A token's slot is physical_block * block_size + offset.
- * Element types (pa_dtype): f32, f16, bf16 and OCP fp8 E4M3FN (cache only).
- *   Supported (q, cache) pairs: (f32,f32) (f16,f16) (bf16,bf16) (bf16,fp8)
- *   (f16,fp8).  Outputs have the query's type.  For an fp8 cache the stored
- *   code times the per-tensor k_scale / v_scale is the value; the scales are
- *   applied the same way for other cache types (pass 1.0f).
+ * Element types (pa_dtype): f32, f16, bf16, OCP fp8 E4M3FN and int8 (cache
+ *   only).  Supported (q, cache) pairs: (f32,f32) (f16,f16) (bf16,bf16)
+ *   (bf16,fp8) (f16,fp8); with separate K/V types also an fp8 K pool beside a
+ *   V pool of the query type (pa_*_kv); int8 K and V pools with per-block
+ *   scales and bf16/f16 queries (pa_*_int8).  Outputs have the query's type.
+ *   For an fp8 cache the stored code times the per-tensor k_scale / v_scale
+ *   is the value; the scales are applied the same way for other cache types
+ *   (pass 1.0f).
  * Shapes.  head_dim is 64 or 128; block_size is 8, 16, 32 or 64; num_q_heads is a
  *   multiple of num_kv_heads with at most 16 query heads per KV head.  Query
  *   head h uses KV head h / (num_q_heads / num_kv_heads).
@@ -57,7 +60,8 @@ typedef enum {
   PA_DTYPE_F32 = 0,
   PA_DTYPE_F16 = 1,
   PA_DTYPE_BF16 = 2,
-  PA_DTYPE_FP8_E4M3 = 3
+  PA_DTYPE_FP8_E4M3 = 3,
+  PA_DTYPE_INT8 = 4      /* symmetric int8 codes with per-(block, KV head) scales */
 } pa_dtype;
 
 typedef enum {
@@ -116,6 +120,28 @@ pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_po
                                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t block_size, pa_dtype src_dtype, pa_dtype k_cache_dtype,
                                   pa_dtype v_cache_dtype, float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_reshape_and_cache_int8 — the scatter into an INT8 cache ([ybb] §6.2:
+ * an INT8 or FP8 KV cache halves the bytes per token; the page fixes no scale
+ * granularity or rounding).  Each (block, KV head) of the K pool has one
+ * float32 scale k_scales[block][head], likewise v_scales for V, set by the
+ * caller (for instance from the amax of the block's tokens) before tokens
+ * are written into the block.  Element x of token t (slot s, block
+ * b = s / block_size) of head h is stored as
+ *   code = clamp(round_half_even(float32(x) / k_scales[b][h]), -127, 127)
+ * with one correctly rounded float32 division; NaN stores 0.  Scales must be
+ * finite and positive (device data, not checked).  The other arguments and
+ * rules are those of pa_reshape_and_cache with src_dtype f32/f16/bf16; pools
+ * hold int8 codes.
+ *   k_scales, v_scales  float32 [num_blocks][num_kv_heads], device memory
+ */
+pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_pool, void* v_pool,
+                                    const float* k_scales, const float* v_scales,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    int64_t key_token_stride, int64_t value_token_stride,
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, pa_dtype src_dtype, void* stream);
 
 /*
  * pa_copy_blocks — copy whole blocks for copy-on-write.
@@ -313,6 +339,36 @@ pa_status pa_decode_reduce_kv(void* out, const void* q, const void* k_pool, cons
                               pa_dtype v_cache_dtype, float k_scale, float v_scale,
                               int32_t partition_size, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * pa_decode_int8 — pa_decode over an INT8 cache with per-block scales (see
+ * pa_reshape_and_cache_int8): for token j in block b,
+ *   logit_j = scale * k_scales[b][kv] * (q . Kcode[j])
+ *   out = sum_j softmax(logit)_j * v_scales[b][kv] * Vcode[j]
+ * q_dtype bf16 or f16 (codes enter the matrix products exactly as that
+ * type).  Other arguments, limits, workspace and partition rules are those
+ * of pa_decode; the attention / reduce stages are split as for pa_decode.
+ */
+pa_status pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                         const int32_t* seq_lens, float scale, int32_t block_size, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_blocks_per_seq, int32_t max_seq_len, pa_dtype q_dtype,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_attention_int8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                   const float* k_scales, const float* v_scales,
+                                   const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                                   int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                   int32_t max_seq_len, pa_dtype q_dtype, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_decode_reduce_int8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                const float* k_scales, const float* v_scales,
+                                const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                                int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                int32_t max_seq_len, pa_dtype q_dtype, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_prefill_chunk — causal attention of one prefill chunk per sequence

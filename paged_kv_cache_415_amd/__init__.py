@@ -31,6 +31,7 @@ PA_DTYPE = {
     torch.float16: 1,
     torch.bfloat16: 2,
     torch.float8_e4m3fn: 3,
+    torch.int8: 4,
 }
 STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
           4: "PA_ERR_HIP", 5: "PA_ERR_OUT_OF_BLOCKS"}
@@ -69,6 +70,13 @@ def _load() -> ctypes.CDLL:
     for name in ("pa_decode_kv", "pa_decode_attention_kv", "pa_decode_reduce_kv"):
         getattr(lib, name).argtypes = dec[:16] + [i32] + dec[16:]
         getattr(lib, name).restype = i32
+    dec8 = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    for name in ("pa_decode_int8", "pa_decode_attention_int8", "pa_decode_reduce_int8"):
+        getattr(lib, name).argtypes = dec8
+        getattr(lib, name).restype = i32
+    lib.pa_reshape_and_cache_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32,
+                                              i32, i32, vp]
+    lib.pa_reshape_and_cache_int8.restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, f32, vp]
     lib.pa_status_string.argtypes = [i32]
@@ -158,6 +166,72 @@ def _scatter(fn, key, value, k_pool, v_pool, slot_mapping, k_scale, v_scale, str
     _check(fn(_ptr(key, False), _ptr(value, False), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping),
               t, key_stride, value_stride, nb, hkv, d, bs, _dtype(key), *types, k_scale, v_scale,
               _stream(stream)))
+
+
+def _scales(t, k_pool):
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    if t.dtype != torch.float32 or tuple(t.shape) != (nb, hkv):
+        raise ValueError("per-block scales must be float32 [num_blocks][num_kv_heads]")
+    return _ptr(t)
+
+
+def pa_reshape_and_cache_int8(key, value, k_pool, v_pool, k_scales, v_scales, slot_mapping,
+                              stream=None) -> None:
+    """Scatter key/value into an int8 cache with per-(block, KV head) scales (see pa.h)."""
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
+        raise TypeError("int8 pools expected")
+    nb, hkv, bs, d = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("V pool shape does not match the K pool")
+    t = slot_mapping.shape[0]
+    for x in (key, value):
+        if x.dim() != 3 or x.shape[1:] != (hkv, d) or x.stride(2) != 1 or x.stride(1) != d:
+            raise ValueError("key/value must be [T][num_kv_heads][head_dim] with dense rows")
+    _check(_lib.pa_reshape_and_cache_int8(
+        _ptr(key, False), _ptr(value, False), _ptr(k_pool), _ptr(v_pool), _scales(k_scales, k_pool),
+        _scales(v_scales, k_pool), _ptr(slot_mapping), t, key.stride(0) if t > 0 else 0,
+        value.stride(0) if t > 0 else 0, nb, hkv, d, bs, _dtype(key), _stream(stream)))
+
+
+def _decode_int8_call(fn, out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens, scale,
+                      max_seq_len, partition_size, workspace, stream):
+    s, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8 or v_pool.shape != k_pool.shape:
+        raise TypeError("int8 pools of one shape expected")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _scales(k_scales, k_pool),
+              _scales(v_scales, k_pool), _ptr(block_tables), _ptr(seq_lens), float(scale), bs, s,
+              hq, hkv, d, block_tables.shape[1], int(max_seq_len), _dtype(q), int(partition_size),
+              _ptr(workspace), wbytes, _stream(stream)))
+
+
+def pa_decode_int8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                   scale: float, max_seq_len: int = 0, partition_size: int = 0, workspace=None,
+                   stream=None) -> None:
+    """Decode attention over an int8 cache with per-(block, KV head) scales (see pa.h)."""
+    _decode_int8_call(_lib.pa_decode_int8, out, q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                      seq_lens, scale, max_seq_len, partition_size, workspace, stream)
+
+
+def pa_decode_attention_int8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                             scale: float, max_seq_len: int = 0, partition_size: int = 0,
+                             workspace=None, stream=None) -> None:
+    """First stage of pa_decode_int8."""
+    _decode_int8_call(_lib.pa_decode_attention_int8, out, q, k_pool, v_pool, k_scales, v_scales,
+                      block_tables, seq_lens, scale, max_seq_len, partition_size, workspace, stream)
+
+
+def pa_decode_reduce_int8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                          scale: float, max_seq_len: int = 0, partition_size: int = 0,
+                          workspace=None, stream=None) -> None:
+    """Second stage of pa_decode_int8."""
+    _decode_int8_call(_lib.pa_decode_reduce_int8, out, q, k_pool, v_pool, k_scales, v_scales,
+                      block_tables, seq_lens, scale, max_seq_len, partition_size, workspace, stream)
 
 
 def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
@@ -349,7 +423,8 @@ def pa_probe_copy(dst, src, stream=None) -> None:
 
 __all__ = [
     "pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_decode_kv", "pa_decode_attention_kv",
-    "pa_decode_reduce_kv", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
+    "pa_decode_reduce_kv", "pa_reshape_and_cache_int8", "pa_decode_int8", "pa_decode_attention_int8",
+    "pa_decode_reduce_int8", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
     "layer_pool_pointers",
     "pa_swap_blocks", "pa_decode", "pa_decode_attention",
     "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",

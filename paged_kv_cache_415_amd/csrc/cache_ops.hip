@@ -90,6 +90,42 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterParams p) {
   }
 }
 
+// Quantising scatter into an int8 pool with one scale per (block, KV head):
+// each thread turns 16 source elements of K and of V into 16 codes each.
+template <typename SrcT>
+__global__ __launch_bounds__(256) void scatter_i8_kernel(ScatterParams p) {
+  const int t = blockIdx.x;
+  const int64_t slot = p.slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / p.block_size;
+  const int row = (int)(slot - blk * p.block_size);
+  const int groups_per_head = p.head_dim / 16;
+  const int ngroups = p.num_kv_heads * groups_per_head;
+  const SrcT* ksrc = reinterpret_cast<const SrcT*>(p.key) + (int64_t)t * p.key_stride;
+  const SrcT* vsrc = reinterpret_cast<const SrcT*>(p.value) + (int64_t)t * p.value_stride;
+  for (int i = threadIdx.x; i < ngroups; i += blockDim.x) {
+    const int h = i / groups_per_head;
+    const int c = i - h * groups_per_head;
+    const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 16;
+    const int64_t src = (int64_t)h * p.head_dim + c * 16;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const SrcT* s = which ? vsrc : ksrc;
+      const float scale = (which ? p.v_scales : p.k_scales)[blk * p.num_kv_heads + h];
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc |= ((uint32_t)i8_encode((float)s[src + q * 4 + b], scale) & 0xFFu) << (8 * b);
+        w[q] = acc;
+      }
+      st16((char*)(which ? p.v_pool : p.k_pool) + dst, u32x4{w[0], w[1], w[2], w[3]});
+    }
+  }
+}
+
 // Copy nvec 16-byte vectors with the workgroups of grid dimension x; each
 // thread keeps four loads in flight.
 __device__ __forceinline__ void copy_vecs(char* dst, const char* src, int64_t nvec) {
@@ -176,7 +212,11 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream) {
   if (p.num_tokens == 0) return hipSuccess;
   dim3 grid(p.num_tokens), block(256);
   const bool vq = p.v_cache_dtype != p.src_dtype;   // V quantised too
-  if (p.cache_dtype == p.src_dtype) {
+  if (p.cache_dtype == kI8) {
+    if (p.src_dtype == kBF16) hipLaunchKernelGGL(scatter_i8_kernel<__bf16>, grid, block, 0, stream, p);
+    else if (p.src_dtype == kF16) hipLaunchKernelGGL(scatter_i8_kernel<_Float16>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(scatter_i8_kernel<float>, grid, block, 0, stream, p);
+  } else if (p.cache_dtype == p.src_dtype) {
     hipLaunchKernelGGL(scatter_copy_kernel<void>, grid, block, 0, stream, p);
   } else if (p.src_dtype == kBF16) {
     if (vq) hipLaunchKernelGGL((scatter_fp8_kernel<__bf16, true>), grid, block, 0, stream, p);

@@ -71,6 +71,7 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // Block-table rows are read through the constant address space: uniform
 // indices then become scalar loads (the kernels never write the tables).
 typedef const __attribute__((address_space(4))) int* ctab_ptr;
+typedef const __attribute__((address_space(4))) float* cscale_ptr;   // per-block scales, read-only
 
 // ---------------------------------------------------------------------------
 // Plan: clamped lengths and the exclusive prefix sum of per-sequence counts
@@ -163,14 +164,20 @@ struct TableWindow {
 };
 
 // ---------------------------------------------------------------------------
-// MFMA segment for 16-bit and fp8 caches.
+// MFMA segment for 16-bit, fp8 and int8 caches.
 //   QT: query / output / MFMA operand type (__bf16 or _Float16)
-//   KF8, VF8: the K / V pool holds E4M3 codes (decoded exactly to QT);
-//   otherwise it holds QT.  K fp8 with V in QT is the mixed format of the
-//   intelligence-ai page §6.1 (fp8 K cache, bf16 V cache).
+//   KF, VF: element format of the K / V pool: kFmtQ (QT itself), kFmtFp8
+//   (E4M3 codes, decoded exactly to QT) or kFmtI8 (int8 codes with one
+//   float32 scale per (block, KV head), in p.k_scales / p.v_scales).  K fp8
+//   with V in QT is the mixed format of the intelliparadigm page §6.1 (fp8 K
+//   cache, bf16 V cache).
 // ---------------------------------------------------------------------------
-template <typename QT, bool KF8, bool VF8, int D, int BS>
+enum : int { kFmtQ = 0, kFmtFp8 = 1, kFmtI8 = 2 };
+
+template <typename QT, int KF, int VF, int D, int BS>
 struct MfmaDecode {
+  static constexpr bool KF8 = KF != kFmtQ, VF8 = VF != kFmtQ;   // one byte per element
+  static constexpr bool kBlockScales = KF == kFmtI8;             // K and V int8 together
   static constexpr int NC = D / 32;             // QK MFMAs per 16-token tile
   static constexpr int DPL = D / 16;            // value dims per lane = PV MFMAs per step
   static constexpr int KEB = KF8 ? 1 : 2, VEB = VF8 ? 1 : 2;
@@ -183,6 +190,7 @@ struct MfmaDecode {
   struct Buf {
     u32x4 k[2][KL];
     uint32_t v[2][4][VW];
+    float ks[2], vs[2];   // int8: scales of the blocks of this lane's score rows (per tile)
   };
 
   // Block ids of step j, read with scalar loads (constant address space:
@@ -223,6 +231,17 @@ struct MfmaDecode {
         const int64_t tile = (((int64_t)id.b[tau] * p.num_kv_heads + kvh) * BS + row0) * D;  // elements
         krow = tile + (int64_t)c16 * D;
         vrow = tile + (int64_t)(4 * G) * D;
+      }
+      if constexpr (kBlockScales) {
+        // the lane's score rows (tokens 4 G .. 4 G + 3 of the tile) lie in
+        // block id.b[tau], or, for 8-token blocks, in half G / 2 of the tile
+        const int b0 = BS < 16 ? id.b[2 * tau] : id.b[tau];
+        const int b1 = BS < 16 ? id.b[2 * tau + 1] : id.b[tau];
+        const cscale_ptr ksp = (cscale_ptr)p.k_scales, vsp = (cscale_ptr)p.v_scales;
+        const int64_t i0 = (int64_t)b0 * p.num_kv_heads + kvh, i1 = (int64_t)b1 * p.num_kv_heads + kvh;
+        const float k0 = ksp[i0], k1 = ksp[i1], v0 = vsp[i0], v1 = vsp[i1];
+        buf.ks[tau] = G < 2 ? k0 : k1;
+        buf.vs[tau] = G < 2 ? v0 : v1;
       }
       const char* kt = kpool + krow * KEB;
       if constexpr (KF8) {
@@ -276,7 +295,7 @@ struct MfmaDecode {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       u32x4 ka[NC];
-      if constexpr (KF8) {
+      if constexpr (KF == kFmtFp8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) {
           const u32x4 raw = buf.k[tau][h];
@@ -285,6 +304,15 @@ struct MfmaDecode {
           ka[2 * h + 1] = u32x4{fp8x2_to<QT>(raw.z, false), fp8x2_to<QT>(raw.z, true),
                                 fp8x2_to<QT>(raw.w, false), fp8x2_to<QT>(raw.w, true)};
         }
+      } else if constexpr (KF == kFmtI8) {
+#pragma unroll
+        for (int h = 0; h < KL; ++h) {
+          const u32x4 raw = buf.k[tau][h];
+          ka[2 * h] = u32x4{i8x2_to<QT>(raw.x, false), i8x2_to<QT>(raw.x, true),
+                            i8x2_to<QT>(raw.y, false), i8x2_to<QT>(raw.y, true)};
+          ka[2 * h + 1] = u32x4{i8x2_to<QT>(raw.z, false), i8x2_to<QT>(raw.z, true),
+                                i8x2_to<QT>(raw.w, false), i8x2_to<QT>(raw.w, true)};
+        }
       } else {
 #pragma unroll
         for (int c = 0; c < NC; ++c) ka[c] = buf.k[tau][c];
@@ -292,10 +320,12 @@ struct MfmaDecode {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) sc = Mma<QT>::mma(ka[c], qop[c], sc);
+      // int8: the block's K scale joins the logit scale
+      const float cs = kBlockScales ? qk_scale_log2 * buf.ks[tau] : qk_scale_log2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rel = rel0 + 16 * tau + 4 * G + i;
-        s[tau][i] = (rel < len) ? mul_rn(sc[i], qk_scale_log2) : -INFINITY;
+        s[tau][i] = (rel < len) ? mul_rn(sc[i], cs) : -INFINITY;
       }
     }
     float smax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -323,7 +353,8 @@ struct MfmaDecode {
         const float a = __builtin_amdgcn_exp2f(s[tau][i] - st.m);
         const float b = __builtin_amdgcn_exp2f(s[tau][i + 1] - st.m);
         const uint32_t w = pack2<QT>(a, b);
-        pw[tau * 2 + i / 2] = w;
+        // int8: the value operand carries the block's V scale; the sum does not
+        pw[tau * 2 + i / 2] = kBlockScales ? pack2<QT>(a * buf.vs[tau], b * buf.vs[tau]) : w;
         // sum the rounded probabilities so that the weights stay normalised
         psum += lo_f32<QT>(w) + hi_f32<QT>(w);
       }
@@ -347,8 +378,12 @@ struct MfmaDecode {
           const uint32_t tc = (k & 1) ? perm(r3, r2, 0x07030501u) : perm(r3, r2, 0x06020400u);
           x[tau] = (k & 2) ? perm(tc, ta, 0x07060302u) : perm(tc, ta, 0x05040100u);
         }
-        a = u32x4{fp8x2_to<QT>(x[0], false), fp8x2_to<QT>(x[0], true),
-                  fp8x2_to<QT>(x[1], false), fp8x2_to<QT>(x[1], true)};
+        if constexpr (VF == kFmtI8)
+          a = u32x4{i8x2_to<QT>(x[0], false), i8x2_to<QT>(x[0], true),
+                    i8x2_to<QT>(x[1], false), i8x2_to<QT>(x[1], true)};
+        else
+          a = u32x4{fp8x2_to<QT>(x[0], false), fp8x2_to<QT>(x[0], true),
+                    fp8x2_to<QT>(x[1], false), fp8x2_to<QT>(x[1], true)};
       } else {
         const int w = n >> 1;
         const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
@@ -753,13 +788,13 @@ hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename QT, bool KF8, bool VF8, int D>
+template <typename QT, int KF, int VF, int D>
 hipError_t launch_mfma_bs(const DecodeParams& p, hipStream_t s) {
   switch (p.block_size) {
-    case 8: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 8>, QT>(p, s);
-    case 16: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 16>, QT>(p, s);
-    case 32: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 32>, QT>(p, s);
-    default: return launch_persistent<MfmaDecode<QT, KF8, VF8, D, 64>, QT>(p, s);
+    case 8: return launch_persistent<MfmaDecode<QT, KF, VF, D, 8>, QT>(p, s);
+    case 16: return launch_persistent<MfmaDecode<QT, KF, VF, D, 16>, QT>(p, s);
+    case 32: return launch_persistent<MfmaDecode<QT, KF, VF, D, 32>, QT>(p, s);
+    default: return launch_persistent<MfmaDecode<QT, KF, VF, D, 64>, QT>(p, s);
   }
 }
 
@@ -773,18 +808,19 @@ hipError_t launch_f32_bs(const DecodeParams& p, hipStream_t s) {
   }
 }
 
-template <typename QT, bool KF8, bool VF8>
+template <typename QT, int KF, int VF>
 hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
-  if (p.head_dim == 128) return launch_mfma_bs<QT, KF8, VF8, 128>(p, s);
-  return launch_mfma_bs<QT, KF8, VF8, 64>(p, s);
+  if (p.head_dim == 128) return launch_mfma_bs<QT, KF, VF, 128>(p, s);
+  return launch_mfma_bs<QT, KF, VF, 64>(p, s);
 }
 
 template <typename QT>
 hipError_t launch_mfma_formats(const DecodeParams& p, hipStream_t s) {
+  if (p.cache_dtype == kI8) return launch_mfma<QT, kFmtI8, kFmtI8>(p, s);
   const bool kf8 = p.cache_dtype == kFP8, vf8 = p.v_cache_dtype == kFP8;
-  if (kf8 && vf8) return launch_mfma<QT, true, true>(p, s);
-  if (kf8) return launch_mfma<QT, true, false>(p, s);
-  return launch_mfma<QT, false, false>(p, s);
+  if (kf8 && vf8) return launch_mfma<QT, kFmtFp8, kFmtFp8>(p, s);
+  if (kf8) return launch_mfma<QT, kFmtFp8, kFmtQ>(p, s);
+  return launch_mfma<QT, kFmtQ, kFmtQ>(p, s);
 }
 
 }  // namespace

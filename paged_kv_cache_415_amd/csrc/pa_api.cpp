@@ -40,6 +40,7 @@ int elem_bytes(int dt) {
     case PA_DTYPE_F16: return 2;
     case PA_DTYPE_BF16: return 2;
     case PA_DTYPE_FP8_E4M3: return 1;
+    case PA_DTYPE_INT8: return 1;
     default: return 0;
   }
 }
@@ -64,10 +65,11 @@ pa_status check_attention_shape(int num_q_heads, int num_kv_heads, int head_dim,
     return fail(PA_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64)", block_size);
   if (elem_bytes(q_dtype) == 0 || elem_bytes(cache_dtype) == 0 || elem_bytes(v_cache_dtype) == 0)
     return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
-  const bool same = q_dtype == cache_dtype && q_dtype != PA_DTYPE_FP8_E4M3;
-  const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3 &&
-                   (q_dtype == PA_DTYPE_BF16 || q_dtype == PA_DTYPE_F16);
-  if (!same && !fp8) return fail(PA_ERR_UNSUPPORTED, "unsupported (q, cache) dtype pair");
+  const bool q16 = q_dtype == PA_DTYPE_BF16 || q_dtype == PA_DTYPE_F16;
+  const bool same = q_dtype == cache_dtype && q_dtype != PA_DTYPE_FP8_E4M3 && q_dtype != PA_DTYPE_INT8;
+  const bool fp8 = cache_dtype == PA_DTYPE_FP8_E4M3 && q16;
+  const bool i8 = cache_dtype == PA_DTYPE_INT8 && q16;
+  if (!same && !fp8 && !i8) return fail(PA_ERR_UNSUPPORTED, "unsupported (q, cache) dtype pair");
   // V: the K format, or (beside an fp8 K pool) the query type
   if (v_cache_dtype != cache_dtype && !(fp8 && v_cache_dtype == q_dtype))
     return fail(PA_ERR_UNSUPPORTED, "unsupported (K cache, V cache) dtype pair");
@@ -155,7 +157,8 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
                       int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
                       pa_dtype v_cache_dtype, float k_scale, float v_scale,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, const float* k_scales = nullptr,
+                      const float* v_scales = nullptr) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
@@ -163,6 +166,12 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   if (st != PA_OK) return st;
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_INVALID_ARG, "scale, k_scale and v_scale must be finite");
+  if (cache_dtype == PA_DTYPE_INT8) {
+    if (!k_scales || !v_scales)
+      return fail(PA_ERR_INVALID_ARG, "an int8 cache needs its per-block scales (pa_decode_int8)");
+    if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
+      return fail(PA_ERR_INVALID_ARG, "misaligned per-block scales");
+  }
   Plan plan;
   st = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                    max_seq_len, partition_size, &plan);
@@ -213,6 +222,8 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   p.q_dtype = q_dtype;
   p.cache_dtype = cache_dtype;
   p.v_cache_dtype = v_cache_dtype;
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stage != Stage::kReduce) {
     hipError_t e = pa::launch_decode_attention(p, s);
@@ -237,12 +248,13 @@ pa_status report(pa_status code, const char* message) {
 
 extern "C" {
 
-pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_pool, void* v_pool,
-                                  const int64_t* slot_mapping, int32_t num_tokens,
-                                  int64_t key_token_stride, int64_t value_token_stride,
-                                  int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t block_size, pa_dtype src_dtype, pa_dtype k_cache_dtype,
-                                  pa_dtype v_cache_dtype, float k_scale, float v_scale, void* stream) {
+static pa_status scatter_impl(const void* key, const void* value, void* k_pool, void* v_pool,
+                              const int64_t* slot_mapping, int32_t num_tokens,
+                              int64_t key_token_stride, int64_t value_token_stride,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, pa_dtype src_dtype, pa_dtype k_cache_dtype,
+                              pa_dtype v_cache_dtype, float k_scale, float v_scale, void* stream,
+                              const float* k_scales, const float* v_scales) {
   const pa_dtype cache_dtype = k_cache_dtype;
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || block_size <= 0)
     return fail(PA_ERR_INVALID_ARG, "negative size or non-positive heads/block_size");
@@ -253,9 +265,15 @@ pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_po
   const int seb = elem_bytes(src_dtype), ceb = elem_bytes(cache_dtype);
   if (seb == 0 || ceb == 0 || elem_bytes(v_cache_dtype) == 0)
     return fail(PA_ERR_INVALID_ARG, "unknown dtype code");
+  if (src_dtype == PA_DTYPE_INT8) return fail(PA_ERR_UNSUPPORTED, "int8 is not a source type");
   const bool same = src_dtype == cache_dtype;
   const bool quant = cache_dtype == PA_DTYPE_FP8_E4M3 && src_dtype != PA_DTYPE_FP8_E4M3;
-  if (!same && !quant) return fail(PA_ERR_UNSUPPORTED, "unsupported (src, cache) dtype pair");
+  const bool i8 = cache_dtype == PA_DTYPE_INT8 && src_dtype != PA_DTYPE_FP8_E4M3;
+  if (!same && !quant && !i8) return fail(PA_ERR_UNSUPPORTED, "unsupported (src, cache) dtype pair");
+  if (i8 && (!k_scales || !v_scales))
+    return fail(PA_ERR_INVALID_ARG, "an int8 cache needs its per-block scales (pa_reshape_and_cache_int8)");
+  if (i8 && (!aligned(k_scales, 4) || !aligned(v_scales, 4)))
+    return fail(PA_ERR_INVALID_ARG, "misaligned per-block scales");
   // V: the K format, or (beside an fp8 K pool) the source type
   if (v_cache_dtype != cache_dtype && !(quant && v_cache_dtype == src_dtype))
     return fail(PA_ERR_UNSUPPORTED, "unsupported (K cache, V cache) dtype pair");
@@ -292,7 +310,31 @@ pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_po
   p.src_elem_bytes = seb;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
   return hip_status(pa::launch_scatter(p, static_cast<hipStream_t>(stream)), "scatter launch");
+}
+
+pa_status pa_reshape_and_cache_kv(const void* key, const void* value, void* k_pool, void* v_pool,
+                                  const int64_t* slot_mapping, int32_t num_tokens,
+                                  int64_t key_token_stride, int64_t value_token_stride,
+                                  int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, pa_dtype src_dtype, pa_dtype k_cache_dtype,
+                                  pa_dtype v_cache_dtype, float k_scale, float v_scale, void* stream) {
+  return scatter_impl(key, value, k_pool, v_pool, slot_mapping, num_tokens, key_token_stride,
+                      value_token_stride, num_blocks, num_kv_heads, head_dim, block_size, src_dtype,
+                      k_cache_dtype, v_cache_dtype, k_scale, v_scale, stream, nullptr, nullptr);
+}
+
+pa_status pa_reshape_and_cache_int8(const void* key, const void* value, void* k_pool, void* v_pool,
+                                    const float* k_scales, const float* v_scales,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    int64_t key_token_stride, int64_t value_token_stride,
+                                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, pa_dtype src_dtype, void* stream) {
+  return scatter_impl(key, value, k_pool, v_pool, slot_mapping, num_tokens, key_token_stride,
+                      value_token_stride, num_blocks, num_kv_heads, head_dim, block_size, src_dtype,
+                      PA_DTYPE_INT8, PA_DTYPE_INT8, 1.0f, 1.0f, stream, k_scales, v_scales);
 }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
@@ -514,6 +556,23 @@ pa_status pa_decode_reduce_kv(void* out, const void* q, const void* k_pool, cons
                      max_blocks_per_seq, max_seq_len, q_dtype, k_cache_dtype, v_cache_dtype,
                      k_scale, v_scale, partition_size, workspace, workspace_bytes, stream);
 }
+
+#define PA_DECODE_INT8(NAME, STAGE)                                                           \
+  pa_status NAME(void* out, const void* q, const void* k_pool, const void* v_pool,              \
+                 const float* k_scales, const float* v_scales, const int32_t* block_tables,      \
+                 const int32_t* seq_lens, float scale, int32_t block_size, int32_t num_seqs,     \
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,                    \
+                 int32_t max_blocks_per_seq, int32_t max_seq_len, pa_dtype q_dtype,              \
+                 int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) { \
+    return decode_impl(STAGE, out, q, k_pool, v_pool, block_tables, seq_lens, scale, block_size, \
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,       \
+                       max_seq_len, q_dtype, PA_DTYPE_INT8, PA_DTYPE_INT8, 1.0f, 1.0f,          \
+                       partition_size, workspace, workspace_bytes, stream, k_scales, v_scales); \
+  }
+PA_DECODE_INT8(pa_decode_int8, Stage::kBoth)
+PA_DECODE_INT8(pa_decode_attention_int8, Stage::kAttention)
+PA_DECODE_INT8(pa_decode_reduce_int8, Stage::kReduce)
+#undef PA_DECODE_INT8
 
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
                            const void* k_pool, const void* v_pool, const int32_t* block_tables,

@@ -90,6 +90,24 @@ __device__ __forceinline__ uint32_t fp8x2_to<_Float16>(uint32_t w, bool hi) {
             : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
 }
 
+// ----------------------------------------------------- int8 codes
+
+// Two int8 codes (bytes 0,1 of `w` when hi == false, bytes 2,3 when true)
+// -> packed pair of 16-bit values of type T, exactly (|code| <= 127 fits the
+// 8 significant bits of bf16).
+template <typename T>
+__device__ __forceinline__ uint32_t i8x2_to(uint32_t w, bool hi) {
+  const int s = hi ? 16 : 0;
+  return pack2<T>((float)(int)(int8_t)(w >> s), (float)(int)(int8_t)(w >> (s + 8)));
+}
+
+// float32 -> symmetric int8 code under a positive scale: round half to even
+// of one correctly rounded float32 division, clamped to [-127, 127]; NaN -> 0.
+__device__ __forceinline__ int i8_encode(float x, float scale) {
+  const float q = __builtin_rintf(x / scale);
+  return q != q ? 0 : (int)fminf(fmaxf(q, -127.f), 127.f);
+}
+
 // ----------------------------------------------------- fp8 E4M3 encoding
 
 // float32 -> OCP E4M3FN code, written from the format definition (1 sign,

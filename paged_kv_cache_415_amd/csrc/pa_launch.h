@@ -8,7 +8,7 @@
 namespace pa {
 
 // Element-type codes; numerically equal to the public pa_dtype values.
-enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3, kI8 = 4 };
 
 constexpr int kProbeBlocks = 2048;
 
@@ -30,6 +30,8 @@ struct ScatterParams {
   int src_elem_bytes;
   float k_scale;
   float v_scale;
+  const float* k_scales;   // int8 cache: [num_blocks][num_kv_heads] per-block scales
+  const float* v_scales;
 };
 
 struct CopyParams {
@@ -108,6 +110,8 @@ struct DecodeParams {
   int q_dtype;
   int cache_dtype;     // K pool element type
   int v_cache_dtype;   // V pool element type (the same, or QT beside an fp8 K pool)
+  const float* k_scales;   // int8 cache: [num_blocks][num_kv_heads] per-block scales
+  const float* v_scales;
 };
 
 struct PrefillParams {

@@ -51,6 +51,10 @@ class DecodeRun:
         self.k_pool = up(case.k_pool, s.cache_dtype)
         self.v_pool = up(case.v_pool, s.v_dtype)
         self.mixed = s.v_dtype != s.cache_dtype
+        self.int8 = s.cache_dtype == "int8"
+        if self.int8:
+            self.k_scales = torch.from_numpy(case.k_block_scales).to(dev())
+            self.v_scales = torch.from_numpy(case.v_block_scales).to(dev())
         self.new_k = up(case.new_k, case.src_dtype)
         self.new_v = up(case.new_v, case.src_dtype)
         self.tables = up_int(case.block_tables)
@@ -60,6 +64,10 @@ class DecodeRun:
 
     def scatter(self):
         pa = lib()
+        if self.int8:
+            pa.pa_reshape_and_cache_int8(self.new_k, self.new_v, self.k_pool, self.v_pool,
+                                         self.k_scales, self.v_scales, self.slots)
+            return
         fn = pa.pa_reshape_and_cache_kv if self.mixed else pa.pa_reshape_and_cache
         fn(self.new_k, self.new_v, self.k_pool, self.v_pool, self.slots, self.case.k_scale,
            self.case.v_scale)
@@ -73,7 +81,15 @@ class DecodeRun:
         out = torch.empty_like(self.q)
         args = (out, self.q, self.k_pool, self.v_pool, self.tables, self.lens, s.scale, msl,
                 self.case.k_scale, self.case.v_scale, ps, ws)
-        if self.mixed:
+        if self.int8:
+            a8 = (out, self.q, self.k_pool, self.v_pool, self.k_scales, self.v_scales, self.tables,
+                  self.lens, s.scale, msl, ps, ws)
+            if stages:
+                pa.pa_decode_attention_int8(*a8)
+                pa.pa_decode_reduce_int8(*a8)
+            else:
+                pa.pa_decode_int8(*a8)
+        elif self.mixed:
             if stages:
                 pa.pa_decode_attention_kv(*args)
                 pa.pa_decode_reduce_kv(*args)
@@ -93,10 +109,14 @@ def oracle_step(case: W.DecodeCase):
     s = case.spec
     kp, vp = oracle.reshape_and_cache(case.k_pool, case.v_pool, s.cache_dtype, case.new_k,
                                       case.new_v, case.src_dtype, case.slot_mapping, s.block_size,
-                                      case.k_scale, case.v_scale, v_cache_dtype=s.v_dtype)
+                                      case.k_scale, case.v_scale, v_cache_dtype=s.v_dtype,
+                                      k_block_scales=case.k_block_scales,
+                                      v_block_scales=case.v_block_scales)
     out = oracle.decode_attention(case.q, s.q_dtype, kp, vp, s.cache_dtype, case.block_tables,
                                   case.seq_lens, s.scale, s.block_size, s.num_kv_heads,
-                                  case.k_scale, case.v_scale, v_cache_dtype=s.v_dtype)
+                                  case.k_scale, case.v_scale, v_cache_dtype=s.v_dtype,
+                                  k_block_scales=case.k_block_scales,
+                                  v_block_scales=case.v_block_scales)
     return out, kp, vp
 
 

@@ -172,6 +172,37 @@ def test_scatter_kv_checks_the_format_pair(lib, src, kdt, vdt, code):
     assert st == code
 
 
+INT8 = 4
+
+
+def test_int8_cache_needs_its_scales(lib):
+    # the plain calls have no per-block scales to read
+    assert _decode(lib, cdt=INT8) == INVALID
+    assert b"per-block scales" in lib.pa_last_error()
+    st = lib.pa_reshape_and_cache(None, None, None, None, None, 5, 0, 0, 4, 2, 128, 16, BF16, INT8,
+                                  1.0, 1.0, None)
+    assert st == INVALID
+    # the int8 calls check the query type and the shapes before anything else
+    fake = ctypes.c_void_p(256)
+    args = [None] * 8 + [0.1, 16, 4, 8, 2, 128, 8, 128]
+    assert lib.pa_decode_int8(*args, F32, 0, None, 0, None) == UNSUPPORTED
+    assert lib.pa_decode_int8(*args, BF16, 0, None, 0, None) == INVALID          # null pointers
+    assert lib.pa_decode_int8(*([None] * 8 + [0.1, 16, 0, 8, 2, 128, 8, 128]), BF16, 0, None, 0,
+                              None) == INVALID                                   # no scales
+    assert lib.pa_decode_int8(*([fake] * 8 + [0.1, 16, 0, 8, 2, 96, 8, 128]), BF16, 0, None, 0,
+                              None) == UNSUPPORTED                               # head_dim 96
+    assert lib.pa_reshape_and_cache_int8(None, None, None, None, None, None, None, 0, 0, 0, 4, 2,
+                                         128, 16, BF16, None) == INVALID         # no scales
+    assert lib.pa_reshape_and_cache_int8(None, None, None, None, fake, fake, None, 0, 0, 0, 4, 2,
+                                         128, 16, BF16, None) == OK              # nothing to do
+    assert lib.pa_reshape_and_cache_int8(None, None, None, None, fake, fake, None, 0, 0, 0, 4, 2,
+                                         128, 16, INT8, None) == UNSUPPORTED     # int8 source
+    # prefill reads 16-bit caches only
+    st = lib.pa_prefill_chunk(None, None, None, None, None, None, None, 0.1, 16, 1, 4, 4, 8, 2, 128,
+                              8, BF16, INT8, 1.0, 1.0, None)
+    assert st == UNSUPPORTED
+
+
 def test_scatter_and_copy_empty_are_ok(lib):
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 0, 0, 4, 2, 128, 16, BF16,
                                     BF16, 1.0, 1.0, None) == OK

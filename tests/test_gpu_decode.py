@@ -16,7 +16,7 @@ from gpu_cases import TOL, DecodeRun, as_f64, custom_spec, lib, max_abs, oracle_
 pytestmark = pytest.mark.gpu
 
 FULL_CONFIGS = ["tiny_f32", "llama2_7b_mha_f16", "llama3_8b_gqa_bf16", "llama3_70b_fp8kv",
-                "llama3_8b_kfp8_vbf16"]
+                "llama3_8b_kfp8_vbf16", "llama3_8b_int8kv"]
 
 
 @pytest.fixture(scope="module")
@@ -232,6 +232,58 @@ def test_mixed_length_one_returns_its_value_row():
     out = run.decode()
     exp = torch.from_numpy(ref).to(out.dtype)
     assert torch.equal(out.cpu().view(torch.int16), exp.view(torch.int16))
+
+
+INT8 = [
+    # int8 K and V with per-(block, KV head) scales: (q, Hq, Hkv, D, bs)
+    ("bf16", 8, 8, 128, 16),
+    ("bf16", 32, 8, 128, 32),
+    ("f16", 12, 3, 128, 16),
+    ("bf16", 8, 1, 64, 16),
+    ("f16", 4, 4, 64, 32),
+    ("bf16", 16, 2, 128, 8),
+    ("bf16", 8, 8, 64, 64),
+]
+
+
+@pytest.mark.parametrize("q_dt,hq,hkv,d,bs", INT8)
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_int8_per_block_scales_sweep(q_dt, hq, hkv, d, bs, partition):
+    """ybb.press §6.2 (INT8 KV cache), per-(block, KV head) scales: scatter byte-exact, decode
+    within the bar, staged == single call bitwise."""
+    if partition > 0 and partition % bs:
+        pytest.skip("partition must be a multiple of block_size")
+    spec = custom_spec(f"int8_{q_dt}_{hq}_{hkv}_{d}_{bs}", hq, hkv, d, bs, q_dt, "int8")
+    case = W.make_decode_case(spec, lens=LENS)
+    ref, okp, ovp = oracle_step(case)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(run.k_pool, "int8"), okp)
+    assert np.array_equal(W.torch_to_bits(run.v_pool, "int8"), ovp)
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL[q_dt]
+    if partition == 64:
+        staged = run.decode(partition_size=partition, stages=True)
+        assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+
+
+def test_int8_every_code_decodes_exactly():
+    """Length-1 sequences (p = 1) whose value rows hold every code -127..127, scale 1."""
+    spec = custom_spec("int8_codes", 1, 1, 128, 16, "bf16", "int8")
+    case = W.make_decode_case(spec, lens=[1, 1])
+    codes = np.r_[np.arange(-127, 128), np.zeros(1)].astype(np.int8)        # 256 entries
+    for s in range(2):
+        blk = case.block_tables[s, 0]
+        case.v_pool[blk, 0, 0, :] = codes[s * 128:(s + 1) * 128].view(np.uint8)
+        case.k_pool[blk, 0, 0, :] = 0
+        case.k_block_scales[blk, 0] = case.v_block_scales[blk, 0] = 1.0
+    case.slot_mapping[:] = -1
+    run = DecodeRun(case)
+    run.scatter()
+    out = as_f64(run.decode())
+    want = codes.astype(np.float64).reshape(2, 1, 128)
+    assert np.array_equal(out, want)
 
 
 def _rewrite_k_dim0(case, values_per_seq, k_scale=None):

@@ -28,12 +28,16 @@ import math
 import numpy as np
 import torch
 
-BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
-NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}
+BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8,
+              "int8": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "int8": 1}
+# int8 has no NaN: unwritten slots hold -128, a code the quantiser never writes
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F, "int8": 0x80}
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "fp8_e4m3": torch.float8_e4m3fn}
-TORCH_BITS = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "fp8_e4m3": torch.uint8}
+               "fp8_e4m3": torch.float8_e4m3fn, "int8": torch.int8}
+TORCH_BITS = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16, "fp8_e4m3": torch.uint8,
+              "int8": torch.int8}
+INT8_MAX = 127.0
 FP8_MAX = 448.0
 
 
@@ -197,6 +201,13 @@ DECODE_SPECS = {
         description="70B-shaped layer on one GPU: 128 sequences, 64/8 heads, head_dim 128, block 16, "
                     "lens lognormal(median 1500, sigma 0.8) in [16,8192], fp8 e4m3 KV with "
                     "per-tensor scales, bf16 q, 512-token split-KV partitions"),
+    "llama3_8b_int8kv": DecodeSpec(
+        "llama3_8b_int8kv", 256, 32, 8, 128, 16, "bf16", "int8",
+        ("lognormal", 1200.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
+        description="Llama-3-8B-shaped GQA layer with an INT8 KV cache (one float32 scale per "
+                    "block and KV head for K and for V, amax/127), bf16 q: batch 256, 32/8 heads, "
+                    "head_dim 128, block 16, lens lognormal(median 1200, sigma 0.8) in [16,8192], "
+                    "pool 1.1x"),
     "llama3_8b_kfp8_vbf16": DecodeSpec(
         "llama3_8b_kfp8_vbf16", 256, 32, 8, 128, 16, "bf16", "fp8_e4m3",
         ("lognormal", 1200.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
@@ -244,6 +255,8 @@ class DecodeCase:
     k_scale: float
     v_scale: float
     poison_block: int
+    k_block_scales: np.ndarray | None = None   # int8 cache: float32 [NB][Hkv]
+    v_block_scales: np.ndarray | None = None
     extra: dict = field(default_factory=dict)
 
     @property
@@ -349,15 +362,37 @@ def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None 
         if v_dt == "fp8_e4m3":
             v_scale = float(np.float32(amax(v_vals, new_v) / FP8_MAX))
 
+    k_bsc = v_bsc = None
+    if cache_dt == "int8":
+        # one scale per (block, KV head): the amax of the block's tokens, the
+        # newest (as its source-type value) included, over 127
+        def block_scales(vals, new_bits):
+            sc = np.ones((nb, H), np.float32)
+            newf = bits_to_torch(new_bits, src_dt).float().numpy()
+            for q, n in enumerate(seq_lens):
+                n = int(n)
+                v = vals[q].copy()
+                v[(n - 1) // bs, :, (n - 1) % bs, :] = newf[q]
+                flat = v.transpose(1, 0, 2, 3).reshape(H, -1, D)
+                flat[:, n:, :] = 0
+                per = np.abs(flat.reshape(H, -1, bs, D)).max(axis=(2, 3)).T        # [nblk][H]
+                sc[np.asarray(tables[q])] = np.where(per > 0, per / np.float32(INT8_MAX), 1.0)
+            return sc.astype(np.float32)
+        k_bsc, v_bsc = block_scales(k_vals, new_k), block_scales(v_vals, new_v)
+
     k_pool = np.full((nb, H, bs, D), NAN_BITS[cache_dt], dtype=BITS_DTYPE[cache_dt])
     v_pool = np.full((nb, H, bs, D), NAN_BITS[v_dt], dtype=BITS_DTYPE[v_dt])
     for s, n in enumerate(seq_lens):
         n = int(n)
         ids = np.asarray(tables[s], dtype=np.int64)
-        for vals, pool, sc, dt in ((k_vals[s], k_pool, k_scale, cache_dt),
-                                   (v_vals[s], v_pool, v_scale, v_dt)):
+        for vals, pool, sc, dt, bsc in ((k_vals[s], k_pool, k_scale, cache_dt, k_bsc),
+                                        (v_vals[s], v_pool, v_scale, v_dt, v_bsc)):
             nan = NAN_BITS[dt]
-            stored = to_bits(vals / np.float32(sc) if dt == "fp8_e4m3" else vals, dt)
+            if dt == "int8":      # torch.round: half to even
+                q8 = torch.from_numpy(vals / bsc[ids][:, :, None, None]).round().clamp(-127, 127)
+                stored = q8.to(torch.int8).numpy().view(np.uint8).copy()
+            else:
+                stored = to_bits(vals / np.float32(sc) if dt == "fp8_e4m3" else vals, dt)
             # poison every slot from the newest token on (the newest is written by the scatter)
             flat = stored.transpose(1, 0, 2, 3).reshape(H, -1, D)
             flat[:, n - 1:, :] = nan
@@ -367,7 +402,8 @@ def make_decode_case(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | None 
     return DecodeCase(spec=spec, q=to_bits(q_vals, q_dt), k_pool=k_pool, v_pool=v_pool,
                       block_tables=block_tables, seq_lens=seq_lens.astype(np.int32),
                       new_k=new_k, new_v=new_v, src_dtype=src_dt, slot_mapping=slot_mapping,
-                      k_scale=k_scale, v_scale=v_scale, poison_block=poison_block)
+                      k_scale=k_scale, v_scale=v_scale, poison_block=poison_block,
+                      k_block_scales=k_bsc, v_block_scales=v_bsc)
 
 
 # ---------------------------------------------------------------------------
@@ -526,6 +562,12 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
 # ---------------------------------------------------------------------------
 # Byte accounting used by the benchmark
 # ---------------------------------------------------------------------------
+
+def block_scale_bytes(seq_lens, num_kv_heads: int, block_size: int) -> int:
+    """Bytes of the per-block K and V scales an int8 decode step reads (float32 each)."""
+    nblk = sum(blocks_for(int(n), block_size) for n in np.asarray(seq_lens).ravel())
+    return nblk * num_kv_heads * 2 * 4
+
 
 def effective_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int, cache_dtype: str,
                        v_cache_dtype: str | None = None) -> int:
