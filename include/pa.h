@@ -371,6 +371,42 @@ pa_status pa_decode_reduce_int8(void* out, const void* q, const void* k_pool, co
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append — pa_reshape_and_cache of each sequence's newest token
+ * followed by pa_decode, in one kernel ([datawhale] Step 4: a decode step
+ * stores the new token's K/V in its block, then attends over the table).
+ * Sequence s with n = seq_lens[s] > 0 has its newest token at position
+ * n - 1; its slot is block_tables[s][(n - 1) / block_size] * block_size +
+ * (n - 1) % block_size.  The call's result equals
+ *   pa_reshape_and_cache(new_k, new_v, ..., slot_mapping = those slots)
+ *   pa_decode(...)
+ * on one stream, bit for bit: the attention reads the newest rows from
+ * new_k / new_v, and the wave that covers them writes them into the pool.
+ *   new_k, new_v  [num_seqs][num_kv_heads][head_dim] in the cache type; row
+ *                 s starts at s * new_*_stride elements (0 = dense)
+ * Requirements: q_dtype == cache_dtype, bf16 or f16; seq_lens[s] <=
+ * max_seq_len (when max_seq_len > 0) so that no length is clamped; n <= 0
+ * appends nothing.  pa_decode_attention_append is the first stage
+ * (pa_decode_reduce with the same pools, tables and workspace completes it).
+ */
+pa_status pa_decode_append(void* out, const void* q, const void* new_k, const void* new_v,
+                           int64_t new_k_stride, int64_t new_v_stride, void* k_pool, void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                           int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,
+                           float v_scale, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream);
+pa_status pa_decode_attention_append(void* out, const void* q, const void* new_k, const void* new_v,
+                                     int64_t new_k_stride, int64_t new_v_stride, void* k_pool,
+                                     void* v_pool, const int32_t* block_tables,
+                                     const int32_t* seq_lens, float scale, int32_t block_size,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_blocks_per_seq,
+                                     int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                                     float k_scale, float v_scale, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_chunk — causal attention of one prefill chunk per sequence
  * over its paged context.
  *

@@ -77,6 +77,11 @@ def _load() -> ctypes.CDLL:
     lib.pa_reshape_and_cache_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32,
                                               i32, i32, vp]
     lib.pa_reshape_and_cache_int8.restype = i32
+    app = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+           f32, f32, i32, vp, sz, vp]
+    for name in ("pa_decode_append", "pa_decode_attention_append"):
+        getattr(lib, name).argtypes = app
+        getattr(lib, name).restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, f32, vp]
     lib.pa_status_string.argtypes = [i32]
@@ -381,6 +386,43 @@ def pa_decode_reduce_kv(out, q, k_pool, v_pool, block_tables, seq_lens, scale: f
                  scale, max_seq_len, k_scale, v_scale, partition_size, workspace, stream, mixed=True)
 
 
+def _append_call(fn, out, q, new_k, new_v, k_pool, v_pool, block_tables, seq_lens, scale,
+                 max_seq_len, k_scale, v_scale, partition_size, workspace, stream):
+    s, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    for x in (new_k, new_v):
+        if x.dim() != 3 or tuple(x.shape) != (s, hkv, d) or x.stride(2) != 1 or x.stride(1) != d:
+            raise ValueError("new_k/new_v must be [num_seqs][num_kv_heads][head_dim] with dense rows")
+    if _dtype(v_pool) != _dtype(k_pool):
+        raise ValueError("K and V pools must have one type")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(_ptr(out), _ptr(q), _ptr(new_k, False), _ptr(new_v, False),
+              new_k.stride(0) if s > 0 else 0, new_v.stride(0) if s > 0 else 0, _ptr(k_pool),
+              _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), float(scale), bs, s, hq, hkv, d,
+              block_tables.shape[1], int(max_seq_len), _dtype(q), _dtype(k_pool), float(k_scale),
+              float(v_scale), int(partition_size), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def pa_decode_append(out, q, new_k, new_v, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                     max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                     partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Scatter of each sequence's newest token plus decode, in one kernel (see pa.h)."""
+    _append_call(_lib.pa_decode_append, out, q, new_k, new_v, k_pool, v_pool, block_tables,
+                 seq_lens, scale, max_seq_len, k_scale, v_scale, partition_size, workspace, stream)
+
+
+def pa_decode_attention_append(out, q, new_k, new_v, k_pool, v_pool, block_tables, seq_lens,
+                               scale: float, max_seq_len: int = 0, k_scale: float = 1.0,
+                               v_scale: float = 1.0, partition_size: int = 0, workspace=None,
+                               stream=None) -> None:
+    """First stage of pa_decode_append (pa_decode_reduce completes it)."""
+    _append_call(_lib.pa_decode_attention_append, out, q, new_k, new_v, k_pool, v_pool,
+                 block_tables, seq_lens, scale, max_seq_len, k_scale, v_scale, partition_size,
+                 workspace, stream)
+
+
 def pa_decode_attention(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
                         max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
                         partition_size: int = 0, workspace=None, stream=None) -> None:
@@ -424,7 +466,7 @@ def pa_probe_copy(dst, src, stream=None) -> None:
 __all__ = [
     "pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_decode_kv", "pa_decode_attention_kv",
     "pa_decode_reduce_kv", "pa_reshape_and_cache_int8", "pa_decode_int8", "pa_decode_attention_int8",
-    "pa_decode_reduce_int8", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
+    "pa_decode_reduce_int8", "pa_decode_append", "pa_decode_attention_append", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
     "layer_pool_pointers",
     "pa_swap_blocks", "pa_decode", "pa_decode_attention",
     "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",

@@ -174,7 +174,11 @@ struct TableWindow {
 // ---------------------------------------------------------------------------
 enum : int { kFmtQ = 0, kFmtFp8 = 1, kFmtI8 = 2 };
 
-template <typename QT, int KF, int VF, int D, int BS>
+// APPEND: the newest token of every sequence (position seq_len - 1) is read
+// from p.new_k / p.new_v instead of the pool, and the wave that covers it
+// writes it into its pool slot (the scatter folded into the decode; 16-bit
+// caches only).
+template <typename QT, int KF, int VF, int D, int BS, bool APPEND = false>
 struct MfmaDecode {
   static constexpr bool KF8 = KF != kFmtQ, VF8 = VF != kFmtQ;   // one byte per element
   static constexpr bool kBlockScales = KF == kFmtI8;             // K and V int8 together
@@ -211,9 +215,10 @@ struct MfmaDecode {
 
   // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).
   static __device__ __forceinline__ void load(Buf& buf, Ids id, const DecodeParams& p, int kvh,
-                                              int j) {
+                                              int j, int s = 0, int len = 0) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, c16 = lane & 15;
+    static_assert(!APPEND || (KF == kFmtQ && VF == kFmtQ), "append needs a 16-bit cache");
     const char* kpool = reinterpret_cast<const char*>(p.k_pool);
     const char* vpool = reinterpret_cast<const char*>(p.v_pool);
 #pragma unroll
@@ -244,6 +249,18 @@ struct MfmaDecode {
         buf.vs[tau] = G < 2 ? v0 : v1;
       }
       const char* kt = kpool + krow * KEB;
+      // APPEND: the tile holding the newest token takes that row from the input
+      const int t0 = j * kStep + 16 * tau;
+      const bool new_tile = APPEND && len - 1 >= t0 && len - 1 < t0 + 16;   // uniform
+      const char* nk = nullptr;
+      const char* nv = nullptr;
+      if constexpr (APPEND) {
+        if (new_tile) {
+          nk = reinterpret_cast<const char*>(p.new_k) + ((int64_t)s * p.new_k_stride + (int64_t)kvh * D) * 2;
+          nv = reinterpret_cast<const char*>(p.new_v) + ((int64_t)s * p.new_v_stride + (int64_t)kvh * D) * 2;
+          if (t0 + c16 == len - 1) kt = nk;
+        }
+      }
       if constexpr (KF8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16_nt(kt + 64 * h + 16 * G);
@@ -255,6 +272,9 @@ struct MfmaDecode {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const char* src = vt + (int64_t)i * D * VEB;
+        if constexpr (APPEND) {
+          if (new_tile && t0 + 4 * G + i == len - 1) src = nv + (int64_t)DPL * c16 * 2;
+        }
         if constexpr (VW == 4) {
           const u32x4 x = ld16_nt(src);
           buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y; buf.v[tau][i][2] = x.z; buf.v[tau][i][3] = x.w;
@@ -433,28 +453,44 @@ struct MfmaDecode {
     if constexpr (kDoubleBuffer) {
       Buf A, B;
       Ids nxt = ids(trow, nblk, min(j0 + 1, j1 - 1));
-      load(A, cur, p, kvh, j0);
+      load(A, cur, p, kvh, j0, s, len);
       for (int j = j0; j < j1; j += 2) {
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 2, j1 - 1));
-        if (j + 1 < j1) load(B, cur, p, kvh, j + 1);
+        if (j + 1 < j1) load(B, cur, p, kvh, j + 1, s, len);
         compute(A, st, qop, p.qk_scale_log2, len, j);
         if (j + 1 >= j1) break;
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 3, j1 - 1));
-        if (j + 2 < j1) load(A, cur, p, kvh, j + 2);
+        if (j + 2 < j1) load(A, cur, p, kvh, j + 2, s, len);
         compute(B, st, qop, p.qk_scale_log2, len, j + 1);
       }
     } else {
       for (int j = j0; j < j1; ++j) {
         const Ids nxt = ids(trow, nblk, min(j + 1, j1 - 1));
         Buf buf;
-        load(buf, cur, p, kvh, j);
+        load(buf, cur, p, kvh, j, s, len);
         compute(buf, st, qop, p.qk_scale_log2, len, j);
         cur = nxt;
       }
     }
 
+    if constexpr (APPEND) {
+      // the segment that covered the newest token stores its K and V rows in
+      // the pool slot (lanes 0-31: K, 32-63: V; D / 16 bytes each)
+      if (len > 0 && j1 == (len + kStep - 1) / kStep) {
+        const int pos = len - 1;
+        const int blk = trow[pos / BS];
+        const int64_t off = (((int64_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * D * 2;
+        const bool is_v = lane >= 32;
+        const char* src = reinterpret_cast<const char*>(is_v ? p.new_v : p.new_k) +
+                          ((int64_t)s * (is_v ? p.new_v_stride : p.new_k_stride) + (int64_t)kvh * D) * 2;
+        char* dst = reinterpret_cast<char*>(const_cast<void*>(is_v ? p.v_pool : p.k_pool)) + off;
+        const int b = (lane & 31) * (D / 16);
+        if constexpr (D == 128) *reinterpret_cast<u32x2*>(dst + b) = *reinterpret_cast<const u32x2*>(src + b);
+        else *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
+      }
+    }
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
     float l_tot = xor_sum(st.l, 16);
     l_tot = xor_sum(l_tot, 32);
@@ -788,13 +824,13 @@ hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename QT, int KF, int VF, int D>
+template <typename QT, int KF, int VF, int D, bool APPEND = false>
 hipError_t launch_mfma_bs(const DecodeParams& p, hipStream_t s) {
   switch (p.block_size) {
-    case 8: return launch_persistent<MfmaDecode<QT, KF, VF, D, 8>, QT>(p, s);
-    case 16: return launch_persistent<MfmaDecode<QT, KF, VF, D, 16>, QT>(p, s);
-    case 32: return launch_persistent<MfmaDecode<QT, KF, VF, D, 32>, QT>(p, s);
-    default: return launch_persistent<MfmaDecode<QT, KF, VF, D, 64>, QT>(p, s);
+    case 8: return launch_persistent<MfmaDecode<QT, KF, VF, D, 8, APPEND>, QT>(p, s);
+    case 16: return launch_persistent<MfmaDecode<QT, KF, VF, D, 16, APPEND>, QT>(p, s);
+    case 32: return launch_persistent<MfmaDecode<QT, KF, VF, D, 32, APPEND>, QT>(p, s);
+    default: return launch_persistent<MfmaDecode<QT, KF, VF, D, 64, APPEND>, QT>(p, s);
   }
 }
 
@@ -808,14 +844,15 @@ hipError_t launch_f32_bs(const DecodeParams& p, hipStream_t s) {
   }
 }
 
-template <typename QT, int KF, int VF>
+template <typename QT, int KF, int VF, bool APPEND = false>
 hipError_t launch_mfma(const DecodeParams& p, hipStream_t s) {
-  if (p.head_dim == 128) return launch_mfma_bs<QT, KF, VF, 128>(p, s);
-  return launch_mfma_bs<QT, KF, VF, 64>(p, s);
+  if (p.head_dim == 128) return launch_mfma_bs<QT, KF, VF, 128, APPEND>(p, s);
+  return launch_mfma_bs<QT, KF, VF, 64, APPEND>(p, s);
 }
 
 template <typename QT>
 hipError_t launch_mfma_formats(const DecodeParams& p, hipStream_t s) {
+  if (p.new_k != nullptr) return launch_mfma<QT, kFmtQ, kFmtQ, true>(p, s);
   if (p.cache_dtype == kI8) return launch_mfma<QT, kFmtI8, kFmtI8>(p, s);
   const bool kf8 = p.cache_dtype == kFP8, vf8 = p.v_cache_dtype == kFP8;
   if (kf8 && vf8) return launch_mfma<QT, kFmtFp8, kFmtFp8>(p, s);

@@ -158,7 +158,9 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
                       pa_dtype v_cache_dtype, float k_scale, float v_scale,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
                       void* stream, const float* k_scales = nullptr,
-                      const float* v_scales = nullptr) {
+                      const float* v_scales = nullptr, const void* new_k = nullptr,
+                      const void* new_v = nullptr, int64_t new_k_stride = 0,
+                      int64_t new_v_stride = 0) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
@@ -166,6 +168,20 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   if (st != PA_OK) return st;
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_INVALID_ARG, "scale, k_scale and v_scale must be finite");
+  const bool append = new_k != nullptr || new_v != nullptr;
+  if (append) {
+    if (!new_k || !new_v) return fail(PA_ERR_INVALID_ARG, "append needs both new_k and new_v");
+    if (q_dtype != cache_dtype || v_cache_dtype != cache_dtype ||
+        (q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16))
+      return fail(PA_ERR_UNSUPPORTED, "append supports bf16/f16 queries with a cache of the same type");
+    const int64_t dense = (int64_t)num_kv_heads * head_dim;
+    if (new_k_stride == 0) new_k_stride = dense;
+    if (new_v_stride == 0) new_v_stride = dense;
+    if (new_k_stride < dense || new_v_stride < dense || (new_k_stride * 2) % 16 || (new_v_stride * 2) % 16)
+      return fail(PA_ERR_INVALID_ARG, "new-token strides must be >= num_kv_heads * head_dim and keep rows 16-byte aligned");
+    if (!aligned(new_k, 16) || !aligned(new_v, 16))
+      return fail(PA_ERR_INVALID_ARG, "misaligned new-token pointer");
+  }
   if (cache_dtype == PA_DTYPE_INT8) {
     if (!k_scales || !v_scales)
       return fail(PA_ERR_INVALID_ARG, "an int8 cache needs its per-block scales (pa_decode_int8)");
@@ -224,6 +240,10 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   p.v_cache_dtype = v_cache_dtype;
   p.k_scales = k_scales;
   p.v_scales = v_scales;
+  p.new_k = append ? new_k : nullptr;
+  p.new_v = append ? new_v : nullptr;
+  p.new_k_stride = new_k_stride;
+  p.new_v_stride = new_v_stride;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stage != Stage::kReduce) {
     hipError_t e = pa::launch_decode_attention(p, s);
@@ -573,6 +593,26 @@ PA_DECODE_INT8(pa_decode_int8, Stage::kBoth)
 PA_DECODE_INT8(pa_decode_attention_int8, Stage::kAttention)
 PA_DECODE_INT8(pa_decode_reduce_int8, Stage::kReduce)
 #undef PA_DECODE_INT8
+
+#define PA_DECODE_APPEND(NAME, STAGE)                                                          \
+  pa_status NAME(void* out, const void* q, const void* new_k, const void* new_v,                \
+                 int64_t new_k_stride, int64_t new_v_stride, void* k_pool, void* v_pool,        \
+                 const int32_t* block_tables, const int32_t* seq_lens, float scale,             \
+                 int32_t block_size, int32_t num_seqs, int32_t num_q_heads,                     \
+                 int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,            \
+                 int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype, float k_scale,    \
+                 float v_scale, int32_t partition_size, void* workspace,                        \
+                 size_t workspace_bytes, void* stream) {                                        \
+    if (!new_k || !new_v) return fail(PA_ERR_INVALID_ARG, "append needs new_k and new_v");     \
+    return decode_impl(STAGE, out, q, k_pool, v_pool, block_tables, seq_lens, scale, block_size, \
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,       \
+                       max_seq_len, q_dtype, cache_dtype, cache_dtype, k_scale, v_scale,        \
+                       partition_size, workspace, workspace_bytes, stream, nullptr, nullptr,    \
+                       new_k, new_v, new_k_stride, new_v_stride);                               \
+  }
+PA_DECODE_APPEND(pa_decode_append, Stage::kBoth)
+PA_DECODE_APPEND(pa_decode_attention_append, Stage::kAttention)
+#undef PA_DECODE_APPEND
 
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
                            const void* k_pool, const void* v_pool, const int32_t* block_tables,

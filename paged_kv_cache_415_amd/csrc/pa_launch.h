@@ -112,6 +112,11 @@ struct DecodeParams {
   int v_cache_dtype;   // V pool element type (the same, or QT beside an fp8 K pool)
   const float* k_scales;   // int8 cache: [num_blocks][num_kv_heads] per-block scales
   const float* v_scales;
+  // append: each sequence's newest token [S][Hkv][D] (row s at s * stride elements)
+  const void* new_k;
+  const void* new_v;
+  int64_t new_k_stride;
+  int64_t new_v_stride;
 };
 
 struct PrefillParams {

@@ -203,6 +203,22 @@ def test_int8_cache_needs_its_scales(lib):
     assert st == UNSUPPORTED
 
 
+def test_append_checks(lib):
+    fake = ctypes.c_void_p(256)
+    base = [0.1, 16, 4, 8, 2, 128, 8, 128]
+
+    def call(qdt, cdt, nk=fake, nv=fake, ks=0, vs=0, ptrs=None):
+        p = ptrs or [None] * 6
+        return lib.pa_decode_append(p[0], p[1], nk, nv, ks, vs, p[2], p[3], p[4], p[5], *base, qdt,
+                                    cdt, 1.0, 1.0, 0, None, 0, None)
+    assert call(BF16, BF16) == INVALID                       # null pointers, format accepted
+    assert call(F32, F32) == UNSUPPORTED
+    assert call(BF16, FP8) == UNSUPPORTED
+    assert call(BF16, BF16, nk=None) == INVALID
+    assert call(BF16, BF16, ks=100) == INVALID                # stride below Hkv * D
+    assert call(BF16, BF16, ks=256 + 4) == INVALID            # rows not 16-byte aligned
+
+
 def test_scatter_and_copy_empty_are_ok(lib):
     assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 0, 0, 4, 2, 128, 16, BF16,
                                     BF16, 1.0, 1.0, None) == OK

@@ -286,6 +286,61 @@ def test_int8_every_code_decodes_exactly():
     assert np.array_equal(out, want)
 
 
+APPEND = [
+    # (q = cache, Hq, Hkv, D, bs, lens)
+    ("f16", 32, 32, 128, 16, None),            # the Llama-2-7B-shaped workload in full
+    ("bf16", 8, 2, 128, 16, LENS),
+    ("bf16", 16, 1, 128, 32, LENS),
+    ("f16", 6, 2, 64, 16, LENS),
+    ("bf16", 8, 2, 128, 8, LENS),
+    ("f16", 4, 4, 64, 64, LENS),
+]
+
+
+@pytest.mark.parametrize("q_dt,hq,hkv,d,bs,lens", APPEND)
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_append_equals_scatter_then_decode(q_dt, hq, hkv, d, bs, lens, partition):
+    """pa_decode_append == pa_reshape_and_cache + pa_decode, bit for bit (outputs and pools)."""
+    if partition > 0 and partition % bs:
+        pytest.skip("partition must be a multiple of block_size")
+    if lens is None:
+        case = W.make_decode_case("llama2_7b_mha_f16")
+    else:
+        spec = custom_spec(f"append_{q_dt}_{hq}_{hkv}_{d}_{bs}", hq, hkv, d, bs, q_dt, q_dt)
+        case = W.make_decode_case(spec, lens=lens)
+    pa = lib()
+    ref_run = DecodeRun(case)
+    ref_run.scatter()
+    ref = ref_run.decode(partition_size=partition)
+    run = DecodeRun(case)
+    # the new rows as a strided view (every other row of a buffer twice as tall)
+    wide_k = torch.zeros((2 * run.new_k.shape[0], *run.new_k.shape[1:]), dtype=run.new_k.dtype,
+                         device=run.new_k.device)
+    wide_k[::2] = run.new_k
+    nk = wide_k[::2]
+    out = torch.empty_like(run.q)
+    ws = pa.decode_workspace(run.q, run.k_pool, run.max_len, partition)
+    pa.pa_decode_append(out, run.q, nk, run.new_v, run.k_pool, run.v_pool, run.tables, run.lens,
+                        case.spec.scale, max_seq_len=run.max_len, partition_size=partition,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(run.k_pool.view(torch.int16), ref_run.k_pool.view(torch.int16))
+    assert torch.equal(run.v_pool.view(torch.int16), ref_run.v_pool.view(torch.int16))
+    # the two stages give the same
+    run2 = DecodeRun(case)
+    out2 = torch.empty_like(run2.q)
+    args = (out2, run2.q, run2.new_k, run2.new_v, run2.k_pool, run2.v_pool, run2.tables, run2.lens,
+            case.spec.scale)
+    pa.pa_decode_attention_append(*args, max_seq_len=run2.max_len, partition_size=partition,
+                                  workspace=ws)
+    pa.pa_decode_reduce(out2, run2.q, run2.k_pool, run2.v_pool, run2.tables, run2.lens,
+                        case.spec.scale, max_seq_len=run2.max_len, partition_size=partition,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), ref.view(torch.int16))
+
+
 def _rewrite_k_dim0(case, values_per_seq, k_scale=None):
     """Set dimension 0 of every K row of head 0 to the given per-token values
     (the newest token's through the scatter input); other dims keep their
