@@ -197,7 +197,7 @@ def run_decode_bench(args, dev):
         if ev is not None:
             ev[2].record()
 
-    step = step_append if can_append else step_separate
+    step = step_separate
     for i in range(args.warmup):
         step(batches[i % len(batches)])
     torch.cuda.synchronize()
@@ -211,20 +211,20 @@ def run_decode_bench(args, dev):
     attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
     red_ms = [e[1].elapsed_time(e[2]) for e in evs]
 
-    # After the timed region: the same steps as three launches (scatter kernel,
-    # decode, reduce), for comparison with the folded scatter
-    separate = None
+    # After the timed region: the same steps with the scatter folded into the
+    # decode kernel (two launches), for comparison
+    appended = None
     if can_append:
         for i in range(args.warmup):
-            step_separate(batches[i % len(batches)])
+            step_append(batches[i % len(batches)])
         torch.cuda.synchronize()
-        sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        aevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step_separate(batches[i % len(batches)], sevs[i])
+            step_append(batches[i % len(batches)], aevs[i])
         torch.cuda.synchronize()
-        separate = ((time.perf_counter() - t0) * 1e3 / args.steps,
-                    float(np.mean([e[0].elapsed_time(e[1]) for e in sevs])))
+        appended = ((time.perf_counter() - t0) * 1e3 / args.steps,
+                    float(np.mean([e[0].elapsed_time(e[1]) for e in aevs])))
 
     # After the timed region: the same steps replayed from captured HIP graphs
     # (one graph per batch), as a serving loop replays captured decode steps.
@@ -268,9 +268,8 @@ def run_decode_bench(args, dev):
                    "head_dim": spec.head_dim, "block_size": spec.block_size,
                    "total_context_tokens": int(lay.seq_lens.sum()), "max_seq_len": max_len,
                    "partition_size": resolved, "rotated_batches": len(batches)},
-        "roofline": {"bound": "hbm", "kernel": ("decode_kernel<MfmaDecode<..., APPEND>>" if can_append
-                                                else "decode_kernel<MfmaDecode>" if spec.cache_dtype != "f32"
-                                                else "decode_kernel<F32Decode>"),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<MfmaDecode>" if spec.cache_dtype != "f32"
+                     else "decode_kernel<F32Decode>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": (decode_traffic_bytes()
@@ -289,12 +288,11 @@ def run_decode_bench(args, dev):
                                       np.percentile(attn_ms, [10, 50, 90])],
         "effective_kv_bytes_per_step": eff,
     }
-    res["step"] = ("pa_decode_attention_append + pa_decode_reduce (scatter folded into the "
-                   "decode kernel)" if can_append else "scatter kernel + decode attention + reduce")
-    if separate is not None:
-        res["separate_kernels_ms_per_step"] = round(separate[0], 5)
-        res["separate_kernels_gbps"] = round(eff / (separate[0] * 1e-3) / 1e9, 1)
-        res["separate_decode_attention_avg_ms"] = round(separate[1], 5)
+    res["step"] = "scatter kernel + decode attention + reduce"
+    if appended is not None:
+        res["append_ms_per_step"] = round(appended[0], 5)
+        res["append_gbps"] = round(eff / (appended[0] * 1e-3) / 1e9, 1)
+        res["append_attention_avg_ms"] = round(appended[1], 5)
     return res
 
 

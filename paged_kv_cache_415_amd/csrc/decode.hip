@@ -214,11 +214,12 @@ struct MfmaDecode {
   }
 
   // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).
+  template <bool APP = false>
   static __device__ __forceinline__ void load(Buf& buf, Ids id, const DecodeParams& p, int kvh,
                                               int j, int s = 0, int len = 0) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, c16 = lane & 15;
-    static_assert(!APPEND || (KF == kFmtQ && VF == kFmtQ), "append needs a 16-bit cache");
+    static_assert(!APP || (KF == kFmtQ && VF == kFmtQ && !kDoubleBuffer), "append: 16-bit cache");
     const char* kpool = reinterpret_cast<const char*>(p.k_pool);
     const char* vpool = reinterpret_cast<const char*>(p.v_pool);
 #pragma unroll
@@ -251,10 +252,10 @@ struct MfmaDecode {
       const char* kt = kpool + krow * KEB;
       // APPEND: the tile holding the newest token takes that row from the input
       const int t0 = j * kStep + 16 * tau;
-      const bool new_tile = APPEND && len - 1 >= t0 && len - 1 < t0 + 16;   // uniform
+      const bool new_tile = APP && len - 1 >= t0 && len - 1 < t0 + 16;   // uniform
       const char* nk = nullptr;
       const char* nv = nullptr;
-      if constexpr (APPEND) {
+      if constexpr (APP) {
         if (new_tile) {
           nk = reinterpret_cast<const char*>(p.new_k) + ((int64_t)s * p.new_k_stride + (int64_t)kvh * D) * 2;
           nv = reinterpret_cast<const char*>(p.new_v) + ((int64_t)s * p.new_v_stride + (int64_t)kvh * D) * 2;
@@ -272,7 +273,7 @@ struct MfmaDecode {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const char* src = vt + (int64_t)i * D * VEB;
-        if constexpr (APPEND) {
+        if constexpr (APP) {
           if (new_tile && t0 + 4 * G + i == len - 1) src = nv + (int64_t)DPL * c16 * 2;
         }
         if constexpr (VW == 4) {
@@ -453,25 +454,36 @@ struct MfmaDecode {
     if constexpr (kDoubleBuffer) {
       Buf A, B;
       Ids nxt = ids(trow, nblk, min(j0 + 1, j1 - 1));
-      load(A, cur, p, kvh, j0, s, len);
+      load(A, cur, p, kvh, j0);
       for (int j = j0; j < j1; j += 2) {
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 2, j1 - 1));
-        if (j + 1 < j1) load(B, cur, p, kvh, j + 1, s, len);
+        if (j + 1 < j1) load(B, cur, p, kvh, j + 1);
         compute(A, st, qop, p.qk_scale_log2, len, j);
         if (j + 1 >= j1) break;
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 3, j1 - 1));
-        if (j + 2 < j1) load(A, cur, p, kvh, j + 2, s, len);
+        if (j + 2 < j1) load(A, cur, p, kvh, j + 2);
         compute(B, st, qop, p.qk_scale_log2, len, j + 1);
       }
     } else {
-      for (int j = j0; j < j1; ++j) {
+      // APPEND: the step that holds the newest token (the last step of the
+      // pair) is peeled off, so the loop is that of the plain kernel
+      const bool last_step = APPEND && j1 == (len + kStep - 1) / kStep;
+      const int jend = last_step ? j1 - 1 : j1;
+      for (int j = j0; j < jend; ++j) {
         const Ids nxt = ids(trow, nblk, min(j + 1, j1 - 1));
         Buf buf;
-        load(buf, cur, p, kvh, j, s, len);
+        load(buf, cur, p, kvh, j);
         compute(buf, st, qop, p.qk_scale_log2, len, j);
         cur = nxt;
+      }
+      if constexpr (APPEND) {
+        if (last_step) {
+          Buf buf;
+          load<true>(buf, cur, p, kvh, jend, s, len);
+          compute(buf, st, qop, p.qk_scale_log2, len, jend);
+        }
       }
     }
 
