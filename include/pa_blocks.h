@@ -30,7 +30,8 @@
  *    that are cached under the same keys with the same namespace, parent key
  *    and tokens, then hands out fresh blocks; each fresh full block is
  *    cached under its key unless that key is taken; a partial last block is
- *    never cached;
+ *    not cached (pa_bm_register_blocks caches blocks once decode steps have
+ *    filled them);
  *  - a cached block whose count drops to zero stays cached on an LRU list; a
  *    fresh block is taken from the free list, else by evicting the LRU front
  *    (it leaves the cache);
@@ -75,6 +76,17 @@ int32_t pa_bm_ref_count(const pa_block_manager* m, int32_t block);
 pa_status pa_bm_allocate_prompt(pa_block_manager* m, uint64_t namespace_id, const int32_t* tokens,
                                 int32_t num_tokens, int32_t* blocks_out, int32_t capacity,
                                 int32_t* num_blocks_out, int32_t* num_cached_blocks_out);
+
+/* Cache the full blocks a sequence has filled since its prompt (multi-turn
+ * prefix sharing, [intelli] §6.2): for each full block i of `tokens` (the
+ * sequence's token ids so far), block table[i] is cached under the key of
+ * tokens[0 .. (i+1) * block_size) in `namespace_id`, unless that block is
+ * already cached or the key is taken.  Blocks must be in use; the caller
+ * guarantees that the pools hold the K/V of these tokens.
+ * *num_registered_out (may be NULL) receives the number of blocks added. */
+pa_status pa_bm_register_blocks(pa_block_manager* m, uint64_t namespace_id, const int32_t* tokens,
+                                int32_t num_tokens, const int32_t* table, int32_t num_blocks,
+                                int32_t* num_registered_out);
 
 /* Grow a table of num_blocks ids (array of capacity entries) so that it
  * covers new_len tokens; *num_blocks_out receives the new length.  Blocks

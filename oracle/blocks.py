@@ -25,7 +25,8 @@ taken (and the native manager documents the same):
     block's token ids (int32 each); a hit also needs equal namespace, parent
     key and tokens, so equal keys alone never share a block;
   - only full blocks are cached; a fresh full block is cached unless its key
-    is already in the cache;
+    is already in the cache; blocks that decode steps fill are cached the
+    same way when the caller registers them;
   - a cached block nobody uses stays cached; fresh blocks come from the free
     list, else from evicting the least recently released cached block;
   - a finished sequence releases its blocks last first;
@@ -127,6 +128,25 @@ class PrefixBlockManager:
                     self.entry[b] = (keys[i], parent, namespace, chunk)
                 parent = keys[i]
         return out, hits
+
+    def register_blocks(self, namespace: int, tokens, table: list) -> int:
+        """Cache the full blocks of ``tokens`` held by ``table`` (blocks filled by
+        decode steps; intelliparadigm §6.2, prefix sharing across turns of a
+        dialogue): block i is cached under the key of the first (i + 1) full
+        blocks, unless it is already cached or the key is taken."""
+        bs = self.block_size
+        full = len(tokens) // bs
+        added, parent = 0, 0
+        for i in range(full):
+            chunk = tuple(int(t) for t in tokens[i * bs:(i + 1) * bs])
+            k = block_key(parent, namespace, chunk)
+            b = table[i]
+            if b not in self.entry and k not in self.cache:
+                self.cache[k] = b
+                self.entry[b] = (k, parent, namespace, chunk)
+                added += 1
+            parent = k
+        return added
 
     def append(self, table: list, new_len: int) -> None:
         need = -(-new_len // self.block_size)

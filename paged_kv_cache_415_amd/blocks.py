@@ -27,11 +27,12 @@ def _setup(lib):
     lib.pa_bm_ref_count.restype = _i32
     lib.pa_bm_allocate_prompt.argtypes = [_vp, _u64, _P32, _i32, _P32, _i32, _P32, _P32]
     lib.pa_bm_append.argtypes = [_vp, _P32, _i32, _i32, _i32, _P32]
+    lib.pa_bm_register_blocks.argtypes = [_vp, _u64, _P32, _i32, _P32, _i32, _P32]
     lib.pa_bm_fork.argtypes = [_vp, _P32, _i32]
     lib.pa_bm_copy_on_write.argtypes = [_vp, _P32, _i32, _i32, _P64]
     lib.pa_bm_release.argtypes = [_vp, _P32, _i32]
     for name in ("pa_bm_allocate_prompt", "pa_bm_append", "pa_bm_fork", "pa_bm_copy_on_write",
-                 "pa_bm_release"):
+                 "pa_bm_release", "pa_bm_register_blocks"):
         getattr(lib, name).restype = _i32
     return lib
 
@@ -102,6 +103,15 @@ class BlockManager:
         _check(_lib.pa_bm_allocate_prompt(self._h, int(namespace) & (2**64 - 1), _p32(tok), tok.size,
                                           _p32(out), cap, ctypes.byref(n), ctypes.byref(hits)))
         return out[:n.value].tolist(), hits.value
+
+    def register_blocks(self, namespace: int, tokens, table: list) -> int:
+        """Cache the full blocks of a sequence's tokens that its table holds."""
+        tok = _arr(tokens)
+        buf = _arr(table) if table else np.zeros(1, np.int32)
+        n = _i32()
+        _check(_lib.pa_bm_register_blocks(self._h, int(namespace) & (2**64 - 1), _p32(tok), tok.size,
+                                          _p32(buf), len(table), ctypes.byref(n)))
+        return n.value
 
     def append(self, table: list, new_len: int) -> None:
         need = -(-new_len // self.block_size)

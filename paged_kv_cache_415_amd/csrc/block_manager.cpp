@@ -252,6 +252,37 @@ pa_status pa_bm_allocate_prompt(pa_block_manager* m, uint64_t namespace_id, cons
   return done();
 }
 
+pa_status pa_bm_register_blocks(pa_block_manager* m, uint64_t namespace_id, const int32_t* tokens,
+                                int32_t num_tokens, const int32_t* table, int32_t num_blocks,
+                                int32_t* num_registered_out) {
+  if (!m || num_tokens < 0 || num_blocks < 0 || (num_tokens > 0 && !tokens) || (num_blocks > 0 && !table))
+    return bad("arguments");
+  const int32_t bs = m->block_size;
+  const int32_t full = num_tokens / bs;
+  if (full > num_blocks) return bad("the table is shorter than the full blocks of the tokens");
+  for (int32_t i = 0; i < full; ++i)
+    if (!valid_block(m, table[i]) || m->ref[table[i]] <= 0) return bad("block not in use");
+  int32_t added = 0;
+  uint64_t par = 0;
+  for (int32_t i = 0; i < full; ++i) {
+    const int32_t* tk = tokens + (size_t)i * bs;
+    const uint64_t k = block_key(par, namespace_id, tk, bs);
+    const int32_t b = table[i];
+    if (!m->cached[b] && m->by_key.find(k) == m->by_key.end()) {
+      m->by_key[k] = b;
+      m->cached[b] = 1;
+      m->key[b] = k;
+      m->parent[b] = par;
+      m->ns[b] = namespace_id;
+      std::memcpy(&m->tokens[(size_t)b * bs], tk, sizeof(int32_t) * bs);
+      ++added;
+    }
+    par = k;
+  }
+  if (num_registered_out) *num_registered_out = added;
+  return done();
+}
+
 pa_status pa_bm_append(pa_block_manager* m, int32_t* table, int32_t num_blocks, int32_t capacity,
                        int32_t new_len, int32_t* num_blocks_out) {
   if (!m || !num_blocks_out || num_blocks < 0 || new_len < 0 || (num_blocks > 0 && !table))

@@ -30,13 +30,16 @@ def test_random_streams_match_the_oracle(native, seed):
     o = PrefixBlockManager(nb, bs, order=order)
     prefixes = [list(map(int, rng.integers(0, 4, size=int(rng.integers(0, 4 * bs)))))
                 for _ in range(4)]
-    live_m, live_o = [], []
+    live_m, live_o, toks, nss = [], [], [], []
     for _ in range(300):
-        op = int(rng.integers(0, 6))
+        op = int(rng.integers(0, 7))
         k = int(rng.integers(0, len(live_o))) if live_o else 0
         if op <= 1 or not live_o:
             ns = int(rng.integers(0, 3)) * 0x9E3779B97F4A7C15 % 2**64
-            p = prefixes[int(rng.integers(0, 4))] + list(map(int, rng.integers(0, 4, int(rng.integers(0, 2 * bs + 1)))))
+            if live_o and rng.integers(0, 3) == 0:        # a later turn of a live dialogue
+                p = toks[k] + list(map(int, rng.integers(0, 4, int(rng.integers(0, 2 * bs + 1)))))
+            else:
+                p = prefixes[int(rng.integers(0, 4))] + list(map(int, rng.integers(0, 4, int(rng.integers(0, 2 * bs + 1)))))
             try:
                 want = o.allocate_prompt(ns, p)
             except OracleOOM:
@@ -46,6 +49,8 @@ def test_random_streams_match_the_oracle(native, seed):
                 assert m.allocate_prompt(ns, p) == want
                 live_o.append(list(want[0]))
                 live_m.append(list(want[0]))
+                toks.append(list(p))
+                nss.append(ns)
         elif op == 2:
             new_len = len(live_o[k]) * bs + int(rng.integers(0, 3 * bs))
             try:
@@ -55,9 +60,13 @@ def test_random_streams_match_the_oracle(native, seed):
                     m.append(live_m[k], new_len)
             else:
                 m.append(live_m[k], new_len)
+                # the sequence generated tokens up to new_len
+                toks[k] = toks[k] + list(map(int, rng.integers(0, 4, max(0, new_len - len(toks[k])))))
         elif op == 3:
             live_o.append(o.fork(live_o[k]))
             live_m.append(m.fork(live_m[k]))
+            toks.append(list(toks[k]))
+            nss.append(nss[k])
         elif op == 4 and live_o[k]:
             j = int(rng.integers(0, len(live_o[k])))
             try:
@@ -70,6 +79,12 @@ def test_random_streams_match_the_oracle(native, seed):
         elif op == 5:
             o.release(live_o.pop(k))
             m.release(live_m.pop(k))
+            toks.pop(k)
+            nss.pop(k)
+        elif op == 6:
+            # blocks the sequence has filled join the cache (tokens so far)
+            t = toks[k][:len(live_o[k]) * bs]
+            assert m.register_blocks(nss[k], t, live_m[k]) == o.register_blocks(nss[k], t, live_o[k])
         assert live_m == live_o
         _same_state(m, o)
 

@@ -101,6 +101,25 @@ def test_released_prefix_stays_cached_then_is_evicted_lru_tail_first():
     assert m.num_evictable() == 1 and m.ref[3] == 0
 
 
+def test_blocks_filled_by_decode_serve_the_next_turn():
+    # a dialogue: turn 1's prompt, then its reply generated token by token;
+    # turn 2's prompt repeats both and adds the new question
+    m = PrefixBlockManager(16, 4)
+    p1 = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10]                    # 2 full blocks + 2 tokens
+    t1, h1 = m.allocate_prompt(3, p1)
+    assert (t1, h1) == ([0, 1, 2], 0) and m.num_cached() == 2
+    reply = [11, 12, 13, 14, 15, 16]
+    m.append(t1, len(p1) + len(reply))                     # 16 tokens: blocks 2 and 3 full
+    assert t1 == [0, 1, 2, 3]
+    assert m.register_blocks(3, p1 + reply, t1) == 2       # blocks 2 and 3 join the cache
+    assert m.register_blocks(3, p1 + reply, t1) == 0       # idempotent
+    t2, h2 = m.allocate_prompt(3, p1 + reply + [20, 21])
+    assert h2 == 4 and t2[:4] == t1 and t2[4] == 4
+    # another namespace still shares nothing
+    _, h3 = m.allocate_prompt(4, p1 + reply)
+    assert h3 == 0
+
+
 def test_copy_on_write_and_fork():
     m = PrefixBlockManager(6, 4)
     a, _ = m.allocate_prompt(0, [1, 2, 3, 4, 5])
