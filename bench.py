@@ -498,11 +498,18 @@ KERNEL_SOURCES = ["decode.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"]
 
 
 def kernel_sources_sha256() -> str:
+    """Hash of the decode sources with comments and blank lines removed (a
+    comment edit does not change the kernel the counters were taken on)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_415_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_415_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

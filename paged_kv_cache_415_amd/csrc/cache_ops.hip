@@ -7,8 +7,10 @@
 // physical block handed out for it) with the slot linearisation
 // physical * block_size + offset.  The block copy follows the ybb.press page
 // "vLLM 与 LLM 推理部署实战" §2.2 (a write to a shared block duplicates the
-// whole block first).  Both are pure data movement: one 16-byte load and one
-// store per thread, coalesced along head_dim.
+// whole block first).  Both are data movement: 16-byte loads and stores per
+// thread, coalesced along head_dim; the quantising scatters (fp8 E4M3 with
+// per-tensor scales, int8 with per-(block, KV head) scales) turn 16 source
+// elements into one 16-byte store of codes.
 #include "pa_device.h"
 #include "pa_launch.h"
 

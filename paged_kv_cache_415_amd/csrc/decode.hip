@@ -35,6 +35,15 @@
 // head's own lanes.  The value operand wants 4+4 tokens of one dimension
 // per lane while the cache stores dimensions contiguously; each lane loads
 // 16-byte row pieces and transposes them in registers with byte permutes.
+//
+// Cache formats: 16-bit (the query's type), fp8 E4M3 (codes decoded exactly
+// with gfx950's packed scaled converts, per-tensor scales folded into the
+// logit scale and the output), fp8 K beside a 16-bit V, and int8 with one
+// scale per (block, KV head) (codes converted exactly; the block's K scale
+// joins each score's scale, its V scale each probability of the value
+// product).  For 16-bit caches the newest token of each sequence can be
+// taken from the input and written to its slot by the wave that covers it
+// (the scatter folded into the decode).
 #include <mutex>
 
 #include "pa_device.h"
