@@ -725,11 +725,13 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
   if (threadIdx.x == 0) queue = 0;
   build_plan<NW>(p, lens, pre);  // ends with a barrier
 
-  // Sequences with no tokens get a zero output.
+  // Sequences with no tokens get a zero output (and a partial count of 0).
   for (int s = blockIdx.x; s < S; s += gridDim.x) {
     if (lens[s] == 0) {
       QT* out = reinterpret_cast<QT*>(p.out) + (int64_t)s * p.num_q_heads * p.head_dim;
       for (int i = threadIdx.x; i < p.num_q_heads * p.head_dim; i += NT) out[i] = (QT)0.0f;
+      if (p.nparts != nullptr)
+        for (int h = threadIdx.x; h < H; h += NT) p.nparts[s * H + h] = 0;
     }
   }
 
@@ -751,48 +753,89 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of split partials of one (sequence, KV head) pair:
+// Log-sum-exp merge of the split partials of one (sequence, query head):
 //   M = max_i m_i,  out = v_scale * sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
+// One wave per query head (four per workgroup): lane i takes partial i's
+// weight; the dims of the output are spread over the lanes.  The partial
+// rows are read eight at a time, the first eight together with m and l, so
+// a head costs two dependent memory round trips (its count, then the rest).
+// The attention kernel stores a count for every pair, 0 for an empty
+// sequence and 1 for a pair it finished without partials.
 // ---------------------------------------------------------------------------
-template <typename QT>
-__global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
-  __shared__ float s_max[16], s_inv[16];
-  const int h = blockIdx.x, s = blockIdx.y;
-  int len = p.seq_lens[s];
-  len = len < p.max_len ? len : p.max_len;
-  if (len <= 0) return;
-  const int np = p.nparts[s * p.num_kv_heads + h];
-  if (np <= 1) return;
-  const int D = p.head_dim, g = p.group;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)s * p.num_q_heads + h * g) * p.max_parts;
-  // M and L of each head: one wave per head, lanes over the partials.
-  for (int j = wave; j < g; j += 4) {
-    const float* m = p.part_m + row0 + (int64_t)j * p.max_parts;
-    const float* l = p.part_l + row0 + (int64_t)j * p.max_parts;
-    float M = -INFINITY;
-    for (int i = lane; i < np; i += 64) M = fmaxf(M, m[i]);
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float L = 0.f;
-    for (int i = lane; i < np; i += 64) L += __builtin_amdgcn_exp2f(m[i] - M) * l[i];
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-    if (lane == 0) {
-      s_max[j] = M;
-      s_inv[j] = p.v_scale / L;
+template <int E>
+__device__ __forceinline__ void load_rows8(const float* po, int D, int first, int last, float (&x)[8][E]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t row = min(first + u, last);   // rows past the last are re-read, weight 0
+    if constexpr (E == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(po + row * D);
+      x[u][0] = v.x;
+      x[u][1] = v.y;
+    } else {
+      x[u][0] = po[row * D];
     }
   }
-  __syncthreads();
-  // Weighted sum of the partial outputs; the loads of several partials are
-  // issued together (they do not depend on each other).
-  for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
-    const int j = idx / D, d = idx - j * D;
-    const int64_t b = row0 + (int64_t)j * p.max_parts;
-    const float M = s_max[j];
-    float O = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < np; ++i) O += __builtin_amdgcn_exp2f(p.part_m[b + i] - M) * p.part_o[(b + i) * D + d];
-    reinterpret_cast<QT*>(p.out)[((int64_t)s * p.num_q_heads + h * g + j) * D + d] = (QT)(O * s_inv[j]);
+}
+
+template <int E>
+__device__ __forceinline__ void accum_rows8(float w, int t, const float (&x)[8][E], float (&O)[E]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    // lane t + u <= 63 holds that partial's weight (0 past the count)
+    const float wf = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t + u));
+#pragma unroll
+    for (int e = 0; e < E; ++e) O[e] += wf * x[u][e];
   }
+}
+
+template <typename QT, int D>
+__global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
+  constexpr int E = D / 64;   // output dims per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hq = blockIdx.x * 4 + wave, s = blockIdx.y;
+  if (hq >= p.num_q_heads) return;
+  const int np = p.nparts[s * p.num_kv_heads + hq / p.group];
+  if (np <= 1) return;
+  const int64_t b = ((int64_t)s * p.num_q_heads + hq) * p.max_parts;
+  const float* pm = p.part_m + b;
+  const float* pl = p.part_l + b;
+  const float* po = p.part_o + b * D + E * lane;
+
+  const int n0 = min(64, np);
+  float x[8][E];
+  load_rows8<E>(po, D, 0, n0 - 1, x);
+  const float m0 = lane < n0 ? pm[lane] : -INFINITY;
+  const float l0 = lane < n0 ? pl[lane] : 0.f;
+  float M = m0;
+  for (int i = 64 + lane; i < np; i += 64) M = fmaxf(M, pm[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+
+  float O[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) O[e] = 0.f;
+  float w = lane < n0 ? __builtin_amdgcn_exp2f(m0 - M) : 0.f;
+  float L = w * l0;
+  accum_rows8<E>(w, 0, x, O);
+  for (int t = 8; t < n0; t += 8) {
+    load_rows8<E>(po, D, t, n0 - 1, x);
+    accum_rows8<E>(w, t, x, O);
+  }
+  for (int c = 64; c < np; c += 64) {
+    const int n = min(64, np - c);
+    w = lane < n ? __builtin_amdgcn_exp2f(pm[c + lane] - M) : 0.f;
+    L += lane < n ? w * pl[c + lane] : 0.f;
+    for (int t = 0; t < n; t += 8) {
+      load_rows8<E>(po, D, c + t, c + n - 1, x);
+      accum_rows8<E>(w, t, x, O);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+  const float inv = p.v_scale / L;
+  QT* orow = reinterpret_cast<QT*>(p.out) + ((int64_t)s * p.num_q_heads + hq) * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) orow[e] = (QT)(O[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -890,15 +933,25 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream) {
   return launch_mfma_formats<_Float16>(p, stream);
 }
 
+namespace {
+
+template <int D>
+void launch_reduce_d(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((p.num_q_heads + 3) / 4, p.num_seqs);
+  if (p.q_dtype == kF32)
+    hipLaunchKernelGGL((lse_reduce_kernel<float, D>), grid, dim3(256), 0, stream, p);
+  else if (p.q_dtype == kBF16)
+    hipLaunchKernelGGL((lse_reduce_kernel<__bf16, D>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((lse_reduce_kernel<_Float16, D>), grid, dim3(256), 0, stream, p);
+}
+
+}  // namespace
+
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.mode == kSplitNone) return hipSuccess;
-  const dim3 grid(p.num_kv_heads, p.num_seqs);
-  if (p.q_dtype == kF32)
-    hipLaunchKernelGGL(lse_reduce_kernel<float>, grid, dim3(256), 0, stream, p);
-  else if (p.q_dtype == kBF16)
-    hipLaunchKernelGGL(lse_reduce_kernel<__bf16>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(lse_reduce_kernel<_Float16>, grid, dim3(256), 0, stream, p);
+  if (p.head_dim == 128) launch_reduce_d<128>(p, stream);
+  else launch_reduce_d<64>(p, stream);
   return hipGetLastError();
 }
 
