@@ -13,7 +13,9 @@
 // one per wave), so every wave streams about the same number of KV bytes
 // whatever the length mix.  A chunk that covers a pair partly yields a
 // partial result (o, m, l); a pair inside one chunk gets its output written
-// directly.  The log-sum-exp reduce kernel merges the partials.  Two other
+// directly.  Partials of a pair whose chunks all belong to one workgroup are
+// kept in LDS and merged (log-sum-exp) by the last of its waves to finish;
+// the others go to the workspace and the reduce kernel merges them.  Two other
 // cuts exist: fixed partitions of a given length from each sequence's start,
 // and whole pairs (no partials at all).  Each workgroup owns an even share of
 // the chunks (or items); its waves take them from an LDS queue.
@@ -139,6 +141,24 @@ __device__ __forceinline__ int find_seq(const int* pre, int S, int x) {
   return lo;
 }
 
+// Partials merged on the CU.  When every partial of a (sequence, KV head)
+// pair comes from the same workgroup's share of the work list, the waves put
+// them in LDS instead of the workspace, and the last of them to finish
+// merges them (log-sum-exp) and stores the output: partial outputs never
+// travel to HBM and back.  Pairs that cross a share boundary use the
+// workspace and the reduce kernel.
+//   slots: [local_slots][group * D] floats, ml: [local_slots][32] (running
+//   max of 16 heads, then their sums), cnt: [local_slots] arrival counters.
+// Partial `part` of the pair sits in slot stride * (base + part) (+ odd0 for
+// part 0); `counter` < 0 marks a pair merged through the workspace.
+struct LocalMerge {
+  float* slots;
+  float* ml;
+  int* cnt;
+  int base, stride, odd0, counter;
+  __device__ __forceinline__ int slot(int part) const { return stride * (base + part) + (part == 0 ? odd0 : 0); }
+};
+
 // Block-table entries of one sequence, 128 consecutive ones held as two
 // registers per lane; entry b is read out with v_readlane.
 template <int BS>
@@ -197,6 +217,9 @@ struct MfmaDecode {
   static constexpr int VW = DPL * VEB / 4;      // dwords per V row piece
   static constexpr int KL = KF8 ? D / 64 : NC;  // 16-byte K loads per lane and tile
   static constexpr bool kDoubleBuffer = KF8 && VF8;
+  // partials merged in LDS (not with the scatter folded in, whose registers
+  // are at the limit of three waves per SIMD)
+  static constexpr bool kLocalMerge = !APPEND;
   // waves per workgroup = waves one CU keeps resident at this register count
   static constexpr int kWaves = D == 64 ? 16 : (KF8 && VF8 ? 8 : 12);
 
@@ -424,9 +447,78 @@ struct MfmaDecode {
     }
   }
 
+  // Output rows of query head hq: v_scale * acc / l_tot in QT (lanes of the
+  // head's column).
+  static __device__ __forceinline__ void store_output(const DecodeParams& p, const f32x4 (&acc)[DPL],
+                                                      float l_tot, int s, int hq) {
+    const int G = (threadIdx.x & 63) >> 4;
+    QT* orow = reinterpret_cast<QT*>(p.out) + ((int64_t)s * p.num_q_heads + hq) * D;
+    const float inv = p.v_scale / l_tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w[DPL / 2];
+#pragma unroll
+      for (int n = 0; n < DPL; n += 2) w[n / 2] = pack2<QT>(acc[n][i] * inv, acc[n + 1][i] * inv);
+      QT* dst = orow + DPL * (4 * G + i);
+      if constexpr (DPL == 8) st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+      else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+    }
+  }
+
+  // This wave's partial goes to its LDS slot; the last of the pair's waves
+  // to arrive merges all of them and stores the output.  A lane keeps the
+  // same (head, dims) in every slot, so the merge is lane-local.
+  static __device__ __forceinline__ void merge_local(const DecodeParams& p, f32x4 (&acc)[DPL], float m,
+                                                     float l_tot, int s, int kvh, int part, int nparts,
+                                                     const LocalMerge& lm) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, c16 = lane & 15;
+    const int g = p.group;
+    if (part == 0 && p.nparts != nullptr && lane == 0) p.nparts[s * p.num_kv_heads + kvh] = 1;  // merged here
+    const int lq = G * g + c16;   // this lane's position among the 4 g writing lanes
+    if (c16 < g) {
+      float* dst = lm.slots + (int64_t)lm.slot(part) * g * D;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k)   // quad k = (i, nq): acc[4 nq + e][i]
+        *reinterpret_cast<f32x4*>(dst + (k * 4 * g + lq) * 4) =
+            f32x4{acc[4 * (k % (DPL / 4))][k / (DPL / 4)], acc[4 * (k % (DPL / 4)) + 1][k / (DPL / 4)],
+                  acc[4 * (k % (DPL / 4)) + 2][k / (DPL / 4)], acc[4 * (k % (DPL / 4)) + 3][k / (DPL / 4)]};
+      if (G == 0) {
+        lm.ml[lm.slot(part) * 32 + c16] = m;
+        lm.ml[lm.slot(part) * 32 + 16 + c16] = l_tot;
+      }
+    }
+    __threadfence_block();
+    int old = 0;
+    if (lane == 0) old = atomicAdd(&lm.cnt[lm.counter], 1);
+    old = __builtin_amdgcn_readlane(old, 0);
+    if (old != nparts - 1) return;
+    __threadfence_block();
+    if (c16 >= g) return;
+    float M = -INFINITY;
+    for (int t = 0; t < nparts; ++t) M = fmaxf(M, lm.ml[lm.slot(t) * 32 + c16]);
+    // acc (this wave's own partial, already in its slot) becomes the sum
+#pragma unroll
+    for (int n = 0; n < DPL; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int t = 0; t < nparts; ++t) {
+      const int sl = lm.slot(t);
+      const float w = __builtin_amdgcn_exp2f(lm.ml[sl * 32 + c16] - M);
+      L += w * lm.ml[sl * 32 + 16 + c16];
+      const float* src = lm.slots + (int64_t)sl * g * D;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + (k * 4 * g + lq) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * (k % (DPL / 4)) + e][k / (DPL / 4)] += w * x[e];
+      }
+    }
+    store_output(p, acc, L, s, kvh * g + c16);
+  }
+
   // One wave: steps [j0, j1) of pair (s, kvh), then the output or a partial.
   static __device__ void segment(const DecodeParams& p, int s, int kvh, int len, int j0, int j1,
-                                 int part, int nparts) {
+                                 int part, int nparts, const LocalMerge& lm) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, c16 = lane & 15;
     const int g = p.group;
@@ -515,20 +607,16 @@ struct MfmaDecode {
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
     float l_tot = xor_sum(st.l, 16);
     l_tot = xor_sum(l_tot, 32);
+    if constexpr (kLocalMerge) {
+      if (nparts > 1 && lm.counter >= 0) {
+        merge_local(p, st.acc, st.m, l_tot, s, kvh, part, nparts, lm);
+        return;
+      }
+    }
     if (c16 < g) {
       const int hq = kvh * g + c16;
       if (nparts == 1) {
-        QT* orow = reinterpret_cast<QT*>(p.out) + ((int64_t)s * p.num_q_heads + hq) * D;
-        const float inv = p.v_scale / l_tot;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t w[DPL / 2];
-#pragma unroll
-          for (int n = 0; n < DPL; n += 2) w[n / 2] = pack2<QT>(st.acc[n][i] * inv, st.acc[n + 1][i] * inv);
-          QT* dst = orow + DPL * (4 * G + i);
-          if constexpr (DPL == 8) st16(dst, u32x4{w[0], w[1], w[2], w[3]});
-          else *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-        }
+        store_output(p, st.acc, l_tot, s, hq);
       } else {
         const int64_t b = ((int64_t)s * p.num_q_heads + hq) * p.max_parts + part;
         float* o = p.part_o + b * D;
@@ -558,8 +646,9 @@ struct MfmaDecode {
 template <int D, int BS>
 struct F32Decode {
   static constexpr int kWaves = D == 64 ? 12 : 8;  // resident waves per CU
+  static constexpr bool kLocalMerge = false;
   static __device__ void segment(const DecodeParams& p, int s, int kvh, int len, int j0, int j1,
-                                 int part, int nparts) {
+                                 int part, int nparts, const LocalMerge&) {
     constexpr int E = D / 64;
     const int lane = threadIdx.x & 63;
     const int g = p.group;
@@ -652,7 +741,7 @@ struct F32Decode {
 // ---------------------------------------------------------------------------
 template <class Seg>
 __device__ __forceinline__ void run_chunk(const DecodeParams& p, const int* lens, const int* pre,
-                                          int T, int chunk, int k) {
+                                          int T, int chunk, int k, LocalMerge lm, int k0, int k1) {
   const int S = p.num_seqs, H = p.num_kv_heads;
   int u = k * chunk;
   const int uend = min(T, u + chunk);
@@ -665,7 +754,13 @@ __device__ __forceinline__ void run_chunk(const DecodeParams& p, const int* lens
     const int ps = base * H + h * U;  // first unit of the pair
     const int j1 = min(U, j + (uend - u));
     const int wf = ps / chunk, wl = (ps + U - 1) / chunk;
-    Seg::segment(p, s, h, uni(lens[s]), j, j1, k - wf, wl - wf + 1);
+    // chunk k' holds its pair partials in slots 2 (k' - k0) (the one that
+    // continues a pair) and 2 (k' - k0) + 1 (the one that starts a pair
+    // after the chunk's start)
+    lm.base = wf - k0;
+    lm.odd0 = ps % chunk != 0;
+    lm.counter = (lm.slots != nullptr && wf >= k0 && wl < k1) ? wf - k0 : -1;
+    Seg::segment(p, s, h, uni(lens[s]), j, j1, k - wf, wl - wf + 1, lm);
     u += j1 - j;
     if (u >= uend) break;
     j = 0;
@@ -683,7 +778,7 @@ __device__ __forceinline__ void run_chunk(const DecodeParams& p, const int* lens
 // Work item i of the fixed and whole cuts: one partition of one pair.
 template <class Seg>
 __device__ __forceinline__ void run_item(const DecodeParams& p, const int* lens, const int* pre,
-                                         int i) {
+                                         int i, LocalMerge lm, int k0, int k1) {
   const int S = p.num_seqs, H = p.num_kv_heads;
   const int s = find_seq(pre, S, i / H);
   const int base = uni(pre[s]);
@@ -694,7 +789,12 @@ __device__ __forceinline__ void run_item(const DecodeParams& p, const int* lens,
   const int U = (len + kStep - 1) / kStep;
   const int j0 = part * p.chunk;
   const int j1 = min(U, j0 + p.chunk);
-  Seg::segment(p, s, h, len, j0, j1, part, q);
+  // item i' holds its partial in slot i' - k0
+  const int first = i - part;
+  lm.base = first - k0;
+  lm.odd0 = 0;
+  lm.counter = (lm.slots != nullptr && first >= k0 && first + q <= k1) ? first - k0 : -1;
+  Seg::segment(p, s, h, len, j0, j1, part, q, lm);
 }
 
 // Next ticket of the workgroup's queue (LDS counter), the same in all lanes.
@@ -722,7 +822,13 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
   const int S = p.num_seqs, H = p.num_kv_heads;
   int* lens = plan_lds;
   int* pre = plan_lds + S;
+  // slots for partials merged on the CU, after the plan (16-byte aligned)
+  const int nslots = p.local_slots;
+  int* cnt = plan_lds + ((2 * S + 1 + 3) & ~3);
+  float* ml = reinterpret_cast<float*>(cnt + ((nslots + 3) & ~3));
+  float* slots = ml + 32 * nslots;
   if (threadIdx.x == 0) queue = 0;
+  for (int i = threadIdx.x; i < nslots; i += NT) cnt[i] = 0;
   build_plan<NW>(p, lens, pre);  // ends with a barrier
 
   // Sequences with no tokens get a zero output (and a partial count of 0).
@@ -746,9 +852,19 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
   }
   const int k0 = (int)((int64_t)nwork * blockIdx.x / gridDim.x);
   const int k1 = (int)((int64_t)nwork * (blockIdx.x + 1) / gridDim.x);
+  // local merging needs a slot for every partial of the share
+  LocalMerge lm;
+  const int need = p.mode == kSplitBalanced ? 2 * (k1 - k0) : k1 - k0;
+  lm.slots = (nslots > 0 && need <= nslots && p.mode != kSplitNone) ? slots : nullptr;
+  lm.ml = ml;
+  lm.cnt = cnt;
+  lm.stride = p.mode == kSplitBalanced ? 2 : 1;
+  lm.base = 0;
+  lm.odd0 = 0;
+  lm.counter = -1;
   for (int k = k0 + take_ticket(&queue); k < k1; k = k0 + take_ticket(&queue)) {
-    if (p.mode == kSplitBalanced) run_chunk<Seg>(p, lens, pre, T, chunk, k);
-    else run_item<Seg>(p, lens, pre, k);
+    if (p.mode == kSplitBalanced) run_chunk<Seg>(p, lens, pre, T, chunk, k, lm, k0, k1);
+    else run_item<Seg>(p, lens, pre, k, lm, k0, k1);
   }
 }
 
@@ -814,8 +930,14 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   float O[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) O[e] = 0.f;
+  // Sums run over the partials in order (the weights from lane t), the same
+  // arithmetic as the attention kernel's merge of partials it keeps in LDS,
+  // so both give the same bits.
   float w = lane < n0 ? __builtin_amdgcn_exp2f(m0 - M) : 0.f;
-  float L = w * l0;
+  float L = 0.f;
+  for (int t = 0; t < n0; ++t)
+    L += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t)) *
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l0), t));
   accum_rows8<E>(w, 0, x, O);
   for (int t = 8; t < n0; t += 8) {
     load_rows8<E>(po, D, t, n0 - 1, x);
@@ -824,14 +946,15 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(DecodeParams p) {
   for (int c = 64; c < np; c += 64) {
     const int n = min(64, np - c);
     w = lane < n ? __builtin_amdgcn_exp2f(pm[c + lane] - M) : 0.f;
-    L += lane < n ? w * pl[c + lane] : 0.f;
+    const float lc = lane < n ? pl[c + lane] : 0.f;
+    for (int t = 0; t < n; ++t)
+      L += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), t)) *
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lc), t));
     for (int t = 0; t < n; t += 8) {
       load_rows8<E>(po, D, c + t, c + n - 1, x);
       accum_rows8<E>(w, t, x, O);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
   const float inv = p.v_scale / L;
   QT* orow = reinterpret_cast<QT*>(p.out) + ((int64_t)s * p.num_q_heads + hq) * D + E * lane;
 #pragma unroll
@@ -871,10 +994,37 @@ int64_t wave_work_bound(const DecodeParams& p) {
   return pairs * ((umax + p.chunk - 1) / p.chunk);
 }
 
+int g_lds_max[kMaxDevices];
+std::once_flag g_lds_once[kMaxDevices];
+
+// Dynamic LDS a decode workgroup may take: the device's per-workgroup limit
+// less 8 KB (static LDS and margin), at most 150 KB.
+size_t lds_budget() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 56 * 1024;
+  std::call_once(g_lds_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || n <= 0)
+      n = 64 * 1024;
+    g_lds_max[dev] = n;
+  });
+  return std::min<size_t>(150 * 1024, (size_t)g_lds_max[dev] - 8 * 1024);
+}
+
 template <class Seg, typename QT>
-hipError_t launch_persistent(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_persistent(const DecodeParams& p0, hipStream_t stream) {
   constexpr int NT = 64 * Seg::kWaves;
-  const size_t lds = decode_plan_lds_bytes(p.num_seqs);
+  DecodeParams p = p0;
+  // LDS: the plan, then as many merge slots as fit (up to three per wave)
+  const size_t plan = (size_t)((2 * p.num_seqs + 1 + 3) & ~3) * sizeof(int);
+  const size_t per_slot = (size_t)p.group * p.head_dim * sizeof(float) + 33 * sizeof(float);
+  const size_t budget = lds_budget();
+  int slots = 0;
+  if (Seg::kLocalMerge && p.mode != kSplitNone && plan + 64 < budget)
+    slots = (int)std::min<size_t>((size_t)3 * Seg::kWaves, (budget - plan - 64) / per_slot);
+  p.local_slots = slots;
+  const size_t lds = plan + (size_t)((slots + 3) & ~3) * sizeof(int) + (size_t)slots * 32 * sizeof(float) +
+                     (size_t)slots * p.group * p.head_dim * sizeof(float);
   auto kernel = decode_kernel<Seg, QT>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), NT,

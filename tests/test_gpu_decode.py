@@ -49,6 +49,19 @@ def test_full_config_scatter_and_decode(name, full_cases):
     assert err <= TOL[case.spec.q_dtype]
 
 
+@pytest.mark.parametrize("partition", [32, 512])
+def test_full_gqa_fixed_partitions(partition, full_cases):
+    """Fixed partitions over the full Llama-3-8B-shaped batch: with 512-token partitions every
+    workgroup's share fits its LDS merge slots (partials merged on the CU); 32-token partitions
+    give shares of hundreds of partitions, which go through the workspace and the reduce."""
+    case, (ref, _, _) = full_cases("llama3_8b_gqa_bf16")
+    print(f"[decode parity] llama3_8b_gqa_bf16 fixed partitions of {partition}", flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL[case.spec.q_dtype]
+
+
 @pytest.mark.parametrize("partition", [32, 64, 160, 512, -1])
 def test_split_sizes_agree(partition):
     sub = W.make_decode_case("llama3_8b_gqa_bf16", lens=[1, 31, 32, 33, 200, 511, 512, 513, 2500])
