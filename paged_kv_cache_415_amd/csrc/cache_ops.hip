@@ -45,8 +45,8 @@ __device__ __forceinline__ float src_elem(const char* base, int i) {
   return (float)reinterpret_cast<const SrcT*>(base)[i];
 }
 
-// Quantising scatter into an fp8 E4M3 pool: each thread turns 16 source
-// elements into 16 codes (one 16-byte store).  With VQ false only K is
+// Quantising scatter into an fp8 E4M3 pool: each thread turns 4 source
+// elements into 4 codes (one 32-bit store).  With VQ false only K is
 // quantised and the V elements are copied unchanged (fp8 K cache beside a
 // 16-bit V cache).
 template <typename SrcT, bool VQ>
@@ -56,44 +56,40 @@ __global__ __launch_bounds__(256) void scatter_fp8_kernel(ScatterParams p) {
   if (slot < 0) return;
   const int64_t blk = slot / p.block_size;
   const int row = (int)(slot - blk * p.block_size);
-  const int groups_per_head = p.head_dim / 16;
+  // one thread per 4 elements of a head row (a 32-bit word of codes): the
+  // per-element divides of a token are spread over the whole workgroup
+  const int groups_per_head = p.head_dim / 4;
   const int ngroups = p.num_kv_heads * groups_per_head;
   const SrcT* ksrc = reinterpret_cast<const SrcT*>(p.key) + (int64_t)t * p.key_stride;
   const SrcT* vsrc = reinterpret_cast<const SrcT*>(p.value) + (int64_t)t * p.value_stride;
   for (int i = threadIdx.x; i < ngroups; i += blockDim.x) {
     const int h = i / groups_per_head;
     const int c = i - h * groups_per_head;
-    const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 16;
-    const int64_t src = (int64_t)h * p.head_dim + c * 16;
+    const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 4;
+    const int64_t src = (int64_t)h * p.head_dim + c * 4;
     if constexpr (!VQ) {
       const char* vs = reinterpret_cast<const char*>(vsrc + src);
       char* vd = (char*)p.v_pool + dst * (int64_t)sizeof(SrcT);
-#pragma unroll
-      for (int q = 0; q < (int)sizeof(SrcT); ++q) st16(vd + 16 * q, ld16(vs + 16 * q));
+      if constexpr (sizeof(SrcT) == 2) *reinterpret_cast<u32x2*>(vd) = ld8(vs);
+      else st16(vd, ld16(vs));
     }
 #pragma unroll
     for (int which = 0; which < (VQ ? 2 : 1); ++which) {
       const SrcT* s = which ? vsrc : ksrc;
       const float scale = which ? p.v_scale : p.k_scale;
-      uint32_t w[4];
+      uint32_t acc = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float x = (float)s[src + q * 4 + b];
-          acc |= e4m3_encode(x / scale) << (8 * b);   // correctly rounded fp32 divide
-        }
-        w[q] = acc;
+      for (int b = 0; b < 4; ++b) {
+        const float x = (float)s[src + b];
+        acc |= e4m3_encode(x / scale) << (8 * b);   // correctly rounded fp32 divide
       }
-      u32x4 v = {w[0], w[1], w[2], w[3]};
-      st16((char*)(which ? p.v_pool : p.k_pool) + dst, v);
+      *reinterpret_cast<uint32_t*>((char*)(which ? p.v_pool : p.k_pool) + dst) = acc;
     }
   }
 }
 
 // Quantising scatter into an int8 pool with one scale per (block, KV head):
-// each thread turns 16 source elements of K and of V into 16 codes each.
+// each thread turns 4 source elements of K and of V into 4 codes each.
 template <typename SrcT>
 __global__ __launch_bounds__(256) void scatter_i8_kernel(ScatterParams p) {
   const int t = blockIdx.x;
@@ -101,29 +97,24 @@ __global__ __launch_bounds__(256) void scatter_i8_kernel(ScatterParams p) {
   if (slot < 0) return;
   const int64_t blk = slot / p.block_size;
   const int row = (int)(slot - blk * p.block_size);
-  const int groups_per_head = p.head_dim / 16;
+  const int groups_per_head = p.head_dim / 4;
   const int ngroups = p.num_kv_heads * groups_per_head;
   const SrcT* ksrc = reinterpret_cast<const SrcT*>(p.key) + (int64_t)t * p.key_stride;
   const SrcT* vsrc = reinterpret_cast<const SrcT*>(p.value) + (int64_t)t * p.value_stride;
   for (int i = threadIdx.x; i < ngroups; i += blockDim.x) {
     const int h = i / groups_per_head;
     const int c = i - h * groups_per_head;
-    const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 16;
-    const int64_t src = (int64_t)h * p.head_dim + c * 16;
+    const int64_t dst = ((blk * p.num_kv_heads + h) * p.block_size + row) * p.head_dim + c * 4;
+    const int64_t src = (int64_t)h * p.head_dim + c * 4;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const SrcT* s = which ? vsrc : ksrc;
       const float scale = (which ? p.v_scales : p.k_scales)[blk * p.num_kv_heads + h];
-      uint32_t w[4];
+      uint32_t acc = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc |= ((uint32_t)i8_encode((float)s[src + q * 4 + b], scale) & 0xFFu) << (8 * b);
-        w[q] = acc;
-      }
-      st16((char*)(which ? p.v_pool : p.k_pool) + dst, u32x4{w[0], w[1], w[2], w[3]});
+      for (int b = 0; b < 4; ++b)
+        acc |= ((uint32_t)i8_encode((float)s[src + b], scale) & 0xFFu) << (8 * b);
+      *reinterpret_cast<uint32_t*>((char*)(which ? p.v_pool : p.k_pool) + dst) = acc;
     }
   }
 }
