@@ -623,6 +623,10 @@ def main():
         res = run_decode_bench(args, dev)
     res["probe_read_gbps"] = round(probe_read_gbps(dev), 1)
     res["probe_copy_bytes"] = probe_copy_once(dev)
+    # the decode kernel's rate against what a plain streaming read gets from HBM
+    dec = res["roofline"] if res["roofline"]["unit"] == "GB/s" else res.get("decode_roofline")
+    if dec is not None and res["probe_read_gbps"] > 0:
+        res["decode_kernel_pct_of_probe"] = round(100 * dec["achieved"] / res["probe_read_gbps"], 1)
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
