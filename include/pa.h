@@ -213,8 +213,11 @@ pa_status pa_swap_blocks(void* dst_pool, const void* src_pool, const int64_t* bl
  * its waves processes one or more segments, a segment being a run of
  * 32-token steps of one (sequence, KV head) pair.  A pair whose context is
  * cut into several segments gets partial results (unnormalised output,
- * running max, running sum) in the workspace, and a log-sum-exp reduce
- * merges them.  partition_size chooses the cut:
+ * running max, running sum), merged by log-sum-exp: in LDS by the attention
+ * kernel itself when all of the pair's segments fall in one workgroup's
+ * share of the work, else through the workspace by the reduce kernel (both
+ * merges sum in the same order and give the same bits).  partition_size
+ * chooses the cut:
  *   0   : balanced (the default) — the (sequence, KV head, 32-token step)
  *         units of the whole batch are cut into equal contiguous ranges, one
  *         per wave, from the lengths on the device; a pair is cut into at
@@ -280,9 +283,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_
 /*
  * The two stages of pa_decode, for callers that time or schedule them
  * separately.  pa_decode_attention runs the attention kernel: pairs
- * processed as one segment (and empty sequences, which get zeros) have
- * their final output in `out`, the others leave partial results and their
- * segment count in `workspace`.  pa_decode_reduce then merges those
+ * processed as one segment, pairs whose partials it merged on the CU, and
+ * empty sequences (which get zeros) have their final output in `out`; the
+ * others leave partial results and their segment count in `workspace`.
+ * pa_decode_reduce then merges those
  * partials into `out` (nothing to do for partition_size -1).  Both take
  * exactly the arguments of pa_decode; calling them in order on one stream
  * equals one pa_decode call.
