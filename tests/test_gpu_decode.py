@@ -62,6 +62,28 @@ def test_full_gqa_fixed_partitions(partition, full_cases):
     assert max_abs(out, ref) <= TOL[case.spec.q_dtype]
 
 
+@pytest.fixture(scope="module")
+def max_seqs_case():
+    """8000 sequences (the most one call plans in LDS) of 1-64 tokens: the plan takes most of
+    the workgroup's LDS, which leaves fewer slots for partials merged on the CU."""
+    spec = custom_spec("maxseqs_bf16_8_2_128_16", 8, 2, 128, 16, "bf16", "bf16")
+    lens = [int(x) for x in np.random.default_rng(7).integers(1, 65, size=8000)]
+    case = W.make_decode_case(spec, lens=lens)
+    return case, oracle_step(case)
+
+
+@pytest.mark.parametrize("partition", [0, 32, -1])
+def test_max_sequences(partition, max_seqs_case):
+    case, (ref, okp, ovp) = max_seqs_case
+    print(f"[decode parity] 8000 sequences, partition {partition}", flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(run.k_pool, "bf16"), okp)
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("partition", [32, 64, 160, 512, -1])
 def test_split_sizes_agree(partition):
     sub = W.make_decode_case("llama3_8b_gqa_bf16", lens=[1, 31, 32, 33, 200, 511, 512, 513, 2500])
