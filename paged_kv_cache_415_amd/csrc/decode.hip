@@ -875,8 +875,9 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
 // weight; the dims of the output are spread over the lanes.  The partial
 // rows are read eight at a time, the first eight together with m and l, so
 // a head costs two dependent memory round trips (its count, then the rest).
-// The attention kernel stores a count for every pair, 0 for an empty
-// sequence and 1 for a pair it finished without partials.
+// The attention kernel stores a count for every pair: 0 for an empty
+// sequence, 1 for a pair whose output it stored itself (one segment, or
+// partials merged on the CU).
 // ---------------------------------------------------------------------------
 template <int E>
 __device__ __forceinline__ void load_rows8(const float* po, int D, int first, int last, float (&x)[8][E]) {
