@@ -173,6 +173,24 @@ def test_fp8_every_code_decodes_exactly(q_dt):
     assert bad[0].size == 0, f"codes decoded wrongly: {[(int(codes[s*128+d]), out[s,0,d]) for s,_,d in zip(*bad)][:8]}"
 
 
+@pytest.mark.parametrize("partition", [0, 32, -1])
+def test_lengths_over_max_seq_len_are_clamped(partition):
+    """seq_lens above max_seq_len are clamped to it: the output is the attention over the first
+    max_seq_len tokens (the newest token of a longer sequence is scattered but not attended)."""
+    case = W.make_decode_case("llama3_8b_gqa_bf16", lens=[50, 150, 300, 128])
+    print(f"[decode parity] lengths clamped to 128, partition {partition}", flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode(partition_size=partition, max_seq_len=128)
+    _, kp, vp = oracle_step(case)
+    s = case.spec
+    clamped = np.minimum(case.seq_lens, 128).astype(np.int32)
+    ref = oracle.decode_attention(case.q, s.q_dtype, kp, vp, s.cache_dtype, case.block_tables,
+                                  clamped, s.scale, s.block_size, s.num_kv_heads, case.k_scale,
+                                  case.v_scale, v_cache_dtype=s.v_dtype)
+    assert max_abs(out, ref) <= TOL["bf16"]
+
+
 def test_zero_length_sequence_gives_zeros():
     case = W.make_decode_case("llama3_8b_gqa_bf16", lens=[40, 1, 17])
     run = DecodeRun(case)
