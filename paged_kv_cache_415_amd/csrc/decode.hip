@@ -217,6 +217,12 @@ struct MfmaDecode {
   static constexpr int VW = DPL * VEB / 4;      // dwords per V row piece
   static constexpr int KL = KF8 ? D / 64 : NC;  // 16-byte K loads per lane and tile
   static constexpr bool kDoubleBuffer = KF8 && VF8;
+  // 8-bit K rows (128 B at D = 128) are read a whole cache line per 8 lanes
+  // and put into the matrix-core layout (one row per lane) through 4 KB of
+  // the wave's LDS: whole-line requests carry twice the bytes of the
+  // half-line pieces the layout asks for (measured faster with 8-bit V,
+  // slower beside a 16-bit V)
+  static constexpr bool kStageK = KF8 && VF8 && D == 128 && BS >= 16 && !APPEND;
   // partials merged in LDS (not with the scatter folded in, whose registers
   // are at the limit of three waves per SIMD)
   static constexpr bool kLocalMerge = !APPEND;
@@ -294,7 +300,12 @@ struct MfmaDecode {
           if (t0 + c16 == len - 1) kt = nk;
         }
       }
-      if constexpr (KF8) {
+      if constexpr (kStageK) {
+        // instruction h: rows 8 h + 2 G + c16 / 8 of the tile, 16 bytes each
+        const char* kr = kt - (int64_t)c16 * D;   // row 0 of the tile
+#pragma unroll
+        for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16_nt(kr + (8 * h + 2 * G + (c16 >> 3)) * D + 16 * (c16 & 7));
+      } else if constexpr (KF8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) buf.k[tau][h] = ld16_nt(kt + 64 * h + 16 * G);
       } else {
@@ -327,7 +338,8 @@ struct MfmaDecode {
   };
 
   static __device__ __forceinline__ void compute(Buf& buf, State& st, const u32x4 (&qop)[NC],
-                                                 float qk_scale_log2, int len, int j) {
+                                                 float qk_scale_log2, int len, int j,
+                                                 char* kst = nullptr) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4;
     const int rel0 = j * kStep;
@@ -348,6 +360,20 @@ struct MfmaDecode {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       u32x4 ka[NC];
+      if constexpr (kStageK) {
+        // whole-line rows to the layout of the score product: row c16, the
+        // 16-byte pieces 4 h + G (pieces XOR-swizzled by row in LDS)
+        const int c16 = lane & 15;
+        char* sb = kst + tau * 2048;
+#pragma unroll
+        for (int h = 0; h < KL; ++h) {
+          const int r = 8 * h + 2 * G + (c16 >> 3);
+          *reinterpret_cast<u32x4*>(sb + r * 128 + (((c16 & 7) ^ (r & 7)) * 16)) = buf.k[tau][h];
+        }
+#pragma unroll
+        for (int h = 0; h < KL; ++h)
+          buf.k[tau][h] = *reinterpret_cast<const u32x4*>(sb + c16 * 128 + (((4 * h + G) ^ (c16 & 7)) * 16));
+      }
       if constexpr (KF == kFmtFp8) {
 #pragma unroll
         for (int h = 0; h < KL; ++h) {
@@ -540,6 +566,8 @@ struct MfmaDecode {
 
     const ctab_ptr trow = (ctab_ptr)(p.block_tables + (int64_t)s * p.max_blocks);
     const int nblk = (len + BS - 1) / BS;
+    extern __shared__ __align__(16) int plan_lds[];
+    char* kst = kStageK ? reinterpret_cast<char*>(plan_lds) + p.kstage_off + (threadIdx.x >> 6) * 4096 : nullptr;
 
     State st;
     st.m = -INFINITY;
@@ -560,12 +588,12 @@ struct MfmaDecode {
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 2, j1 - 1));
         if (j + 1 < j1) load(B, cur, p, kvh, j + 1);
-        compute(A, st, qop, p.qk_scale_log2, len, j);
+        compute(A, st, qop, p.qk_scale_log2, len, j, kst);
         if (j + 1 >= j1) break;
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 3, j1 - 1));
         if (j + 2 < j1) load(A, cur, p, kvh, j + 2);
-        compute(B, st, qop, p.qk_scale_log2, len, j + 1);
+        compute(B, st, qop, p.qk_scale_log2, len, j + 1, kst);
       }
     } else {
       // APPEND: the step that holds the newest token (the last step of the
@@ -576,7 +604,7 @@ struct MfmaDecode {
         const Ids nxt = ids(trow, nblk, min(j + 1, j1 - 1));
         Buf buf;
         load(buf, cur, p, kvh, j);
-        compute(buf, st, qop, p.qk_scale_log2, len, j);
+        compute(buf, st, qop, p.qk_scale_log2, len, j, kst);
         cur = nxt;
       }
       if constexpr (APPEND) {
@@ -647,6 +675,7 @@ template <int D, int BS>
 struct F32Decode {
   static constexpr int kWaves = D == 64 ? 12 : 8;  // resident waves per CU
   static constexpr bool kLocalMerge = false;
+  static constexpr bool kStageK = false;
   static __device__ void segment(const DecodeParams& p, int s, int kvh, int len, int j0, int j1,
                                  int part, int nparts, const LocalMerge&) {
     constexpr int E = D / 64;
@@ -1019,13 +1048,16 @@ hipError_t launch_persistent(const DecodeParams& p0, hipStream_t stream) {
   // LDS: the plan, then as many merge slots as fit (up to three per wave)
   const size_t plan = (size_t)((2 * p.num_seqs + 1 + 3) & ~3) * sizeof(int);
   const size_t per_slot = (size_t)p.group * p.head_dim * sizeof(float) + 33 * sizeof(float);
-  const size_t budget = lds_budget();
+  const size_t stage = Seg::kStageK ? (size_t)Seg::kWaves * 4096 : 0;   // 8-bit K staging
+  const size_t budget = lds_budget() - stage;
   int slots = 0;
   if (Seg::kLocalMerge && p.mode != kSplitNone && plan + 64 < budget)
     slots = (int)std::min<size_t>((size_t)3 * Seg::kWaves, (budget - plan - 64) / per_slot);
   p.local_slots = slots;
-  const size_t lds = plan + (size_t)((slots + 3) & ~3) * sizeof(int) + (size_t)slots * 32 * sizeof(float) +
-                     (size_t)slots * p.group * p.head_dim * sizeof(float);
+  const size_t merge_end = plan + (size_t)((slots + 3) & ~3) * sizeof(int) + (size_t)slots * 32 * sizeof(float) +
+                           (size_t)slots * p.group * p.head_dim * sizeof(float);
+  p.kstage_off = (int)merge_end;
+  const size_t lds = merge_end + stage;
   auto kernel = decode_kernel<Seg, QT>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), NT,

@@ -108,6 +108,7 @@ struct DecodeParams {
   int chunk;           // units: fixed partition length, or the shortest balanced range
   int max_parts;       // partial slots per (sequence, query head)
   int local_slots;     // LDS slots per workgroup for partials merged on the CU (0: none)
+  int kstage_off;      // byte offset in LDS of the waves' 8-bit K staging (4 KB per wave)
   int q_dtype;
   int cache_dtype;     // K pool element type
   int v_cache_dtype;   // V pool element type (the same, or QT beside an fp8 K pool)
