@@ -219,6 +219,7 @@ SWEEP = [
     ("f16", "f16", 4, 4, 64, 64),
     ("bf16", "fp8_e4m3", 16, 2, 128, 8),
     ("bf16", "fp8_e4m3", 8, 8, 64, 64),
+    ("bf16", "fp8_e4m3", 16, 4, 128, 64),
     ("f16", "f16", 32, 32, 128, 64),
     ("f32", "f32", 4, 2, 64, 8),
     ("f32", "f32", 2, 1, 128, 64),
@@ -296,6 +297,7 @@ INT8 = [
     ("f16", 4, 4, 64, 32),
     ("bf16", 16, 2, 128, 8),
     ("bf16", 8, 8, 64, 64),
+    ("f16", 16, 4, 128, 64),
 ]
 
 
