@@ -211,6 +211,10 @@ template <typename QT, int KF, int VF, int D, int BS, bool APPEND = false>
 struct MfmaDecode {
   static constexpr bool KF8 = KF != kFmtQ, VF8 = VF != kFmtQ;   // one byte per element
   static constexpr bool kBlockScales = KF == kFmtI8;             // K and V int8 together
+  // Rescaling slack (log2 units).  With int8 blocks the value operand is
+  // p * (block V scale) in QT; f16's range (65504) then needs p <= 1, i.e.
+  // the reference max always equal to the running max.
+  static constexpr float kSlack = (kBlockScales && __is_same(QT, _Float16)) ? 0.0f : kRescaleSlack;
   static constexpr int NC = D / 32;             // QK MFMAs per 16-token tile
   static constexpr int DPL = D / 16;            // value dims per lane = PV MFMAs per step
   static constexpr int KEB = KF8 ? 1 : 2, VEB = VF8 ? 1 : 2;
@@ -365,14 +369,21 @@ struct MfmaDecode {
         // 16-byte pieces 4 h + G (pieces XOR-swizzled by row in LDS)
         const int c16 = lane & 15;
         char* sb = kst + tau * 2048;
+        // the buffer is the wave's own: the last step's reads of it (by
+        // other lanes of this wave) come before it is overwritten
+        if (tau == 0) wave_lds_acquire();
 #pragma unroll
         for (int h = 0; h < KL; ++h) {
           const int r = 8 * h + 2 * G + (c16 >> 3);
           *reinterpret_cast<u32x4*>(sb + r * 128 + (((c16 & 7) ^ (r & 7)) * 16)) = buf.k[tau][h];
         }
+        // each lane reads pieces other lanes of the wave stored just above
+        wave_lds_release();
+        wave_lds_acquire();
 #pragma unroll
         for (int h = 0; h < KL; ++h)
           buf.k[tau][h] = *reinterpret_cast<const u32x4*>(sb + c16 * 128 + (((4 * h + G) ^ (c16 & 7)) * 16));
+        if (tau == 1) wave_lds_release();
       }
       if constexpr (KF == kFmtFp8) {
 #pragma unroll
@@ -412,10 +423,10 @@ struct MfmaDecode {
     smax = xor_max(smax, 16);
     smax = xor_max(smax, 32);
     // Lazy rescaling: the reference max moves (and the accumulators are
-    // rescaled) only when some head's max exceeds it by more than
-    // kRescaleSlack, so probabilities stay <= 2^kRescaleSlack.  The first
-    // step always sets it (st.m starts at -inf; every step has a valid token).
-    if (__builtin_amdgcn_ballot_w64(smax > st.m + kRescaleSlack) != 0) {
+    // rescaled) only when some head's max exceeds it by more than the slack,
+    // so probabilities stay <= 2^slack.  The first step always sets it (st.m
+    // starts at -inf; every step has a valid token).
+    if (__builtin_amdgcn_ballot_w64(smax > st.m + kSlack) != 0) {
       const float m_new = fmaxf(st.m, smax);
       const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
       st.m = m_new;

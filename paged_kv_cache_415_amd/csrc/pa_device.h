@@ -144,6 +144,21 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
   return a * b;
 }
 
+// ------------------------------------------------- wave-level LDS order
+
+// Order LDS accesses of different lanes of one wave (a wave's LDS
+// instructions execute in order, so these cost no instruction): release
+// after stores that other lanes of the wave will read, acquire before those
+// reads, and before overwriting data that other lanes read.
+__device__ __forceinline__ void wave_lds_release() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ void wave_lds_acquire() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------ wave reductions
 
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }

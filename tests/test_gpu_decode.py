@@ -84,6 +84,59 @@ def test_max_sequences(partition, max_seqs_case):
     assert max_abs(out, ref) <= TOL["bf16"]
 
 
+@pytest.fixture(scope="module")
+def max_seqs_8bit_cases():
+    """The 8000-sequence plan with 8-bit caches at head_dim 128, whose waves also
+    take 4 KB each of LDS for whole-line K staging, placed after the merge slots."""
+    lens = [int(x) for x in np.random.default_rng(8).integers(1, 65, size=8000)]
+    out = {}
+    for c_dt in ("fp8_e4m3", "int8"):
+        spec = custom_spec(f"maxseqs_{c_dt}_8_2_128_16", 8, 2, 128, 16, "bf16", c_dt)
+        case = W.make_decode_case(spec, lens=lens)
+        out[c_dt] = (case, oracle_step(case))
+    return out
+
+
+@pytest.mark.parametrize("c_dt", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("partition", [0, 512, -1])
+def test_max_sequences_8bit(c_dt, partition, max_seqs_8bit_cases):
+    case, (ref, okp, ovp) = max_seqs_8bit_cases[c_dt]
+    print(f"[decode parity] 8000 sequences, {c_dt}, partition {partition}", flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(run.k_pool, c_dt), okp)
+    assert np.array_equal(W.torch_to_bits(run.v_pool, c_dt), ovp)
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("partition", [0, 32, -1])
+def test_int8_rows_past_the_end_never_count(partition):
+    """int8 has no NaN to poison unwritten rows with: they hold the code -128
+    (never written by the quantiser).  With every query -1 and every K code of
+    a valid row >= 0, a poisoned K row would give by far the largest logit and
+    pull the output to -128 x the V scale, so a read past a sequence's end (or
+    into table padding) shows as a large error instead of a NaN."""
+    spec = custom_spec("int8_past_end", 8, 2, 128, 16, "bf16", "int8")
+    case = W.make_decode_case(spec, lens=[1, 15, 17, 31, 33, 100, 257, 1000])
+    kp = case.k_pool.view(np.int8).copy()
+    kp[kp != -128] = np.abs(kp[kp != -128])         # valid K codes >= 0
+    case.k_pool = kp.view(np.uint8)
+    case.new_k = W.to_bits(np.abs(W.bits_to_torch(case.new_k, "bf16").float().numpy()), "bf16")
+    case.q = W.to_bits(-np.ones(W.bits_to_torch(case.q, "bf16").shape, np.float32), "bf16")
+    ref, okp, _ = oracle_step(case)
+    assert (kp.view(np.int8) == -128).any()
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode(partition_size=partition)
+    assert np.array_equal(W.torch_to_bits(run.k_pool, "int8"), okp)
+    assert max_abs(out, ref) <= TOL["bf16"]
+    # the oracle's output stays within the valid V values; -128 x scale would not
+    bound = float(np.max(case.v_block_scales)) * 127
+    assert float(np.abs(ref).max()) <= bound
+
+
 @pytest.mark.parametrize("partition", [32, 64, 160, 512, -1])
 def test_split_sizes_agree(partition):
     sub = W.make_decode_case("llama3_8b_gqa_bf16", lens=[1, 31, 32, 33, 200, 511, 512, 513, 2500])
@@ -461,3 +514,26 @@ def test_decode_any_scale(scale):
                  max_seq_len=run.max_len, workspace=ws)
     torch.cuda.synchronize()
     assert max_abs(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_int8_f16_queries_large_value_scales(partition):
+    """f16 queries over an int8 cache whose V values reach about 6e4 (block V
+    scales near 470): the value operand p x scale must stay inside f16's range
+    while the running max moves (queries x 6 so that logits spread widely)."""
+    spec = custom_spec("int8_f16_big_v", 8, 2, 128, 16, "f16", "int8")
+    case = W.make_decode_case(spec, lens=[3, 40, 130, 700, 1500])
+    grow = np.float32(1.2e4)
+    case.v_block_scales = (case.v_block_scales * grow).astype(np.float32)
+    nv = W.bits_to_torch(case.new_v, "f16").float().numpy() * grow
+    case.new_v = W.to_bits(np.clip(nv, -6e4, 6e4), "f16")
+    case.q = W.to_bits(W.bits_to_torch(case.q, "f16").float().numpy() * 6, "f16")
+    ref, _, ovp = oracle_step(case)
+    assert float(np.max(case.v_block_scales)) > 300
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode(partition_size=partition)
+    assert np.array_equal(W.torch_to_bits(run.v_pool, "int8"), ovp)
+    # relative to the values' size: f16 keeps 11 significant bits
+    err = max_abs(out, ref)
+    assert err <= TOL["f16"] * float(np.abs(ref).max()) / 4, err
