@@ -281,6 +281,30 @@ pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): it takes no workspace argument and calls no allocating
+ * routine.  The split-KV partials go to a device array inside the library,
+ * pa_decode_noalloc_max_workspace_bytes() (64 MiB) long; each GPU the
+ * library runs on holds its own copy from the first call on that device
+ * until the process ends.  The caller still owns out, q, the pools, tables
+ * and lengths.  Arguments, results and limits are those of pa_decode (same
+ * kernels, same bits); a call whose pa_decode_workspace_bytes(...) exceeds
+ * the array returns PA_ERR_WORKSPACE and enqueues nothing.  The array keeps
+ * the last call's contents; nothing in it has to start at zero.  Every call
+ * on one GPU shares that GPU's array, so calls that can overlap on one GPU
+ * (concurrent streams, several host threads) race and must be ordered by
+ * the caller.
+ */
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                            int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                            int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            float k_scale, float v_scale, int32_t partition_size, void* stream);
+size_t pa_decode_noalloc_max_workspace_bytes(void);
+
+/*
  * The two stages of pa_decode, for callers that time or schedule them
  * separately.  pa_decode_attention runs the attention kernel: pairs
  * processed as one segment, pairs whose partials it merged on the CU, and

@@ -67,6 +67,10 @@ def _load() -> ctypes.CDLL:
     for name in ("pa_decode", "pa_decode_attention", "pa_decode_reduce"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = i32
+    lib.pa_decode_noalloc.argtypes = dec[:19] + [vp]
+    lib.pa_decode_noalloc.restype = i32
+    lib.pa_decode_noalloc_max_workspace_bytes.argtypes = []
+    lib.pa_decode_noalloc_max_workspace_bytes.restype = sz
     for name in ("pa_decode_kv", "pa_decode_attention_kv", "pa_decode_reduce_kv"):
         getattr(lib, name).argtypes = dec[:16] + [i32] + dec[16:]
         getattr(lib, name).restype = i32
@@ -361,6 +365,28 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_
                  max_seq_len, k_scale, v_scale, partition_size, workspace, stream)
 
 
+def pa_decode_noalloc(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                      max_seq_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                      partition_size: int = 0, stream=None) -> None:
+    """pa_decode without a workspace argument: the split partials go to the
+    library's own device array (for callers that cannot allocate; see pa.h)."""
+    s, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if v_pool.shape[1:] != k_pool.shape[1:] or _dtype(k_pool) != _dtype(v_pool):
+        raise ValueError("K and V pools must match in block shape and type")
+    _check(_lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                  _ptr(seq_lens), float(scale), bs, s, hq, hkv, d,
+                                  block_tables.shape[1], int(max_seq_len), _dtype(q), _dtype(k_pool),
+                                  float(k_scale), float(v_scale), int(partition_size),
+                                  _stream(stream)))
+
+
+def pa_decode_noalloc_max_workspace_bytes() -> int:
+    return _lib.pa_decode_noalloc_max_workspace_bytes()
+
+
 def pa_decode_kv(out, q, k_pool, v_pool, block_tables, seq_lens, scale: float, max_seq_len: int = 0,
                  k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
                  workspace=None, stream=None) -> None:
@@ -468,7 +494,8 @@ __all__ = [
     "pa_decode_reduce_kv", "pa_reshape_and_cache_int8", "pa_decode_int8", "pa_decode_attention_int8",
     "pa_decode_reduce_int8", "pa_decode_append", "pa_decode_attention_append", "pa_copy_blocks", "pa_copy_blocks_partial", "pa_copy_blocks_layers",
     "layer_pool_pointers",
-    "pa_swap_blocks", "pa_decode", "pa_decode_attention",
+    "pa_swap_blocks", "pa_decode", "pa_decode_noalloc", "pa_decode_noalloc_max_workspace_bytes",
+    "pa_decode_attention",
     "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",
     "pa_decode_workspace_bytes", "decode_workspace", "pa_probe_read", "pa_probe_copy",
     "PagedAttentionError", "library", "LIB_PATH",

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/pa.h"
 #include "../../include/pa_probe.h"
@@ -148,6 +149,38 @@ pa_status plan_decode(int num_seqs, int num_q_heads, int num_kv_heads, int head_
   return PA_OK;
 }
 
+// Workspace of pa_decode_noalloc, for callers that cannot allocate: a
+// file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends).  In host code `scratch` names a host-side stand-in;
+// kernels get the device address that hipGetSymbolAddress returns, looked up
+// once per device on the first call made on it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+pa_status scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device ordinal %d >= %d", dev, kMaxDevices);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    if (slot.err == hipSuccess && slot.ptr == nullptr) slot.err = hipErrorInvalidSymbol;
+  });
+  if (slot.err != hipSuccess) return hip_status(slot.err, "hipGetSymbolAddress(scratch)");
+  *out = slot.ptr;
+  return PA_OK;
+}
+
 enum class Stage { kBoth, kAttention, kReduce };
 
 pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
@@ -160,7 +193,7 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
                       void* stream, const float* k_scales = nullptr,
                       const float* v_scales = nullptr, const void* new_k = nullptr,
                       const void* new_v = nullptr, int64_t new_k_stride = 0,
-                      int64_t new_v_stride = 0) {
+                      int64_t new_v_stride = 0, bool use_scratch = false) {
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
@@ -198,6 +231,17 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer (tensors need 16 bytes, int arrays 4)");
+  if (use_scratch && plan.workspace > 0) {
+    // the no-allocation entry: the library's own device array, never hipMalloc
+    if (plan.workspace > kScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "this call needs %zu bytes of split-KV workspace; the no-allocation entry holds "
+                  "at most %zu (use pa_decode with a caller workspace)",
+                  plan.workspace, kScratchBytes);
+    st = scratch_address(&workspace);
+    if (st != PA_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (plan.workspace > 0) {
     if (!workspace || workspace_bytes < plan.workspace)
       return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace,
@@ -508,6 +552,21 @@ pa_status pa_decode(void* out, const void* q, const void* k_pool, const void* v_
                      max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, cache_dtype, k_scale,
                      v_scale, partition_size, workspace, workspace_bytes, stream);
 }
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                            int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                            int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                            float k_scale, float v_scale, int32_t partition_size, void* stream) {
+  return decode_impl(Stage::kBoth, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                     block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, nullptr, 0, stream, nullptr, nullptr, nullptr,
+                     nullptr, 0, 0, /*use_scratch=*/true);
+}
+
+size_t pa_decode_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 
 pa_status pa_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, const int32_t* seq_lens, float scale,

@@ -267,3 +267,24 @@ def test_prefill_rejects_before_launch(lib, kw, code):
 def test_probe_rejects_bad_sizes(lib):
     assert lib.pa_probe_read(None, 16, None, None) == INVALID
     assert lib.pa_probe_copy(ctypes.c_void_p(256), ctypes.c_void_p(512), 17, None) == INVALID
+
+
+def test_noalloc_decode_rejects_a_batch_beyond_its_array(lib):
+    """pa_decode_noalloc has no workspace argument: a call whose split-KV
+    partials would not fit the library's array fails before any launch."""
+    fake = ctypes.c_void_p(256)           # never dereferenced: the check fails first
+    cap = lib.pa_decode_noalloc_max_workspace_bytes()
+    assert cap == 64 << 20
+    need = lib.pa_decode_workspace_bytes(256, 32, 8, 128, 16, 8192, 0)
+    assert need > cap
+    st = lib.pa_decode_noalloc(fake, fake, fake, fake, fake, fake, 0.1, 16, 256, 32, 8, 128, 512,
+                               8192, BF16, BF16, 1.0, 1.0, 0, None)
+    assert st == WORKSPACE
+    assert b"no-allocation" in lib.pa_last_error()
+    # argument checks come first, as in pa_decode
+    assert lib.pa_decode_noalloc(None, None, None, None, None, None, 0.1, 16, 4, 8, 2, 96, 8, 128,
+                                 BF16, BF16, 1.0, 1.0, 0, None) == UNSUPPORTED
+    assert lib.pa_decode_noalloc(None, None, None, None, None, None, 0.1, 16, 4, 8, 2, 128, 8, 128,
+                                 BF16, BF16, 1.0, 1.0, 0, None) == INVALID
+    assert lib.pa_decode_noalloc(None, None, None, None, None, None, 0.1, 16, 0, 8, 2, 128, 8, 128,
+                                 BF16, BF16, 1.0, 1.0, 0, None) == OK
