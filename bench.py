@@ -1,6 +1,6 @@
 """Benchmark of the paged KV-cache decode path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--rotate R]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all] [--rotate R]
 
 One step is one pass of the decode hot path over one batch: scatter of each
 sequence's newest K/V into its pool slot (pa_reshape_and_cache), then paged
@@ -9,23 +9,31 @@ partials (pa_decode_reduce), all on torch's current stream.  For the mixed
 workload a step is copy-on-write (pa_copy_blocks), the scatter of every new
 token, the causal prefill chunks (pa_prefill_chunk) and the decodes.
 
-The default workload is the Llama-2-7B-shaped layer (64 sequences, 32/32
-heads, head_dim 128, block 16, lengths U[128, 2048], fp16).  Throughput is
-effective KV bytes per second: sum over sequences of len * Hkv * D * (bytes
-of K + bytes of V), the K and V the method must read, divided by the time
-of the whole step.  Batch layouts (lengths, shuffled physical ids, tables,
-slots) come from workloads.py; element values are drawn on the device with
-torch's seeded generator (same distributions).  R batches with separate
+By default (--config all) the headline is the largest single-GPU decode
+workload, the Llama-3-8B-shaped GQA layer (256 sequences, 32/8 heads,
+head_dim 128, block 16, lognormal lengths, bf16); the same JSON line carries
+the Llama-2-7B-shaped MHA layer, the 70B-shaped fp8 layer (512-token
+partitions), the mixed prefill + decode step and the tiny fp32 case under
+"configs", each with its own step time, rate and roofline.  --config NAME
+runs one workload alone.
+
+Throughput is effective KV bytes per second: sum over sequences of len * Hkv
+* D * (bytes of K + bytes of V), the K and V the method must read, divided by
+the time of the whole step.  Batch layouts (lengths, shuffled physical ids,
+tables, slots) come from workloads.py; element values are drawn on the device
+with torch's seeded generator (same distributions).  R batches with separate
 pools are rotated so that no step finds its KV in the 256 MB last-level
 cache.
 
-After the timed region the same steps are also replayed from captured HIP
-graphs (one per batch) and that rate is reported beside the eager one.
+The CPU baseline runs the fp64 oracle, as it stands, on bounded samples of
+the same workloads (generated on the CPU by workloads.py), before the GPU is
+touched: on every host core this process may use (one oracle process per
+core, sequences or heads spread over them) and, for the two smallest
+workloads, on one thread.
 
 Printed: one JSON line with the step rate, a roofline object for the
 dominant kernel (its average duration measured with HIP events on the
-launch stream) and a CPU baseline (the fp64 oracle on a bounded sample, on
-this host's cores).
+launch stream) and the CPU baseline.
 """
 
 from __future__ import annotations
@@ -51,8 +59,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama2_7b_mha_f16",
-                    help="llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
+    ap.add_argument("--config", default="all",
+                    help="all (headline llama3_8b_gqa_bf16 plus the other workloads) | "
+                         "llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
                          "| llama3_8b_int8kv "
                          "| tiny_f32 "
                          "| mixed_prefix_bf16")
@@ -63,9 +72,12 @@ def parse():
                     help="decode workloads: run with this block size (8, 16, 32, 64) instead; a "
                          "fixed pool keeps its token capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU time budget of the oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay comparison")
     return ap.parse_args()
+
+
+HEADLINE = "llama3_8b_gqa_bf16"
+SUB_CONFIGS = ["llama2_7b_mha_f16", "llama3_70b_fp8kv", "mixed_prefix_bf16", "tiny_f32"]
 
 
 # ---------------------------------------------------------------------------
@@ -125,13 +137,16 @@ class DecodeBatch:
         self.out = torch.empty_like(self.q)
 
 
-def run_decode_bench(args, dev):
+def run_decode_bench(args, dev, name: str, extras: bool = True):
+    """One decode workload: the timed steps, then (with ``extras``) the same
+    steps with the scatter folded into the decode kernel and replayed from
+    captured HIP graphs, for comparison."""
     import numpy as np
     import torch
     import paged_kv_cache_415_amd as pa
     import workloads as W
 
-    spec = W.DECODE_SPECS[args.config]
+    spec = W.DECODE_SPECS[name]
     if args.block_size is not None and args.block_size != spec.block_size:
         import dataclasses
         pool = spec.pool
@@ -214,7 +229,7 @@ def run_decode_bench(args, dev):
     # After the timed region: the same steps with the scatter folded into the
     # decode kernel (two launches), for comparison
     appended = None
-    if can_append:
+    if can_append and extras:
         for i in range(args.warmup):
             step_append(batches[i % len(batches)])
         torch.cuda.synchronize()
@@ -230,6 +245,8 @@ def run_decode_bench(args, dev):
     # (one graph per batch), as a serving loop replays captured decode steps.
     graph_ms = None
     try:
+        if not extras or args.no_graph:
+            raise RuntimeError("not requested")
         graphs = []
         for b in batches:
             g = torch.cuda.CUDAGraph()
@@ -245,7 +262,8 @@ def run_decode_bench(args, dev):
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     except RuntimeError as exc:
-        print(f"bench.py: hipGraph replay skipped ({exc})", file=sys.stderr)
+        if str(exc) != "not requested":
+            print(f"bench.py: hipGraph replay skipped ({exc})", file=sys.stderr)
     assert not torch.isnan(b0.out).any(), "NaN in decode output"
 
     eff = W.effective_kv_bytes(lay.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
@@ -272,8 +290,8 @@ def run_decode_bench(args, dev):
                      else "decode_kernel<F32Decode>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": (decode_traffic_bytes()
-                                 if spec.name == "llama2_7b_mha_f16" and spec.block_size == 16 else None),
+                     "traffic": (decode_traffic_bytes(spec.name)
+                                 if args.block_size is None and args.partition is None else None),
                      "traffic_unit": "bytes per launch",
                      "algorithmic_bytes_per_launch": eff,
                      "avg_launch_ms": round(attn_avg, 5)},
@@ -355,28 +373,24 @@ def run_mixed_bench(args, dev):
     elapsed = time.perf_counter() - t0
     # the same step captured as one HIP graph with the prefill and the decode
     # on forked streams (timed after the eager measurement above)
-    side = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step(side=side)
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        g.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(side=side)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step = elapsed * 1e3 / args.steps
-    # causal (query, key) pairs of the chunks: query i of a chunk of L in a
-    # context of n sees n - L + i + 1 keys; 4 * D flops per pair and head
-    pairs_per_head = 0
-    for f in range(len(case.prefill_lens)):
-        n, L = int(case.prefill_lens[f]), int(np.diff(case.query_start_loc)[f])
-        pairs_per_head += sum(n - L + i + 1 for i in range(L))
-    flops = pairs_per_head * s.num_q_heads * 4 * s.head_dim
+    flops = mixed_prefill_flops(case)
     eff = W.effective_kv_bytes(case.decode_lens, s.num_kv_heads, s.head_dim, dt)
     tflops = flops / (pre_ms * 1e-3) / 1e12
     dec_gbps = eff / (dec_ms * 1e-3) / 1e9
@@ -388,14 +402,20 @@ def run_mixed_bench(args, dev):
                    "decode_seqs": int(len(case.decode_lens)), "cow_pairs": int(len(case.cow_pairs))},
         "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(tflops, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": decode_traffic_bytes(s.name, "prefill"),
+                     "traffic_unit": "bytes per launch",
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(pre_ms, 5)},
         "decode_roofline": {"bound": "hbm", "kernel": "decode_kernel<MfmaDecode>",
                             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                            "traffic": decode_traffic_bytes(s.name, "decode"),
+                            "traffic_unit": "bytes per launch",
                             "algorithmic_bytes_per_launch": eff, "avg_launch_ms": round(dec_ms, 5)},
+        "prefill_flops": flops, "effective_kv_bytes_per_step": eff,
+        "prefill_tflops": round(tflops, 2), "decode_gbps": round(dec_gbps, 1),
         "prefill_tokens_per_s": round(int(case.query_start_loc[-1]) / (pre_ms * 1e-3), 1),
-        "hipgraph_two_stream_ms_per_step": round(graph_ms, 5),
+        "hipgraph_two_stream_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "decode_tokens_per_s_per_layer": round(len(case.decode_lens) / (ms_step * 1e-3), 1),
     }
 
@@ -493,17 +513,24 @@ def run_block_ops_bench(dev, iters: int = 20) -> dict:
 # HBM traffic of the decode kernel from committed rocprofv3 counter runs
 # ---------------------------------------------------------------------------
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_mfma_llama2_7b_mha_f16.md")
-KERNEL_SOURCES = ["decode.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"]
+KERNEL_SOURCES = {"decode": ["decode.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"],
+                  "prefill": ["prefill.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"]}
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of the decode sources with comments and blank lines removed (a
+def traffic_profile(name: str) -> str:
+    """The committed rocprofv3 summary that records a workload's counters."""
+    if name == "mixed_prefix_bf16":
+        return os.path.join(ROOT, "profiles", "prefill_mfma_mixed_prefix_bf16.md")
+    return os.path.join(ROOT, "profiles", f"decode_mfma_{name}.md")
+
+
+def kernel_sources_sha256(kind: str = "decode") -> str:
+    """Hash of a kernel's sources with comments and blank lines removed (a
     comment edit does not change the kernel the counters were taken on)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "paged_kv_cache_415_amd", "csrc", f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -513,19 +540,20 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_traffic_bytes():
-    """Bytes per launch from the FETCH_SIZE / WRITE_SIZE runs recorded in
-    profiles/, each scaled by what the same counter reads for a copy of known
-    size; None when the counters were taken on other kernel sources."""
+def decode_traffic_bytes(name: str, kind: str = "decode"):
+    """HBM bytes per launch of the workload's decode (or prefill) kernel from
+    the FETCH_SIZE / WRITE_SIZE runs recorded in profiles/, each scaled by what
+    the same counter reads for a copy of known size; None when no counters are
+    recorded or they were taken on other kernel sources."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(traffic_profile(name)).read()
     except OSError:
         return None
-    line = next((l for l in text.splitlines() if l.startswith("decode_traffic:")), None)
+    line = next((l for l in text.splitlines() if l.startswith(f"{kind}_traffic:")), None)
     if line is None:
         return None
     kv = dict(item.split("=", 1) for item in line.split()[1:])
-    if kv.get("sources_sha256") != kernel_sources_sha256():
+    if kv.get("sources_sha256") != kernel_sources_sha256(kind):
         return None
     copy_bytes = float(kv["copy_bytes"])
     fetch = float(kv["fetch_kib"]) * copy_bytes / float(kv["copy_fetch_kib"])
@@ -569,39 +597,207 @@ def probe_read_gbps(dev, nbytes=4 << 30, iters=10):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle, as it stands, on a bounded sample
+# CPU baseline: the oracle, as it stands, on bounded samples, on the host's cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(args):
+# Samples (CPU-generated by workloads.py with the bench's seeds): sequences
+# taken from the front of each workload's seeded batch.
+CPU_SAMPLES = {"llama3_8b_gqa_bf16": 64, "llama2_7b_mha_f16": 16, "llama3_70b_fp8kv": 32,
+               "tiny_f32": None}
+MIXED_SAMPLE = dict(num_forks=4, num_decode=28)
+_CPU = {}          # inputs shared with the forked oracle processes
+
+
+def host_cores() -> int:
+    """Cores this process may run on, capped by OMP_NUM_THREADS when it is set."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    global _LIMIT
+    _LIMIT = threadpool_limits(limits=1)
+
+
+def _oracle_task(task):
+    """One oracle call on one forked process: the decode of a set of
+    sequences, or the prefill of one chunk over all heads."""
+    import oracle
+    kind, key, idx = task
+    c = _CPU[key]
+    if kind == "decode":
+        s = c.spec
+        oracle.decode_attention(c.q[idx], s.q_dtype, c.k_pool, c.v_pool, s.cache_dtype,
+                                c.block_tables[idx], c.seq_lens[idx], s.scale, s.block_size,
+                                s.num_kv_heads, c.k_scale, c.v_scale, v_cache_dtype=s.v_dtype,
+                                k_block_scales=c.k_block_scales, v_block_scales=c.v_block_scales)
+    elif kind == "mixed_decode":
+        s = c.spec
+        oracle.decode_attention(c.q_decode[idx], s.dtype, c.k_pool, c.v_pool, s.dtype,
+                                c.decode_tables[idx], c.decode_lens[idx], s.scale, s.block_size,
+                                s.num_kv_heads)
+    else:    # one prefill chunk: rows of chunk idx[0], every head
+        s = c.spec
+        f = int(idx[0])
+        qsl = c.query_start_loc
+        lo, hi = int(qsl[f]), int(qsl[f + 1])
+        oracle.prefill_chunk_attention(c.q_chunk[lo:hi], s.dtype, [0, hi - lo], c.k_pool, c.v_pool,
+                                       s.dtype, c.prefill_tables[f:f + 1], c.prefill_lens[f:f + 1],
+                                       s.scale, s.block_size, s.num_kv_heads)
+    return 0
+
+
+def cpu_baseline(args) -> dict:
+    """The oracle on bounded samples of the workloads, timed on this host
+    before the GPU is initialised: every core (one forked oracle process per
+    core, one BLAS thread each) and, for the tiny and the Llama-2-7B-shaped
+    samples, one thread."""
+    import multiprocessing as mp
+    import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
 
-    name = args.config if args.config in W.DECODE_SPECS else "llama3_8b_gqa_bf16"
-    spec = W.DECODE_SPECS[name]
-    nseq = 16
-    case = W.make_decode_case(spec, rep=0, num_seqs=nseq)
-    eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
-                               spec.v_dtype)
-    if spec.cache_dtype == "int8":
-        eff += W.block_scale_bytes(case.seq_lens, spec.num_kv_heads, spec.block_size)
-    passes, spent = 0, 0.0
-    with threadpool_limits(1):
-        while spent < args.cpu_seconds or passes == 0:
+    cores = host_cores()
+    out = {"kind": "oracle", "cores": cores, "cpu_model": cpu_model(),
+           "affinity_cores": len(os.sched_getaffinity(0)), "configs": {}}
+    t_gen = time.perf_counter()
+    tasks = {}
+    for name, n in CPU_SAMPLES.items():
+        case = W.make_decode_case(name, rep=0, num_seqs=n)
+        _CPU[name] = case
+        order = np.argsort(-case.seq_lens.astype(np.int64), kind="stable")   # longest first
+        tasks[name] = [("decode", name, np.array([int(i)])) for i in order]
+    mixed = W.make_mixed_case(**MIXED_SAMPLE)
+    kp, vp = oracle.copy_blocks(mixed.k_pool, mixed.v_pool, mixed.cow_pairs)
+    mixed.k_pool, mixed.v_pool = oracle.reshape_and_cache(
+        kp, vp, mixed.spec.dtype, mixed.new_k, mixed.new_v, mixed.spec.dtype, mixed.slot_mapping,
+        mixed.spec.block_size)
+    _CPU["mixed"] = mixed
+    out["generation_s"] = round(time.perf_counter() - t_gen, 2)
+
+    ctx = mp.get_context("fork")       # the GPU is not initialised yet
+    with ctx.Pool(cores, initializer=_one_blas_thread) as pool:
+        pool.map(_oracle_task, tasks["tiny_f32"][:1])      # start-up of the workers
+        for name in CPU_SAMPLES:
+            case = _CPU[name]
+            spec = case.spec
             t0 = time.perf_counter()
-            oracle.decode_attention(case.q, spec.q_dtype, case.k_pool, case.v_pool,
-                                    spec.cache_dtype, case.block_tables, case.seq_lens,
-                                    spec.scale, spec.block_size, spec.num_kv_heads,
-                                    case.k_scale, case.v_scale, v_cache_dtype=spec.v_dtype,
-                                    k_block_scales=case.k_block_scales,
-                                    v_block_scales=case.v_block_scales)
-            spent += time.perf_counter() - t0
-            passes += 1
-    return {"value": round(eff * passes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"fp64 oracle decode of the first {nseq} sequences of the {name} batch "
-                      f"({int(case.seq_lens.sum())} context tokens, all heads), {passes} passes "
-                      f"in {spent:.1f} s, BLAS limited to 1 thread"}
+            pool.map(_oracle_task, tasks[name], chunksize=1)
+            dt = time.perf_counter() - t0
+            eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim,
+                                       spec.cache_dtype, spec.v_dtype)
+            out["configs"][name] = {
+                "sample": f"first {len(case.seq_lens)} sequences of the seeded batch "
+                          f"({int(case.seq_lens.sum())} context tokens, all heads)",
+                "oracle_wall_s": round(dt, 4), "sample_effective_bytes": eff,
+                "oracle_gbps": round(eff / dt / 1e9, 4)}
+        # mixed step: every prefill chunk (one process each) and the decodes
+        ms = mixed.spec
+        pre = [("prefill", "mixed", np.array([f])) for f in range(len(mixed.prefill_lens))]
+        dec = [("mixed_decode", "mixed", np.array([int(i)]))
+               for i in np.argsort(-mixed.decode_lens.astype(np.int64), kind="stable")]
+        t0 = time.perf_counter()
+        pool.map(_oracle_task, pre + dec, chunksize=1)
+        dt = time.perf_counter() - t0
+    flops = mixed_prefill_flops(mixed)
+    dec_eff = W.effective_kv_bytes(mixed.decode_lens, ms.num_kv_heads, ms.head_dim, ms.dtype)
+    out["configs"]["mixed_prefix_bf16"] = {
+        "sample": f"{len(mixed.prefill_lens)} of the 16 prefill chunks (512 tokens over a "
+                  f"1,536-token context, all heads) and {len(mixed.decode_lens)} of the 112 decodes",
+        "oracle_wall_s": round(dt, 4), "sample_prefill_flops": flops,
+        "sample_decode_effective_bytes": dec_eff,
+        "oracle_tflops_prefill_and_decode": round(flops / dt / 1e12, 5)}
+
+    # one thread: the tiny workload (repeated for at least a second) and the
+    # Llama-2-7B-shaped sample
+    one = {}
+    with threadpool_limits(1):
+        for name, min_s in (("tiny_f32", 1.0), ("llama2_7b_mha_f16", 0.0)):
+            case = _CPU[name]
+            spec = case.spec
+            idx = np.arange(len(case.seq_lens))
+            passes, spent = 0, 0.0
+            while passes == 0 or spent < min_s:
+                t0 = time.perf_counter()
+                _oracle_task(("decode", name, idx))
+                spent += time.perf_counter() - t0
+                passes += 1
+            eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim,
+                                       spec.cache_dtype, spec.v_dtype)
+            one[name] = {"oracle_s_per_pass": round(spent / passes, 6), "passes": passes,
+                         "oracle_gbps": round(eff / (spent / passes) / 1e9, 5)}
+    out["one_thread"] = one
+    _CPU.clear()
+    head = out["configs"][HEADLINE]
+    out["value"] = head["oracle_gbps"]
+    out["unit"] = "GB/s"
+    out["sample"] = (f"fp64 oracle decode of the first {CPU_SAMPLES[HEADLINE]} sequences of the "
+                     f"{HEADLINE} batch on {cores} cores (one oracle process per core, one BLAS "
+                     f"thread each, sequences longest first), {head['oracle_wall_s']} s wall; "
+                     f"the other workloads' samples under 'configs', one-thread runs under "
+                     f"'one_thread'")
+    return out
+
+
+def mixed_prefill_flops(case) -> int:
+    """Causal (query, key) pairs of the chunks x 4 D flops x query heads: query
+    i of a chunk of L tokens in a context of n sees n - L + i + 1 keys."""
+    import numpy as np
+    s = case.spec
+    pairs = 0
+    for f in range(len(case.prefill_lens)):
+        n, L = int(case.prefill_lens[f]), int(np.diff(case.query_start_loc)[f])
+        pairs += L * (n - L) + L * (L + 1) // 2
+    return pairs * s.num_q_heads * 4 * s.head_dim
+
+
+def compare_cpu_gpu(cpu: dict, gpu: dict) -> None:
+    """Oracle seconds beside GPU microseconds per step for each workload (the
+    oracle's seconds scaled from its sample to the full batch by bytes, or
+    flops for the mixed step), and their ratio."""
+    for name, c in cpu.get("configs", {}).items():
+        g = gpu.get(name)
+        if g is None:
+            continue
+        if name == "mixed_prefix_bf16":
+            full = g["prefill_flops"] + 0.0
+            sample = c["sample_prefill_flops"]
+            note = "prefill flops"
+        else:
+            full = g["effective_kv_bytes_per_step"] + 0.0
+            sample = c["sample_effective_bytes"]
+            note = "effective KV bytes"
+        est = c["oracle_wall_s"] * full / sample
+        c["oracle_s_per_step_est"] = round(est, 4)
+        c["oracle_scaled_by"] = note
+        c["gpu_us_per_step"] = round(g["ms_per_step"] * 1e3, 2)
+        c["oracle_over_gpu"] = round(est / (g["ms_per_step"] * 1e-3), 1)
+
+
+def decode_summary(res: dict) -> dict:
+    """The per-workload object of the JSON line."""
+    keep = ("ms_per_step", "value", "unit", "dtype", "pct_of_hbm_peak", "decode_tokens_per_s_per_layer",
+            "decode_gbps_attention_plus_reduce", "reduce_avg_ms", "effective_kv_bytes_per_step")
+    out = {k: res[k] for k in keep if k in res}
+    out["config"] = res["config"]
+    out["roofline"] = res["roofline"]
+    return out
 
 
 def main():
@@ -611,28 +807,50 @@ def main():
               "(the decode path shards by sequence or KV head with no exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.config != "all" and args.config not in SUB_CONFIGS + [HEADLINE, "llama3_8b_int8kv",
+                                                                   "llama3_8b_kfp8_vbf16"]:
+        print(f"unknown --config {args.config}", file=sys.stderr)
+        sys.exit(2)
+    # the CPU baseline forks oracle processes, so it runs before the GPU is initialised
+    cpu = None if (args.no_cpu_baseline or args.config not in ("all", HEADLINE)) else cpu_baseline(args)
+
     import paged_kv_cache_415_amd  # noqa: F401  (fails loudly if libpa.so is missing)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    if args.config == "mixed_prefix_bf16":
+    name = HEADLINE if args.config == "all" else args.config
+    if name == "mixed_prefix_bf16":
         res = run_mixed_bench(args, dev)
         res["block_ops"] = run_block_ops_bench(dev)
     else:
-        res = run_decode_bench(args, dev)
+        res = run_decode_bench(args, dev, name)
+    gpu_by_name = {name: res}
+    if args.config == "all":
+        subs = {}
+        for sub in SUB_CONFIGS:
+            torch.cuda.empty_cache()
+            r = run_mixed_bench(args, dev) if sub == "mixed_prefix_bf16" else \
+                run_decode_bench(args, dev, sub, extras=False)
+            gpu_by_name[sub] = r
+            subs[sub] = r if sub == "mixed_prefix_bf16" else decode_summary(r)
+            subs[sub].pop("metric", None)
+        res["configs"] = subs
+    torch.cuda.empty_cache()
     res["probe_read_gbps"] = round(probe_read_gbps(dev), 1)
     res["probe_copy_bytes"] = probe_copy_once(dev)
     # the decode kernel's rate against what a plain streaming read gets from HBM
     dec = res["roofline"] if res["roofline"]["unit"] == "GB/s" else res.get("decode_roofline")
     if dec is not None and res["probe_read_gbps"] > 0:
         res["decode_kernel_pct_of_probe"] = round(100 * dec["achieved"] / res["probe_read_gbps"], 1)
+    if cpu is not None:
+        compare_cpu_gpu(cpu, gpu_by_name)
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": res.pop("dtype"), "data": "synthetic",
             "config": res.pop("config"), "roofline": res.pop("roofline")}
-    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args)
+    line["cpu_baseline"] = cpu
     line.update(res)
     line["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(line), flush=True)
