@@ -451,8 +451,14 @@ pa_status pa_decode_attention_append(void* out, const void* q, const void* new_k
  *                   query_start_loc[s+1] - 1
  *   query_start_loc int32 [num_seqs + 1], non-decreasing, last = total
  *   max_q_len       >= every chunk length (sizes the grid)
- * Supported: q/cache bf16 or f16 (same type), num_q_heads / num_kv_heads a
- * power of two <= 16.
+ * Supported (q, cache) pairs: (bf16, bf16), (f16, f16), (f32, f32), and an
+ * fp8 E4M3 cache beside bf16 or f16 queries ([ybb] §6.2, KV cache in FP8):
+ * codes are decoded exactly to the query type and the per-tensor k_scale /
+ * v_scale apply as in pa_decode (logit = scale * k_scale * q . Kcode,
+ * out = v_scale * sum softmax * Vcode).  For 16-bit and fp8 caches
+ * num_q_heads / num_kv_heads is a power of two <= 16 (any group <= 16 for
+ * f32).  Accumulation is float32; 16-bit and fp8 paths feed probabilities
+ * to the matrix cores in the query's type.
  */
 pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
                            const void* k_pool, const void* v_pool, const int32_t* block_tables,

@@ -471,6 +471,8 @@ def pa_prefill_chunk(out, q, query_start_loc, k_pool, v_pool, block_tables, seq_
     """Causal attention of one chunk per sequence over its paged context (see pa.h)."""
     t, hq, d = q.shape
     _, hkv, bs, _ = k_pool.shape
+    if _dtype(v_pool) != _dtype(k_pool) or v_pool.shape[1:] != k_pool.shape[1:]:
+        raise ValueError("K and V pools must have one type and block shape")
     num_seqs = query_start_loc.shape[0] - 1
     _check(_lib.pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(query_start_loc), _ptr(k_pool),
                                  _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), float(scale),

@@ -686,10 +686,13 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
                                        max_blocks_per_seq, q_dtype, cache_dtype, cache_dtype);
   if (st != PA_OK) return st;
-  if (cache_dtype != q_dtype || q_dtype == PA_DTYPE_F32)
-    return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16/f16 queries with a cache of the same type");
+  if (cache_dtype != q_dtype && cache_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED,
+                "prefill supports a cache of the query's type (f32, f16, bf16) or an fp8 cache beside "
+                "bf16/f16 queries");
   const int group = num_q_heads / num_kv_heads;
-  if (group & (group - 1)) return fail(PA_ERR_UNSUPPORTED, "prefill needs a power-of-two group");
+  if (q_dtype != PA_DTYPE_F32 && (group & (group - 1)))
+    return fail(PA_ERR_UNSUPPORTED, "prefill over 16-bit or fp8 caches needs a power-of-two group");
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_INVALID_ARG, "scales must be finite");
   if ((long long)max_blocks_per_seq * block_size > (1 << 30))
@@ -724,6 +727,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
   p.block_size = block_size;
   p.max_blocks = max_blocks_per_seq;
   p.q_dtype = q_dtype;
+  p.cache_dtype = cache_dtype;
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 

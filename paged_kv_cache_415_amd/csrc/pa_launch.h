@@ -141,6 +141,7 @@ struct PrefillParams {
   int block_size;
   int max_blocks;
   int q_dtype;
+  int cache_dtype;     // K and V pools: q_dtype, or fp8 beside 16-bit queries
 };
 
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream);

@@ -21,6 +21,13 @@
 // tile's register layout is the value product's B operand, so
 // probabilities stay in their lanes; the value operand V^T is read from the
 // row-major V tile with gfx950's transposing LDS reads (ds_read_b64_tr_b16).
+//
+// An fp8 E4M3 cache (ybb.press page §6.2, KV cache in FP8) is staged through
+// registers instead: the next tile's codes are loaded while the current one
+// is computed, then decoded exactly to the query's 16-bit type and stored in
+// the same LDS layout, so the products are those of the 16-bit kernel; the
+// per-tensor scales fold into the logit scale and the output.  An fp32 cache
+// (small workloads) has a plain vector-unit kernel of its own.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -192,6 +199,74 @@ struct TileSrc {
   }
 };
 
+// fp8 K/V tiles staged through registers.  Thread t of the workgroup owns
+// key row t / 4 of every tile and bytes [D/4 (t % 4), D/4 (t % 4 + 1)) of it
+// (two 16-byte loads per pool at D = 128, one at D = 64); the 16 rows of a
+// wave lie in one cache block (two for 8-token blocks), whose ids come from
+// TileSrc::block_of.  store() decodes the codes to T (exact: every E4M3 value
+// is a bf16 and an f16 value) and writes them where the 16-bit copy would
+// have put them.
+template <typename T, int D, int BS>
+struct TileSrc8 {
+  static constexpr int NL = D / 64;             // 16-byte loads per pool and thread
+  static constexpr int TILE = kKeyTile * D * 2; // bytes of one 16-bit K or V tile in LDS
+  const char* kpool;
+  const char* vpool;
+  const int* trow;
+  int64_t head_off, blk_bytes;                  // in bytes of the 8-bit pools
+  int kend, row, sub;
+  u32x4 k[NL], v[NL];
+
+  __device__ void init(const char* kp, const char* vp, const int* tr, int num_kv_heads, int kvh, int kend_) {
+    kpool = kp;
+    vpool = vp;
+    trow = tr;
+    blk_bytes = (int64_t)num_kv_heads * BS * D;
+    head_off = (int64_t)kvh * BS * D;
+    kend = kend_;
+    row = threadIdx.x >> 2;
+    sub = threadIdx.x & 3;
+  }
+
+  template <class Blk>
+  __device__ __forceinline__ void load(int kt, Blk blk) {
+    const int wave_row = row & 15;                      // row among the wave's 16
+    int64_t off;
+    if (kt * kKeyTile + (row | 15) < kend) {
+      const int bi = (BS < 16 && wave_row >= 8) ? blk.b : blk.a;
+      const int brow = BS < 16 ? wave_row % BS : (kt * kKeyTile + row) % BS;
+      off = (int64_t)bi * blk_bytes + head_off + (int64_t)brow * D;
+    } else {
+      // the wave's rows reach past the context: re-read the last key
+      const int key = min(kt * kKeyTile + row, kend - 1);
+      off = (int64_t)trow[key / BS] * blk_bytes + head_off + (int64_t)(key % BS) * D;
+    }
+    off += sub * (D / 4);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      k[i] = ld16(kpool + off + 16 * i);
+      v[i] = ld16(vpool + off + 16 * i);
+    }
+  }
+
+  // Decode and store into a stage (K tile, then V tile).
+  __device__ __forceinline__ void store(char* stage) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {        // 8 codes -> one 16-byte chunk of 8 values
+        const int chunk = sub * (D / 32) + 2 * i + h;
+        const u32x4 kc = {fp8x2_to<T>(h ? k[i].z : k[i].x, false), fp8x2_to<T>(h ? k[i].z : k[i].x, true),
+                          fp8x2_to<T>(h ? k[i].w : k[i].y, false), fp8x2_to<T>(h ? k[i].w : k[i].y, true)};
+        const u32x4 vc = {fp8x2_to<T>(h ? v[i].z : v[i].x, false), fp8x2_to<T>(h ? v[i].z : v[i].x, true),
+                          fp8x2_to<T>(h ? v[i].w : v[i].y, false), fp8x2_to<T>(h ? v[i].w : v[i].y, true)};
+        *reinterpret_cast<u32x4*>(stage + row * D * 2 + 16 * (chunk ^ k_swz<D>(row))) = kc;
+        *reinterpret_cast<u32x4*>(stage + TILE + row * D * 2 + 16 * (chunk ^ v_swz<D>(row))) = vc;
+      }
+    }
+  }
+};
+
 template <typename T> constexpr uint32_t kOnes = 0;                  // two 1.0 values
 template <> constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
 template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;
@@ -262,7 +337,7 @@ __device__ __forceinline__ void pv_tile(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[
 // Two stages of (K tile, V tile).
 size_t prefill_smem_bytes(int head_dim) { return (size_t)2 * 2 * kKeyTile * head_dim * 2; }
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, bool KV8 = false>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p) {
   extern __shared__ __align__(16) char smem_raw[];
   constexpr int NC = D / 32;
@@ -364,9 +439,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
 
   TileSrc<D, BS> src;
   src.init(kpool, vpool, trow, p.num_kv_heads, kvh, kend, wave, lane);
-  src.copy(0, src.block_of(0), smem_raw);
+  TileSrc8<T, D, BS> src8;
+  if constexpr (KV8) {
+    src8.init(kpool, vpool, trow, p.num_kv_heads, kvh, kend);
+    src8.load(0, src.block_of(0));
+    src8.store(smem_raw);
+  } else {
+    src.copy(0, src.block_of(0), smem_raw);
+  }
   auto blk_next = src.block_of(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (!KV8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -374,7 +456,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     const uint32_t v_base = lds_base + (kt & 1) * 2 * TILE;   // LDS address of the stage
     const bool more = kt + 1 < ntiles;     // uniform over the workgroup
     if (more) {
-      src.copy(kt + 1, blk_next, smem_raw + ((kt + 1) & 1) * 2 * TILE);
+      if constexpr (KV8) src8.load(kt + 1, blk_next);   // into registers
+      else src.copy(kt + 1, blk_next, smem_raw + ((kt + 1) & 1) * 2 * TILE);
       blk_next = src.block_of(kt + 2);   // in flight while this tile is computed
     }
 
@@ -467,9 +550,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
     pv_tile<T, D>(acc, acc_l, pop, v_base, voff);
     __builtin_amdgcn_s_setprio(0);
     if (more) {
-      // this wave's copy of the next tile has landed; after the barrier all
-      // copies have, and every wave is done with this tile's stage
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // this wave's copy of the next tile has landed (8-bit: decoded and
+      // stored now); after the barrier all copies have, and every wave is
+      // done with this tile's stage
+      if constexpr (KV8) src8.store(smem_raw + ((kt + 1) & 1) * 2 * TILE);
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   }
@@ -490,13 +575,114 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 cache (small workloads, vector unit): one wave per (chunk position,
+// KV head, sequence) computes the group's query heads.  The head dimension
+// is spread over the lanes; keys 0 .. n - L + pos are taken one at a time
+// from groups of 16 whose rows are loaded together, with an online softmax
+// per head.
+// ---------------------------------------------------------------------------
+template <int D, int BS>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillParams p) {
+  constexpr int E = D / 64;
+  constexpr int kGroup = 16;
+  const int pos = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const int q0 = p.query_start_loc[seq];
+  const int L = p.query_start_loc[seq + 1] - q0;
+  if (pos >= L) return;
+  int n = p.seq_lens[seq];
+  const int cap = p.max_blocks * BS;
+  n = n < cap ? n : cap;
+  if (n < L) return;                       // malformed: the chunk must be in the context
+  const int t_end = n - L + pos + 1;       // keys [0, t_end) are visible
+  const int lane = threadIdx.x;
+  const int g = p.group;
+  const int* trow = p.block_tables + (int64_t)seq * p.max_blocks;
+  const float* q = reinterpret_cast<const float*>(p.q) + ((int64_t)(q0 + pos) * p.num_q_heads + kvh * g) * D;
+  const float* kpool = reinterpret_cast<const float*>(p.k_pool);
+  const float* vpool = reinterpret_cast<const float*>(p.v_pool);
+  float qv[16][E], acc[16][E], m[16], l[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      qv[j][e] = (j < g) ? q[j * D + lane + 64 * e] : 0.f;
+      acc[j][e] = 0.f;
+    }
+  }
+  for (int t0 = 0; t0 < t_end; t0 += kGroup) {
+    float kv[kGroup][E], vv[kGroup][E];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const int t = min(t0 + k, t_end - 1);   // past the end: the last key again (unused)
+      const int64_t rowoff = (((int64_t)trow[t / BS] * p.num_kv_heads + kvh) * BS + t % BS) * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kv[k][e] = kpool[rowoff + lane + 64 * e];
+        vv[k][e] = vpool[rowoff + lane + 64 * e];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j < g && t0 + k < t_end) {
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) dot += qv[j][e] * kv[k][e];
+#pragma unroll
+          for (int msk = 32; msk >= 1; msk >>= 1) dot += __shfl_xor(dot, msk, 64);
+          const float sc = mul_rn(dot, p.qk_scale_log2);
+          const float m_new = fmaxf(m[j], sc);
+          const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+          const float pr = __builtin_amdgcn_exp2f(sc - m_new);
+          l[j] = l[j] * alpha + pr;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[j][e] = acc[j][e] * alpha + pr * vv[k][e];
+          m[j] = m_new;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < g) {
+      float* orow = reinterpret_cast<float*>(p.out) + ((int64_t)(q0 + pos) * p.num_q_heads + kvh * g + j) * D;
+      const float inv = p.v_scale / l[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) orow[lane + 64 * e] = acc[j][e] * inv;
+    }
+  }
+}
+
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.num_seqs == 0 || p.max_q_len == 0) return hipSuccess;
+  if (p.q_dtype == kF32) {
+    const dim3 grid(p.max_q_len, p.num_kv_heads, p.num_seqs);
+#define PA_PREFILL32(D, BS) hipLaunchKernelGGL((prefill_f32_kernel<D, BS>), grid, dim3(64), 0, stream, p)
+#define PA_PREFILL32_BS(D)                       \
+  switch (p.block_size) {                        \
+    case 8: PA_PREFILL32(D, 8); break;           \
+    case 16: PA_PREFILL32(D, 16); break;         \
+    case 32: PA_PREFILL32(D, 32); break;         \
+    default: PA_PREFILL32(D, 64); break;         \
+  }
+    if (p.head_dim == 128) { PA_PREFILL32_BS(128) } else { PA_PREFILL32_BS(64) }
+#undef PA_PREFILL32_BS
+#undef PA_PREFILL32
+    return hipGetLastError();
+  }
   const int qpos = kRowsPerWG / p.group;
   const dim3 grid((p.max_q_len + qpos - 1) / qpos, p.num_kv_heads, p.num_seqs);
   const size_t smem = prefill_smem_bytes(p.head_dim);
-#define PA_PREFILL(T, D, BS) \
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS>), grid, dim3(kPThreads), smem, stream, p)
+  const bool kv8 = p.cache_dtype == kFP8;
+#define PA_PREFILL(T, D, BS)                                                                          \
+  do {                                                                                               \
+    if (kv8) hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS, true>), grid, dim3(kPThreads), smem, stream, p); \
+    else hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS, false>), grid, dim3(kPThreads), smem, stream, p); \
+  } while (0)
 #define PA_PREFILL_BS(T, D)                      \
   switch (p.block_size) {                        \
     case 8: PA_PREFILL(T, D, 8); break;          \

@@ -250,8 +250,13 @@ def test_partial_layer_and_swap_copies_check_arguments(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(hq=12, hkv=4), UNSUPPORTED),            # group 3: not a power of two
-    (dict(qdt=BF16, cdt=FP8), UNSUPPORTED),
-    (dict(qdt=F32, cdt=F32), UNSUPPORTED),
+    (dict(hq=12, hkv=4, qdt=F32, cdt=F32), INVALID),   # the fp32 kernel takes any group: nulls
+    (dict(qdt=BF16, cdt=FP8), INVALID),           # supported pairs: fail only on the nulls
+    (dict(qdt=F16, cdt=FP8), INVALID),
+    (dict(qdt=F32, cdt=F32), INVALID),
+    (dict(qdt=F32, cdt=FP8), UNSUPPORTED),
+    (dict(qdt=BF16, cdt=F16), UNSUPPORTED),
+    (dict(qdt=FP8, cdt=FP8), UNSUPPORTED),
     (dict(), INVALID),                            # null pointers
     (dict(S=-2), INVALID),
 ])

@@ -12,8 +12,10 @@ from gpu_cases import TOL, as_f64, lib, max_abs, up, up_int
 pytestmark = pytest.mark.gpu
 
 
-def _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype):
-    """Pool holding each sequence's whole context (chunk included) + packed queries."""
+def _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype, q_dtype=None):
+    """Pool holding each sequence's whole context (chunk included) + packed queries.
+    An fp8 pool holds the values / a per-tensor scale (amax / 448); the scales
+    are returned as the last two items."""
     need = [-(-n // bs) for n in ctxs]
     nb = sum(need) + 2
     ids = rng.permutation(nb)
@@ -23,17 +25,30 @@ def _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype):
     vp = np.full((nb, hkv, bs, d), nan, W.BITS_DTYPE[dtype])
     tables = np.full((len(ctxs), max(need)), poison, np.int32)
     cur = 0
+    vals = {0: [], 1: []}
     for s, n in enumerate(ctxs):
         for b in range(need[s]):
             tables[s, b] = ids[cur]
             cur += 1
-        for pool in (kp, vp):
-            vals = W.to_bits(rng.standard_normal((need[s], hkv, bs, d)).astype(np.float32), dtype)
-            flat = vals.transpose(1, 0, 2, 3).reshape(hkv, -1, d)
+        for i in (0, 1):
+            vals[i].append(rng.standard_normal((need[s], hkv, bs, d)).astype(np.float32))
+    scales = [1.0, 1.0]
+    if dtype == "fp8_e4m3":
+        for i in (0, 1):
+            amax = max(float(np.abs(v.transpose(1, 0, 2, 3).reshape(hkv, -1, d)[:, :n]).max())
+                       for v, n in zip(vals[i], ctxs))
+            scales[i] = float(np.float32(amax / W.FP8_MAX))
+    for s, n in enumerate(ctxs):
+        for i, pool in ((0, kp), (1, vp)):
+            x = vals[i][s] / np.float32(scales[i]) if dtype == "fp8_e4m3" else vals[i][s]
+            bits = W.to_bits(x, dtype)
+            flat = bits.transpose(1, 0, 2, 3).reshape(hkv, -1, d)
             flat[:, n:, :] = nan
             pool[tables[s, :need[s]]] = flat.reshape(hkv, need[s], bs, d).transpose(1, 0, 2, 3)
     qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
-    q = W.to_bits(rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32), dtype)
+    q = W.to_bits(rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32), q_dtype or dtype)
+    if dtype == "fp8_e4m3":
+        return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32), scales[0], scales[1]
     return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32)
 
 
@@ -192,3 +207,124 @@ def test_prefill_any_scale(scale):
                            up_int(lens), scale, max(chunks))
     torch.cuda.synchronize()
     assert max_abs(out, ref) <= TOL["bf16"]
+
+
+FP8_CASES = [
+    # (chunks, contexts, Hq, Hkv, D, bs, q dtype)
+    ([5, 16, 1], [5, 40, 70], 4, 1, 128, 16, "bf16"),
+    ([33, 100], [33, 300], 8, 2, 128, 32, "bf16"),
+    ([64, 7], [200, 7], 32, 8, 128, 32, "f16"),
+    ([17, 50], [60, 99], 2, 2, 64, 16, "f16"),
+    ([40], [555], 8, 1, 64, 32, "bf16"),
+    ([20, 9], [85, 9], 8, 2, 128, 8, "bf16"),
+    ([70], [300], 4, 4, 64, 64, "f16"),
+    ([33], [77], 16, 1, 128, 64, "bf16"),
+    ([100], [130], 4, 1, 64, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("chunks,ctxs,hq,hkv,d,bs,q_dt", FP8_CASES)
+def test_prefill_fp8_cache_matches_oracle(chunks, ctxs, hq, hkv, d, bs, q_dt):
+    """Prefill over an fp8 E4M3 cache with per-tensor scales: codes decoded
+    exactly to the query type, the scales folded into the logit scale and
+    the output."""
+    rng = np.random.default_rng(sum(chunks) + 3 * hq + d + bs)
+    q, qsl, kp, vp, tables, lens, ks, vs = _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs,
+                                                          "fp8_e4m3", q_dtype=q_dt)
+    scale = 1.0 / np.sqrt(d)
+    ref = oracle.prefill_chunk_attention(q, q_dt, qsl, kp, vp, "fp8_e4m3", tables, lens, scale, bs,
+                                         hkv, k_scale=ks, v_scale=vs)
+    gq = up(q, q_dt)
+    out = torch.empty_like(gq)
+    lib().pa_prefill_chunk(out, gq, up_int(qsl), up(kp, "fp8_e4m3"), up(vp, "fp8_e4m3"),
+                           up_int(tables), up_int(lens), scale, max(chunks), k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= TOL[q_dt]
+
+
+def test_prefill_fp8_70b_shaped_serving_step():
+    """A 70B-shaped layer (64 query / 8 KV heads, head_dim 128, block 16, fp8
+    cache with per-tensor scales, bf16 activations): four sequences each
+    prefill a 512-token chunk after a 1,024-token prefix.  The chunk's bf16
+    K/V is quantised into the pool by pa_reshape_and_cache, then
+    pa_prefill_chunk reads the whole 1,536-token context through the table;
+    the pools must equal the oracle's byte for byte and every output must
+    match."""
+    rng = np.random.default_rng(70)
+    hq, hkv, d, bs, prefix, chunk, nseq = 64, 8, 128, 16, 1024, 512, 4
+    ctx = prefix + chunk
+    q, qsl, kp, vp, tables, lens, ks, vs = _random_chunks(rng, [chunk] * nseq, [ctx] * nseq, hq, hkv,
+                                                          d, bs, "fp8_e4m3", q_dtype="bf16")
+    # the chunk's rows are not in the pool yet: they arrive through the scatter
+    nan = W.NAN_BITS["fp8_e4m3"]
+    slots = np.zeros(nseq * chunk, np.int64)
+    for s in range(nseq):
+        for i in range(chunk):
+            pos = prefix + i
+            blk = int(tables[s, pos // bs])
+            kp[blk, :, pos % bs, :] = nan
+            vp[blk, :, pos % bs, :] = nan
+            slots[s * chunk + i] = blk * bs + pos % bs
+    new_k = W.to_bits(rng.standard_normal((nseq * chunk, hkv, d)).astype(np.float32), "bf16")
+    new_v = W.to_bits(rng.standard_normal((nseq * chunk, hkv, d)).astype(np.float32), "bf16")
+    okp, ovp = oracle.reshape_and_cache(kp, vp, "fp8_e4m3", new_k, new_v, "bf16", slots, bs, ks, vs)
+    scale = 1.0 / np.sqrt(d)
+    pa = lib()
+    gk, gv = up(kp, "fp8_e4m3"), up(vp, "fp8_e4m3")
+    pa.pa_reshape_and_cache(up(new_k, "bf16"), up(new_v, "bf16"), gk, gv, up_int(slots), ks, vs)
+    gq = up(q, "bf16")
+    out = torch.empty_like(gq)
+    pa.pa_prefill_chunk(out, gq, up_int(qsl), gk, gv, up_int(tables), up_int(lens), scale, chunk,
+                        k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.torch_to_bits(gk, "fp8_e4m3"), okp)
+    assert np.array_equal(W.torch_to_bits(gv, "fp8_e4m3"), ovp)
+    ref = oracle.prefill_chunk_attention(q, "bf16", qsl, okp, ovp, "fp8_e4m3", tables, lens, scale, bs,
+                                         hkv, k_scale=ks, v_scale=vs)
+    err = max_abs(out, ref)
+    print(f"[prefill fp8] 70B-shaped step max-abs {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
+def test_prefill_fp8_last_row_matches_fp8_decode():
+    """The last row of a chunk over an fp8 cache equals the fp8 decode of the
+    same context (two kernels, one result up to rounding)."""
+    rng = np.random.default_rng(9)
+    chunks, ctxs = [9, 30], [100, 64]
+    q, qsl, kp, vp, tables, lens, ks, vs = _random_chunks(rng, chunks, ctxs, 8, 2, 128, 16, "fp8_e4m3",
+                                                          q_dtype="bf16")
+    pa = lib()
+    gq = up(q, "bf16")
+    gk, gv, gt, gl = up(kp, "fp8_e4m3"), up(vp, "fp8_e4m3"), up_int(tables), up_int(lens)
+    out = torch.empty_like(gq)
+    pa.pa_prefill_chunk(out, gq, up_int(qsl), gk, gv, gt, gl, 0.1, 30, k_scale=ks, v_scale=vs)
+    last = gq[torch.tensor([8, 38], device=gq.device)].contiguous()
+    dec = torch.empty_like(last)
+    pa.pa_decode(dec, last, gk, gv, gt, gl, 0.1, max_seq_len=100, k_scale=ks, v_scale=vs,
+                 partition_size=-1)
+    torch.cuda.synchronize()
+    assert np.abs(as_f64(out[[8, 38]]) - as_f64(dec)).max() <= TOL["bf16"]
+
+
+F32_CASES = [
+    # (chunks, contexts, Hq, Hkv, D, bs)
+    ([1, 17, 33, 64], [1, 17, 33, 64], 2, 2, 64, 16),     # the tiny workload's lengths, whole prompts
+    ([5, 16, 1], [5, 40, 70], 4, 1, 128, 16),
+    ([33, 100], [33, 300], 12, 4, 64, 32),                 # group 3
+    ([9], [77], 16, 1, 128, 8),
+    ([70], [300], 4, 4, 64, 64),
+]
+
+
+@pytest.mark.parametrize("chunks,ctxs,hq,hkv,d,bs", F32_CASES)
+def test_prefill_f32_matches_oracle(chunks, ctxs, hq, hkv, d, bs):
+    rng = np.random.default_rng(sum(ctxs) + hq + bs)
+    q, qsl, kp, vp, tables, lens = _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, "f32")
+    scale = 1.0 / np.sqrt(d)
+    ref = oracle.prefill_chunk_attention(q, "f32", qsl, kp, vp, "f32", tables, lens, scale, bs, hkv)
+    gq = up(q, "f32")
+    out = torch.empty_like(gq)
+    lib().pa_prefill_chunk(out, gq, up_int(qsl), up(kp, "f32"), up(vp, "f32"), up_int(tables),
+                           up_int(lens), scale, max(chunks))
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= TOL["f32"]
