@@ -5,7 +5,9 @@
 One step is one pass of the decode hot path over one batch: scatter of each
 sequence's newest K/V into its pool slot (pa_reshape_and_cache), then paged
 decode attention (pa_decode_attention) and the log-sum-exp merge of split
-partials (pa_decode_reduce), all on torch's current stream.  For the mixed
+partials (pa_decode_reduce), all on torch's current stream; for 16-bit caches
+the headline also reports the step with the scatter folded into the decode
+kernel (pa_decode_attention_append + pa_decode_reduce).  For the mixed
 workload a step is copy-on-write (pa_copy_blocks), the scatter of every new
 token, the causal prefill chunks (pa_prefill_chunk) and the decodes.
 
@@ -197,10 +199,11 @@ def run_decode_bench(args, dev, name: str, extras: bool = True):
         if ev is not None:
             ev[2].record()
 
-    # 16-bit caches: the scatter folded into the decode kernel (two launches)
+    # 16-bit caches: the scatter folded into the decode kernel
     can_append = spec.cache_dtype == spec.q_dtype == spec.v_dtype and spec.q_dtype in ("f16", "bf16")
 
     def step_append(b, ev=None):
+        """Decode kernel with the scatter folded in, then the reduce: two launches."""
         if ev is not None:
             ev[0].record()
         pa.pa_decode_attention_append(b.out, b.q, b.new_k, b.new_v, b.k_pool, b.v_pool, b.tables,
@@ -227,19 +230,23 @@ def run_decode_bench(args, dev, name: str, extras: bool = True):
     red_ms = [e[1].elapsed_time(e[2]) for e in evs]
 
     # After the timed region: the same steps with the scatter folded into the
-    # decode kernel (two launches), for comparison
-    appended = None
-    if can_append and extras:
+    # decode kernel (append kernel + reduce), for comparison
+    def time_steps(fn):
         for i in range(args.warmup):
-            step_append(batches[i % len(batches)])
+            fn(batches[i % len(batches)])
         torch.cuda.synchronize()
-        aevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        t0 = time.perf_counter()
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        t1 = time.perf_counter()
         for i in range(args.steps):
-            step_append(batches[i % len(batches)], aevs[i])
+            fn(batches[i % len(batches)], cevs[i])
         torch.cuda.synchronize()
-        appended = ((time.perf_counter() - t0) * 1e3 / args.steps,
-                    float(np.mean([e[0].elapsed_time(e[1]) for e in aevs])))
+        return ((time.perf_counter() - t1) * 1e3 / args.steps,
+                float(np.mean([e[0].elapsed_time(e[1]) for e in cevs])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in cevs])))
+
+    appended = None
+    if extras and can_append:
+        appended = time_steps(step_append)
 
     # After the timed region: the same steps replayed from captured HIP graphs
     # (one graph per batch), as a serving loop replays captured decode steps.
@@ -308,8 +315,8 @@ def run_decode_bench(args, dev, name: str, extras: bool = True):
     }
     res["step"] = "scatter kernel + decode attention + reduce"
     if appended is not None:
-        res["append_ms_per_step"] = round(appended[0], 5)
-        res["append_gbps"] = round(eff / (appended[0] * 1e-3) / 1e9, 1)
+        res["append_plus_reduce_ms_per_step"] = round(appended[0], 5)
+        res["append_plus_reduce_gbps"] = round(eff / (appended[0] * 1e-3) / 1e9, 1)
         res["append_attention_avg_ms"] = round(appended[1], 5)
     return res
 

@@ -203,10 +203,10 @@ struct TableWindow {
 // ---------------------------------------------------------------------------
 enum : int { kFmtQ = 0, kFmtFp8 = 1, kFmtI8 = 2 };
 
-// APPEND: the newest token of every sequence (position seq_len - 1) is read
-// from p.new_k / p.new_v instead of the pool, and the wave that covers it
-// writes it into its pool slot (the scatter folded into the decode; 16-bit
-// caches only).
+// APPEND: the newest token of every sequence (position seq_len - 1) comes
+// from p.new_k / p.new_v: the wave whose segment covers it first stores its
+// K and V rows into the pool slot, then reads the whole context from the
+// pool (the scatter folded into the decode; 16-bit caches only).
 template <typename QT, int KF, int VF, int D, int BS, bool APPEND = false>
 struct MfmaDecode {
   static constexpr bool KF8 = KF != kFmtQ, VF8 = VF != kFmtQ;   // one byte per element
@@ -227,9 +227,8 @@ struct MfmaDecode {
   // half-line pieces the layout asks for (measured faster with 8-bit V,
   // slower beside a 16-bit V)
   static constexpr bool kStageK = KF8 && VF8 && D == 128 && BS >= 16 && !APPEND;
-  // partials merged in LDS (not with the scatter folded in, whose registers
-  // are at the limit of three waves per SIMD)
-  static constexpr bool kLocalMerge = !APPEND;
+  // partials of pairs inside one workgroup's share are merged in LDS
+  static constexpr bool kLocalMerge = true;
   // waves per workgroup = waves one CU keeps resident at this register count
   static constexpr int kWaves = D == 64 ? 16 : (KF8 && VF8 ? 8 : 12);
 
@@ -256,12 +255,9 @@ struct MfmaDecode {
   }
 
   // Issue the loads of step j (tokens 32j .. 32j+31 of the pair).
-  template <bool APP = false>
-  static __device__ __forceinline__ void load(Buf& buf, Ids id, const DecodeParams& p, int kvh,
-                                              int j, int s = 0, int len = 0) {
+  static __device__ __forceinline__ void load(Buf& buf, Ids id, const DecodeParams& p, int kvh, int j) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, c16 = lane & 15;
-    static_assert(!APP || (KF == kFmtQ && VF == kFmtQ && !kDoubleBuffer), "append: 16-bit cache");
     const char* kpool = reinterpret_cast<const char*>(p.k_pool);
     const char* vpool = reinterpret_cast<const char*>(p.v_pool);
 #pragma unroll
@@ -292,18 +288,6 @@ struct MfmaDecode {
         buf.vs[tau] = G < 2 ? v0 : v1;
       }
       const char* kt = kpool + krow * KEB;
-      // APPEND: the tile holding the newest token takes that row from the input
-      const int t0 = j * kStep + 16 * tau;
-      const bool new_tile = APP && len - 1 >= t0 && len - 1 < t0 + 16;   // uniform
-      const char* nk = nullptr;
-      const char* nv = nullptr;
-      if constexpr (APP) {
-        if (new_tile) {
-          nk = reinterpret_cast<const char*>(p.new_k) + ((int64_t)s * p.new_k_stride + (int64_t)kvh * D) * 2;
-          nv = reinterpret_cast<const char*>(p.new_v) + ((int64_t)s * p.new_v_stride + (int64_t)kvh * D) * 2;
-          if (t0 + c16 == len - 1) kt = nk;
-        }
-      }
       if constexpr (kStageK) {
         // instruction h: rows 8 h + 2 G + c16 / 8 of the tile, 16 bytes each
         const char* kr = kt - (int64_t)c16 * D;   // row 0 of the tile
@@ -320,9 +304,6 @@ struct MfmaDecode {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const char* src = vt + (int64_t)i * D * VEB;
-        if constexpr (APP) {
-          if (new_tile && t0 + 4 * G + i == len - 1) src = nv + (int64_t)DPL * c16 * 2;
-        }
         if constexpr (VW == 4) {
           const u32x4 x = ld16_nt(src);
           buf.v[tau][i][0] = x.x; buf.v[tau][i][1] = x.y; buf.v[tau][i][2] = x.z; buf.v[tau][i][3] = x.w;
@@ -577,6 +558,31 @@ struct MfmaDecode {
 
     const ctab_ptr trow = (ctab_ptr)(p.block_tables + (int64_t)s * p.max_blocks);
     const int nblk = (len + BS - 1) / BS;
+    // APPEND: the segment that covers the newest token loads its K and V rows
+    // (lanes 0-31: K, 32-63: V; D / 16 bytes each) here and stores them in
+    // the pool slot once its first step's loads are on their way (before
+    // them if that step is the last one); the last step reads them back from
+    // the pool
+    const bool appends = APPEND && len > 0 && j1 == (len + kStep - 1) / kStep;
+    u32x2 new_row = {0u, 0u};
+    char* new_dst = nullptr;
+    if constexpr (APPEND) {
+      if (appends) {
+        const bool is_v = lane >= 32;
+        const char* src = reinterpret_cast<const char*>(is_v ? p.new_v : p.new_k) +
+                          ((int64_t)s * (is_v ? p.new_v_stride : p.new_k_stride) + (int64_t)kvh * D) * 2;
+        const int b = (lane & 31) * (D / 16);
+        if constexpr (D == 128) new_row = *reinterpret_cast<const u32x2*>(src + b);
+        else new_row.x = *reinterpret_cast<const uint32_t*>(src + b);
+        const int pos = len - 1;
+        const int64_t off = (((int64_t)trow[pos / BS] * p.num_kv_heads + kvh) * BS + pos % BS) * D * 2;
+        new_dst = reinterpret_cast<char*>(const_cast<void*>(is_v ? p.v_pool : p.k_pool)) + off + b;
+      }
+    }
+    auto store_new_row = [&]() {
+      if constexpr (D == 128) *reinterpret_cast<u32x2*>(new_dst) = new_row;
+      else *reinterpret_cast<uint32_t*>(new_dst) = new_row.x;
+    };
     extern __shared__ __align__(16) int plan_lds[];
     char* kst = kStageK ? reinterpret_cast<char*>(plan_lds) + p.kstage_off + (threadIdx.x >> 6) * 4096 : nullptr;
 
@@ -607,40 +613,39 @@ struct MfmaDecode {
         compute(B, st, qop, p.qk_scale_log2, len, j + 1, kst);
       }
     } else {
-      // APPEND: the step that holds the newest token (the last step of the
-      // pair) is peeled off, so the loop is that of the plain kernel
-      const bool last_step = APPEND && j1 == (len + kStep - 1) / kStep;
-      const int jend = last_step ? j1 - 1 : j1;
-      for (int j = j0; j < jend; ++j) {
+      int jfirst = j0;
+      if constexpr (APPEND) {
+        // the first step of an appending segment, peeled so that the new
+        // rows' registers are free in the loop
+        if (appends) {
+          const Ids nxt = ids(trow, nblk, min(j0 + 1, j1 - 1));
+          if (j0 == j1 - 1) {
+            store_new_row();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          }
+          Buf buf;
+          load(buf, cur, p, kvh, j0);
+          if (j0 < j1 - 1) store_new_row();
+          compute(buf, st, qop, p.qk_scale_log2, len, j0, kst);
+          cur = nxt;
+          jfirst = j0 + 1;
+        }
+      }
+      for (int j = jfirst; j < j1; ++j) {
         const Ids nxt = ids(trow, nblk, min(j + 1, j1 - 1));
+        if constexpr (APPEND) {
+          if (appends && j == j1 - 1) {
+            // other lanes of this wave read the rows stored in the first
+            // step in this step's loads
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          }
+        }
         Buf buf;
         load(buf, cur, p, kvh, j);
         compute(buf, st, qop, p.qk_scale_log2, len, j, kst);
         cur = nxt;
-      }
-      if constexpr (APPEND) {
-        if (last_step) {
-          Buf buf;
-          load<true>(buf, cur, p, kvh, jend, s, len);
-          compute(buf, st, qop, p.qk_scale_log2, len, jend);
-        }
-      }
-    }
-
-    if constexpr (APPEND) {
-      // the segment that covered the newest token stores its K and V rows in
-      // the pool slot (lanes 0-31: K, 32-63: V; D / 16 bytes each)
-      if (len > 0 && j1 == (len + kStep - 1) / kStep) {
-        const int pos = len - 1;
-        const int blk = trow[pos / BS];
-        const int64_t off = (((int64_t)blk * p.num_kv_heads + kvh) * BS + pos % BS) * D * 2;
-        const bool is_v = lane >= 32;
-        const char* src = reinterpret_cast<const char*>(is_v ? p.new_v : p.new_k) +
-                          ((int64_t)s * (is_v ? p.new_v_stride : p.new_k_stride) + (int64_t)kvh * D) * 2;
-        char* dst = reinterpret_cast<char*>(const_cast<void*>(is_v ? p.v_pool : p.k_pool)) + off;
-        const int b = (lane & 31) * (D / 16);
-        if constexpr (D == 128) *reinterpret_cast<u32x2*>(dst + b) = *reinterpret_cast<const u32x2*>(src + b);
-        else *reinterpret_cast<uint32_t*>(dst + b) = *reinterpret_cast<const uint32_t*>(src + b);
       }
     }
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n

@@ -449,6 +449,28 @@ def test_append_equals_scatter_then_decode(q_dt, hq, hkv, d, bs, lens, partition
     assert torch.equal(out2.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["llama2_7b_mha_f16", "llama3_8b_gqa_bf16"])
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_append_full_config_matches_oracle(name, partition, full_cases):
+    """pa_decode_append (the scatter folded into the decode kernel) on the full
+    workload against the oracle's scatter + decode: every output, both pools
+    byte for byte."""
+    case, (ref, okp, ovp) = full_cases(name)
+    print(f"[append parity] {name} partition {partition}", flush=True)
+    pa = lib()
+    run = DecodeRun(case)
+    out = torch.empty_like(run.q)
+    ws = pa.decode_workspace(run.q, run.k_pool, run.max_len, partition)
+    pa.pa_decode_append(out, run.q, run.new_k, run.new_v, run.k_pool, run.v_pool, run.tables,
+                        run.lens, case.spec.scale, max_seq_len=run.max_len,
+                        partition_size=partition, workspace=ws)
+    torch.cuda.synchronize()
+    dt = case.spec.cache_dtype
+    assert np.array_equal(W.torch_to_bits(run.k_pool, dt), okp)
+    assert np.array_equal(W.torch_to_bits(run.v_pool, dt), ovp)
+    assert max_abs(out, ref) <= TOL[case.spec.q_dtype]
+
+
 def _rewrite_k_dim0(case, values_per_seq, k_scale=None):
     """Set dimension 0 of every K row of head 0 to the given per-token values
     (the newest token's through the scatter input); other dims keep their
