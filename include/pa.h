@@ -44,7 +44,8 @@
  *   last failure on the calling thread.  Device-resident contents (block
  *   ids, slots, lengths, chunk offsets) are trusted: the kernels clamp
  *   lengths to the table width, but a block id outside the pool is
- *   undefined behaviour.
+ *   undefined behaviour.  pa_check_block_tables / pa_check_slots (end of
+ *   this file) check them on the device and report through an error word.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -467,6 +468,47 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_blocks_per_seq, pa_dtype q_dtype, pa_dtype cache_dtype,
                            float k_scale, float v_scale, void* stream);
+
+/*
+ * Index checks.  The calls above trust device-resident indices (a block id
+ * outside the pool is undefined behaviour there, as checking would need a
+ * synchronisation).  A caller that wants them checked enqueues these calls
+ * on the same stream first: each writes a device error record of three
+ * int32 (caller-owned device memory, reset by the call itself before it
+ * checks): error[0] = OR of the pa_check_flag values found, error[1] =
+ * number of offending sequences (tables) or tokens (slots), error[2] = the
+ * smallest offending sequence / token index (INT32_MAX when none).  Nothing
+ * the indices name is read, so the checks are safe on any input.
+ *
+ * pa_check_block_tables ([datawhale] TODO 5 and [bogosort] §8: a sequence's
+ * blocks are the first ceil(seq_len / block_size) entries of its table row):
+ * for each sequence s, seq_lens[s] must lie in [0, max_blocks_per_seq *
+ * block_size] and, when max_seq_len > 0, not exceed max_seq_len (else
+ * PA_CHECK_LENGTH); each of those entries must lie in [0, num_blocks) (else
+ * PA_CHECK_BLOCK_ID).  With query_start_loc (may be NULL; [num_seqs + 1],
+ * as pa_prefill_chunk takes it): offsets must be non-decreasing from >= 0,
+ * each chunk no longer than its context, and the last offset equal to
+ * total_q_tokens (else PA_CHECK_CHUNK).
+ *
+ * pa_check_slots ([datawhale] Step 4, slot = block * block_size + row):
+ * every non-negative slot must be < num_blocks * block_size (else
+ * PA_CHECK_SLOT); negative slots are the documented skip.  Uniqueness is not
+ * checked.
+ */
+typedef enum {
+  PA_CHECK_BLOCK_ID = 1,
+  PA_CHECK_LENGTH = 2,
+  PA_CHECK_SLOT = 4,
+  PA_CHECK_CHUNK = 8
+} pa_check_flag;
+
+pa_status pa_check_block_tables(const int32_t* block_tables, const int32_t* seq_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs,
+                                int32_t total_q_tokens, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                                int32_t* error, void* stream);
+pa_status pa_check_slots(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size, int32_t* error, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status status);

@@ -88,6 +88,10 @@ def _load() -> ctypes.CDLL:
         getattr(lib, name).restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, f32, vp]
+    lib.pa_check_block_tables.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.pa_check_block_tables.restype = i32
+    lib.pa_check_slots.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.pa_check_slots.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -481,6 +485,37 @@ def pa_prefill_chunk(out, q, query_start_loc, k_pool, v_pool, block_tables, seq_
                                  float(k_scale), float(v_scale), _stream(stream)))
 
 
+CHECK_FLAGS = {"block_id": 1, "length": 2, "slot": 4, "chunk": 8}
+
+
+def pa_check_block_tables(block_tables, seq_lens, num_blocks: int, block_size: int, error,
+                          max_seq_len: int = 0, query_start_loc=None, stream=None) -> None:
+    """Check block ids, lengths (and chunk offsets) on the device; the result
+    lands in ``error`` (int32 [3] on the GPU: flags, count, first index)."""
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 or error.dtype != torch.int32:
+        raise TypeError("block_tables, seq_lens and error must be int32")
+    if error.numel() < 3:
+        raise ValueError("error needs three int32")
+    s = seq_lens.shape[0]
+    total = 0
+    if query_start_loc is not None:
+        if query_start_loc.dtype != torch.int32 or query_start_loc.shape[0] != s + 1:
+            raise ValueError("query_start_loc must be int32 [num_seqs + 1]")
+        total = int(query_start_loc[-1].item()) if s > 0 else 0
+    _check(_lib.pa_check_block_tables(_ptr(block_tables), _ptr(seq_lens), _ptr(query_start_loc), s,
+                                      total, block_tables.shape[1], int(block_size), int(num_blocks),
+                                      int(max_seq_len), _ptr(error), _stream(stream)))
+
+
+def pa_check_slots(slot_mapping, num_blocks: int, block_size: int, error, stream=None) -> None:
+    """Check that every non-negative slot lies inside the pool; the result
+    lands in ``error`` (int32 [3] on the GPU)."""
+    if slot_mapping.dtype != torch.int64 or error.dtype != torch.int32:
+        raise TypeError("slot_mapping must be int64 and error int32")
+    _check(_lib.pa_check_slots(_ptr(slot_mapping), slot_mapping.shape[0], int(num_blocks),
+                               int(block_size), _ptr(error), _stream(stream)))
+
+
 def pa_probe_read(src, sink, stream=None) -> None:
     _check(_lib.pa_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                               _stream(stream)))
@@ -500,6 +535,7 @@ __all__ = [
     "pa_decode_attention",
     "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",
     "pa_decode_workspace_bytes", "decode_workspace", "pa_probe_read", "pa_probe_copy",
+    "pa_check_block_tables", "pa_check_slots", "CHECK_FLAGS",
     "PagedAttentionError", "library", "LIB_PATH",
 ]
 

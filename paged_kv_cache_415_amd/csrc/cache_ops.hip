@@ -11,6 +11,8 @@
 // thread, coalesced along head_dim; the quantising scatters (fp8 E4M3 with
 // per-tensor scales, int8 with per-(block, KV head) scales) turn 16 source
 // elements into one 16-byte store of codes.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -293,6 +295,73 @@ hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream
   const int64_t nvec = (int64_t)(bytes / 16);
   hipLaunchKernelGGL(probe_copy_kernel, dim3(kProbeBlocks), dim3(256), 0, stream, (u32x4*)dst,
                      (const u32x4*)src, nvec);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Index checks: device-resident block ids, lengths, chunk offsets and slots
+// compared against the sizes the caller states; nothing they name is read.
+// err[0] = OR of the flags found, err[1] = number of bad sequences (tables)
+// or tokens (slots), err[2] = the smallest bad sequence / token index.
+// ---------------------------------------------------------------------------
+__global__ void check_reset_kernel(int* err) {
+  err[0] = 0;
+  err[1] = 0;
+  err[2] = 0x7FFFFFFF;
+}
+
+__global__ __launch_bounds__(256) void check_tables_kernel(CheckParams p) {
+  __shared__ int flags_s;
+  for (int s = blockIdx.x; s < p.num_items; s += gridDim.x) {
+    if (threadIdx.x == 0) flags_s = 0;
+    __syncthreads();
+    const int n = p.seq_lens[s];
+    const long long cap = (long long)p.max_blocks * p.block_size;
+    int flags = 0;
+    if (n < 0 || n > cap || (p.max_len > 0 && n > p.max_len)) flags |= kCheckLength;
+    if (p.query_start_loc != nullptr && threadIdx.x == 0) {
+      const int a = p.query_start_loc[s], b = p.query_start_loc[s + 1];
+      if (a < 0 || b < a || b - a > n || (s + 1 == p.num_items && b != p.total)) flags |= kCheckChunk;
+    }
+    const int valid = n < 0 ? 0 : (int)(n > cap ? cap : n);
+    const int nb = (valid + p.block_size - 1) / p.block_size;
+    const int* row = p.block_tables + (int64_t)s * p.max_blocks;
+    for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+      const int id = row[b];
+      if (id < 0 || id >= p.num_blocks) flags |= kCheckBlockId;
+    }
+    if (flags) atomicOr(&flags_s, flags);
+    __syncthreads();
+    if (threadIdx.x == 0 && flags_s) {
+      atomicOr(p.err, flags_s);
+      atomicAdd(p.err + 1, 1);
+      atomicMin(p.err + 2, s);
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void check_slots_kernel(CheckParams p) {
+  const int64_t limit = (int64_t)p.num_blocks * p.block_size;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < p.num_items; t += gridDim.x * blockDim.x) {
+    if (p.slots[t] >= limit) {
+      atomicOr(p.err, kCheckSlot);
+      atomicAdd(p.err + 1, 1);
+      atomicMin(p.err + 2, t);
+    }
+  }
+}
+
+hipError_t launch_check(const CheckParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(check_reset_kernel, dim3(1), dim3(1), 0, stream, p.err);
+  if (p.num_items > 0) {
+    if (p.slots != nullptr) {
+      const int grid = (int)std::min<int64_t>(1024, ((int64_t)p.num_items + 255) / 256);
+      hipLaunchKernelGGL(check_slots_kernel, dim3(grid), dim3(256), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(check_tables_kernel, dim3(std::min(p.num_items, 4096)), dim3(256), 0, stream, p);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -731,6 +731,48 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
+pa_status pa_check_block_tables(const int32_t* block_tables, const int32_t* seq_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs,
+                                int32_t total_q_tokens, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                                int32_t* error, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks < 0 ||
+      max_seq_len < 0 || total_q_tokens < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or non-positive table width / block size");
+  if (!error || !aligned(error, 4)) return fail(PA_ERR_INVALID_ARG, "null or misaligned error word");
+  if (num_seqs > 0 && (!block_tables || !seq_lens || !aligned(block_tables, 4) || !aligned(seq_lens, 4) ||
+                       (query_start_loc && !aligned(query_start_loc, 4))))
+    return fail(PA_ERR_INVALID_ARG, "null or misaligned pointer");
+  pa::CheckParams p{};
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.query_start_loc = query_start_loc;
+  p.err = error;
+  p.num_items = num_seqs;
+  p.max_blocks = max_blocks_per_seq;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_len = max_seq_len;
+  p.total = total_q_tokens;
+  return hip_status(pa::launch_check(p, static_cast<hipStream_t>(stream)), "check launch");
+}
+
+pa_status pa_check_slots(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size, int32_t* error, void* stream) {
+  if (num_tokens < 0 || num_blocks < 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "negative size or non-positive block size");
+  if (!error || !aligned(error, 4)) return fail(PA_ERR_INVALID_ARG, "null or misaligned error word");
+  if (num_tokens > 0 && (!slot_mapping || !aligned(slot_mapping, 8)))
+    return fail(PA_ERR_INVALID_ARG, "null or misaligned slot mapping");
+  pa::CheckParams p{};
+  p.slots = num_tokens > 0 ? slot_mapping : reinterpret_cast<const int64_t*>(error);  // non-null: slots mode
+  p.err = error;
+  p.num_items = num_tokens;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  return hip_status(pa::launch_check(p, static_cast<hipStream_t>(stream)), "check launch");
+}
+
 const char* pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "PA_OK";

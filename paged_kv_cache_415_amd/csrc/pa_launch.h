@@ -144,7 +144,25 @@ struct PrefillParams {
   int cache_dtype;     // K and V pools: q_dtype, or fp8 beside 16-bit queries
 };
 
+// Index checks (flags numerically equal to the public pa_check_flag values).
+enum : int { kCheckBlockId = 1, kCheckLength = 2, kCheckSlot = 4, kCheckChunk = 8 };
+
+struct CheckParams {
+  const int* block_tables;      // tables check (slots == nullptr)
+  const int* seq_lens;
+  const int* query_start_loc;   // optional
+  const int64_t* slots;         // slots check
+  int* err;                     // device int32[3]
+  int num_items;                // sequences or tokens
+  int max_blocks;
+  int block_size;
+  int num_blocks;
+  int max_len;
+  int total;                    // total query tokens (chunk check)
+};
+
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t stream);
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t stream);
 hipError_t launch_copy_rows(const CopyRowsParams& p, hipStream_t stream);
 hipError_t launch_copy_layers(const CopyLayersParams& p, hipStream_t stream);

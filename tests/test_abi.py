@@ -293,3 +293,19 @@ def test_noalloc_decode_rejects_a_batch_beyond_its_array(lib):
                                  BF16, BF16, 1.0, 1.0, 0, None) == INVALID
     assert lib.pa_decode_noalloc(None, None, None, None, None, None, 0.1, 16, 0, 8, 2, 128, 8, 128,
                                  BF16, BF16, 1.0, 1.0, 0, None) == OK
+
+
+def test_index_checks_reject_bad_arguments(lib):
+    fake = ctypes.c_void_p(256)
+    # (tables, lens, qsl, num_seqs, total, max_blocks, block_size, num_blocks, max_len, error, stream)
+    assert lib.pa_check_block_tables(fake, fake, None, 4, 0, 8, 16, 100, 0, None, None) == INVALID
+    assert lib.pa_check_block_tables(fake, fake, None, -1, 0, 8, 16, 100, 0, fake, None) == INVALID
+    assert lib.pa_check_block_tables(fake, fake, None, 4, 0, 0, 16, 100, 0, fake, None) == INVALID
+    assert lib.pa_check_block_tables(None, None, None, 4, 0, 8, 16, 100, 0, fake, None) == INVALID
+    assert lib.pa_check_block_tables(fake, fake, ctypes.c_void_p(258), 4, 0, 8, 16, 100, 0, fake,
+                                     None) == INVALID                      # misaligned offsets
+    # (slots, tokens, num_blocks, block_size, error, stream)
+    assert lib.pa_check_slots(fake, 5, 100, 16, None, None) == INVALID
+    assert lib.pa_check_slots(None, 5, 100, 16, fake, None) == INVALID
+    assert lib.pa_check_slots(ctypes.c_void_p(260), 5, 100, 16, fake, None) == INVALID
+    assert lib.pa_check_slots(fake, 5, 100, 0, fake, None) == INVALID
