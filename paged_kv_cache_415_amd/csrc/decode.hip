@@ -79,6 +79,18 @@ constexpr int kChunksPerWave = 1;       // balanced cut: chunks per wave, on ave
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Issue priority from a wave's progress through its work unit (done of
+// total steps, both wave-uniform): the more of it is left, the higher the
+// priority, so that waves which lose issue arbitration (the younger ones of
+// a SIMD) catch up and the waves of a CU finish together.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const int q = (4 * done) / max(total, 1);
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Block-table rows are read through the constant address space: uniform
 // indices then become scalar loads (the kernels never write the tables).
 typedef const __attribute__((address_space(4))) int* ctab_ptr;
@@ -156,6 +168,7 @@ struct LocalMerge {
   float* ml;
   int* cnt;
   int base, stride, odd0, counter;
+  int prog0, prog_len;   // steps of the wave's work unit done before this segment, and in all
   __device__ __forceinline__ int slot(int part) const { return stride * (base + part) + (part == 0 ? odd0 : 0); }
 };
 
@@ -602,6 +615,7 @@ struct MfmaDecode {
       Ids nxt = ids(trow, nblk, min(j0 + 1, j1 - 1));
       load(A, cur, p, kvh, j0);
       for (int j = j0; j < j1; j += 2) {
+        if (lm.prog_len > 0) progress_priority(lm.prog0 + j - j0, lm.prog_len);
         cur = nxt;
         nxt = ids(trow, nblk, min(j + 2, j1 - 1));
         if (j + 1 < j1) load(B, cur, p, kvh, j + 1);
@@ -633,6 +647,7 @@ struct MfmaDecode {
         }
       }
       for (int j = jfirst; j < j1; ++j) {
+        if (lm.prog_len > 0) progress_priority(lm.prog0 + j - j0, lm.prog_len);
         const Ids nxt = ids(trow, nblk, min(j + 1, j1 - 1));
         if constexpr (APPEND) {
           if (appends && j == j1 - 1) {
@@ -788,7 +803,8 @@ template <class Seg>
 __device__ __forceinline__ void run_chunk(const DecodeParams& p, const int* lens, const int* pre,
                                           int T, int chunk, int k, LocalMerge lm, int k0, int k1) {
   const int S = p.num_seqs, H = p.num_kv_heads;
-  int u = k * chunk;
+  const int ustart = k * chunk;
+  int u = ustart;
   const int uend = min(T, u + chunk);
   int s = find_seq(pre, S, u / H);
   int base = uni(pre[s]);
@@ -805,6 +821,8 @@ __device__ __forceinline__ void run_chunk(const DecodeParams& p, const int* lens
     lm.base = wf - k0;
     lm.odd0 = ps % chunk != 0;
     lm.counter = (lm.slots != nullptr && wf >= k0 && wl < k1) ? wf - k0 : -1;
+    lm.prog0 = u - ustart;
+    lm.prog_len = uend - ustart;
     Seg::segment(p, s, h, uni(lens[s]), j, j1, k - wf, wl - wf + 1, lm);
     u += j1 - j;
     if (u >= uend) break;
@@ -839,6 +857,8 @@ __device__ __forceinline__ void run_item(const DecodeParams& p, const int* lens,
   lm.base = first - k0;
   lm.odd0 = 0;
   lm.counter = (lm.slots != nullptr && first >= k0 && first + q <= k1) ? first - k0 : -1;
+  lm.prog0 = 0;
+  lm.prog_len = 0;   // items differ in length and come from a queue: no progress priority
   Seg::segment(p, s, h, len, j0, j1, part, q, lm);
 }
 
@@ -907,6 +927,8 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
   lm.base = 0;
   lm.odd0 = 0;
   lm.counter = -1;
+  lm.prog0 = 0;
+  lm.prog_len = 1;
   for (int k = k0 + take_ticket(&queue); k < k1; k = k0 + take_ticket(&queue)) {
     if (p.mode == kSplitBalanced) run_chunk<Seg>(p, lens, pre, T, chunk, k, lm, k0, k1);
     else run_item<Seg>(p, lens, pre, k, lm, k0, k1);
