@@ -335,9 +335,18 @@ struct MfmaDecode {
     f32x4 acc[DPL];
   };
 
+  struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+  };
+
+  // One step's products and softmax.  `after_scores` runs once the step's
+  // score products are issued, i.e. after the 8-bit K staging's LDS reads
+  // were waited for: scalar loads issued there (block ids of a later step)
+  // are not covered by that wait.
+  template <class Hook = NoHook>
   static __device__ __forceinline__ void compute(Buf& buf, State& st, const u32x4 (&qop)[NC],
                                                  float qk_scale_log2, int len, int j,
-                                                 char* kst = nullptr) {
+                                                 char* kst = nullptr, Hook after_scores = Hook()) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4;
     const int rel0 = j * kStep;
@@ -404,6 +413,7 @@ struct MfmaDecode {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) sc = Mma<QT>::mma(ka[c], qop[c], sc);
+      if (tau == 1) after_scores();
       // int8: the block's K scale joins the logit scale
       const float cs = kBlockScales ? qk_scale_log2 * buf.ks[tau] : qk_scale_log2;
 #pragma unroll
@@ -414,8 +424,7 @@ struct MfmaDecode {
     }
     float smax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                        fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    smax = xor_max(smax, 16);
-    smax = xor_max(smax, 32);
+    smax = lanes4_max(smax);
     // Lazy rescaling: the reference max moves (and the accumulators are
     // rescaled) only when some head's max exceeds it by more than the slack,
     // so probabilities stay <= 2^slack.  The first step always sets it (st.m
@@ -611,20 +620,25 @@ struct MfmaDecode {
     // register count low enough for more waves per SIMD.
     Ids cur = ids(trow, nblk, j0);
     if constexpr (kDoubleBuffer) {
+      // Block ids are fetched two steps ahead: those of step j + 3 while step
+      // j is computed, after its K staging (see compute), so that neither an
+      // LDS wait nor the next step's loads wait for them.
       Buf A, B;
-      Ids nxt = ids(trow, nblk, min(j0 + 1, j1 - 1));
+      Ids n1 = ids(trow, nblk, min(j0 + 1, j1 - 1));
+      Ids n2 = ids(trow, nblk, min(j0 + 2, j1 - 1));
       load(A, cur, p, kvh, j0);
       for (int j = j0; j < j1; j += 2) {
         if (lm.prog_len > 0) progress_priority(lm.prog0 + j - j0, lm.prog_len);
-        cur = nxt;
-        nxt = ids(trow, nblk, min(j + 2, j1 - 1));
-        if (j + 1 < j1) load(B, cur, p, kvh, j + 1);
-        compute(A, st, qop, p.qk_scale_log2, len, j, kst);
+        Ids n3, n4;
+        if (j + 1 < j1) load(B, n1, p, kvh, j + 1);
+        compute(A, st, qop, p.qk_scale_log2, len, j, kst,
+                [&] { n3 = ids(trow, nblk, min(j + 3, j1 - 1)); });
         if (j + 1 >= j1) break;
-        cur = nxt;
-        nxt = ids(trow, nblk, min(j + 3, j1 - 1));
-        if (j + 2 < j1) load(A, cur, p, kvh, j + 2);
-        compute(B, st, qop, p.qk_scale_log2, len, j + 1, kst);
+        if (j + 2 < j1) load(A, n2, p, kvh, j + 2);
+        compute(B, st, qop, p.qk_scale_log2, len, j + 1, kst,
+                [&] { n4 = ids(trow, nblk, min(j + 4, j1 - 1)); });
+        n1 = n3;
+        n2 = n4;
       }
     } else {
       int jfirst = j0;
@@ -664,8 +678,7 @@ struct MfmaDecode {
       }
     }
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
-    float l_tot = xor_sum(st.l, 16);
-    l_tot = xor_sum(l_tot, 32);
+    const float l_tot = lanes4_sum(st.l);
     if constexpr (kLocalMerge) {
       if (nparts > 1 && lm.counter >= 0) {
         merge_local(p, st.acc, st.m, l_tot, s, kvh, part, nparts, lm);

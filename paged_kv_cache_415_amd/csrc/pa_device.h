@@ -164,6 +164,25 @@ __device__ __forceinline__ void wave_lds_acquire() {
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48, with gfx950's
+// row-swapping lane permutes: vector-ALU operations that, unlike the LDS
+// path of __shfl_xor, add nothing to the LDS / scalar-memory counter, so a
+// wait for them never waits for scalar loads in flight.  Both lanes of a
+// pair add the same two values (commutative), so every lane gets the same
+// bits as the __shfl_xor form.
+__device__ __forceinline__ float lanes4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lanes4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Byte permute: result byte k = sel byte k picks from {lo bytes 0-3 (0..3),
 // hi bytes 0-3 (4..7)}; 0x0C gives a zero byte.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
