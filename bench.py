@@ -27,11 +27,11 @@ with torch's seeded generator (same distributions).  R batches with separate
 pools are rotated so that no step finds its KV in the 256 MB last-level
 cache.
 
-The CPU baseline runs the fp64 oracle, as it stands, on bounded samples of
-the same workloads (generated on the CPU by workloads.py), before the GPU is
-touched: on every host core this process may use (one oracle process per
-core, sequences or heads spread over them) and, for the two smallest
-workloads, on one thread.
+The CPU baseline runs the fp64 oracle, as it stands, on the same workloads
+(generated on the CPU by workloads.py: the whole headline and 70B-shaped
+batches, bounded samples of the others), before the GPU is touched: on every
+host core this process may use (one oracle process per core, sequences or
+heads spread over them) and, for the two smallest workloads, on one thread.
 
 Printed: one JSON line with the step rate, a roofline object for the
 dominant kernel (its average duration measured with HIP events on the
@@ -607,9 +607,9 @@ def probe_read_gbps(dev, nbytes=4 << 30, iters=10):
 # CPU baseline: the oracle, as it stands, on bounded samples, on the host's cores
 # ---------------------------------------------------------------------------
 
-# Samples (CPU-generated by workloads.py with the bench's seeds): sequences
-# taken from the front of each workload's seeded batch.
-CPU_SAMPLES = {"llama3_8b_gqa_bf16": 64, "llama2_7b_mha_f16": 16, "llama3_70b_fp8kv": 32,
+# Samples (CPU-generated by workloads.py with the bench's seeds): the whole
+# seeded batch (None) or the sequences at its front.
+CPU_SAMPLES = {"llama3_8b_gqa_bf16": None, "llama2_7b_mha_f16": 16, "llama3_70b_fp8kv": None,
                "tiny_f32": None}
 MIXED_SAMPLE = dict(num_forks=4, num_decode=28)
 _CPU = {}          # inputs shared with the forked oracle processes
@@ -709,9 +709,11 @@ def cpu_baseline(args) -> dict:
             dt = time.perf_counter() - t0
             eff = W.effective_kv_bytes(case.seq_lens, spec.num_kv_heads, spec.head_dim,
                                        spec.cache_dtype, spec.v_dtype)
+            what = (f"all {len(case.seq_lens)} sequences" if CPU_SAMPLES[name] is None
+                    else f"the first {len(case.seq_lens)} sequences")
             out["configs"][name] = {
-                "sample": f"first {len(case.seq_lens)} sequences of the seeded batch "
-                          f"({int(case.seq_lens.sum())} context tokens, all heads)",
+                "sample": f"{what} of the seeded batch ({int(case.seq_lens.sum())} context tokens, "
+                          f"all heads)",
                 "oracle_wall_s": round(dt, 4), "sample_effective_bytes": eff,
                 "oracle_gbps": round(eff / dt / 1e9, 4)}
         # mixed step: every prefill chunk (one process each) and the decodes
@@ -754,11 +756,10 @@ def cpu_baseline(args) -> dict:
     head = out["configs"][HEADLINE]
     out["value"] = head["oracle_gbps"]
     out["unit"] = "GB/s"
-    out["sample"] = (f"fp64 oracle decode of the first {CPU_SAMPLES[HEADLINE]} sequences of the "
-                     f"{HEADLINE} batch on {cores} cores (one oracle process per core, one BLAS "
-                     f"thread each, sequences longest first), {head['oracle_wall_s']} s wall; "
-                     f"the other workloads' samples under 'configs', one-thread runs under "
-                     f"'one_thread'")
+    out["sample"] = (f"fp64 oracle decode of {head['sample']} of {HEADLINE} on {cores} cores "
+                     f"(one oracle process per core, one BLAS thread each, sequences longest "
+                     f"first), {head['oracle_wall_s']} s wall; the other workloads' samples under "
+                     f"'configs', one-thread runs under 'one_thread'")
     return out
 
 
