@@ -374,7 +374,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   const int kend = ctx0 + last_pos + 1;     // keys [0, kend) can be visible to this tile
   const int* trow = p.block_tables + (int64_t)seq * p.max_blocks;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a wave-uniform value: block ids, copy addresses and the
+  // LDS-DMA destinations (M0) derived from it stay in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4, c16 = lane & 15;
   // logit = c * (q . k) with c = scale * k_scale * log2(e); a negative c is
   // applied as |c| with q negated, so maxima of raw products are maxima of
