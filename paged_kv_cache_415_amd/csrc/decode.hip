@@ -243,7 +243,8 @@ struct MfmaDecode {
   // partials of pairs inside one workgroup's share are merged in LDS
   static constexpr bool kLocalMerge = true;
   // waves per workgroup = waves one CU keeps resident at this register count
-  static constexpr int kWaves = D == 64 ? 16 : (KF8 && VF8 ? 8 : 12);
+  // (int8 at D = 64 needs a few registers more than 16 waves allow)
+  static constexpr int kWaves = D == 64 ? (kBlockScales ? 12 : 16) : (KF8 && VF8 ? 8 : 12);
 
   struct Buf {
     u32x4 k[2][KL];
@@ -330,8 +331,13 @@ struct MfmaDecode {
     }
   }
 
+  // m: the reference max (log2 units); l4: the sums of the rounded
+  // probabilities, formed on the matrix cores by a value product against an
+  // all-ones operand (every element of a lane's l4 holds its head's sum over
+  // all the tokens so far); acc: the unnormalised output.
   struct State {
-    float m, l;
+    float m;
+    f32x4 l4;
     f32x4 acc[DPL];
   };
 
@@ -417,13 +423,18 @@ struct MfmaDecode {
       // int8: the block's K scale joins the logit scale
       const float cs = kBlockScales ? qk_scale_log2 * buf.ks[tau] : qk_scale_log2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rel = rel0 + 16 * tau + 4 * G + i;
-        s[tau][i] = (rel < len) ? mul_rn(sc[i], cs) : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) s[tau][i] = mul_rn(sc[i], cs);
     }
-    float smax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    // tokens past the end (only in a pair's last step) take logit -inf
+    if (rel0 + kStep > len) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (rel0 + 16 * tau + 4 * G + i >= len) s[tau][i] = -INFINITY;
+    }
+    float smax = fmax_nan(fmax_nan(fmax_nan(s[0][0], s[0][1]), fmax_nan(s[0][2], s[0][3])),
+                          fmax_nan(fmax_nan(s[1][0], s[1][1]), fmax_nan(s[1][2], s[1][3])));
     smax = lanes4_max(smax);
     // Lazy rescaling: the reference max moves (and the accumulators are
     // rescaled) only when some head's max exceeds it by more than the slack,
@@ -433,27 +444,27 @@ struct MfmaDecode {
       const float m_new = fmaxf(st.m, smax);
       const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
       st.m = m_new;
-      st.l *= alpha;
+      st.l4 = st.l4 * alpha;
 #pragma unroll
       for (int n = 0; n < DPL; ++n) st.acc[n] = st.acc[n] * alpha;
     }
-    uint32_t pw[4];
-    float psum = 0.f;
+    uint32_t pw[4], pr[4];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         const float a = __builtin_amdgcn_exp2f(s[tau][i] - st.m);
         const float b = __builtin_amdgcn_exp2f(s[tau][i + 1] - st.m);
-        const uint32_t w = pack2<QT>(a, b);
+        pr[tau * 2 + i / 2] = pack2<QT>(a, b);
         // int8: the value operand carries the block's V scale; the sum does not
-        pw[tau * 2 + i / 2] = kBlockScales ? pack2<QT>(a * buf.vs[tau], b * buf.vs[tau]) : w;
-        // sum the rounded probabilities so that the weights stay normalised
-        psum += lo_f32<QT>(w) + hi_f32<QT>(w);
+        pw[tau * 2 + i / 2] = kBlockScales ? pack2<QT>(a * buf.vs[tau], b * buf.vs[tau]) : pr[tau * 2 + i / 2];
       }
     }
-    st.l += psum;
     const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]};
+    // the sum of the rounded probabilities (so that the weights stay
+    // normalised): their product with an all-ones operand
+    st.l4 = Mma<QT>::mma(u32x4{kOnes<QT>, kOnes<QT>, kOnes<QT>, kOnes<QT>},
+                         u32x4{pr[0], pr[1], pr[2], pr[3]}, st.l4);
 
     // Values: A operand for dim DPL*c16 + n holds tokens 4G+0..3 of tile 0
     // then 4G+0..3 of tile 1.
@@ -610,7 +621,7 @@ struct MfmaDecode {
 
     State st;
     st.m = -INFINITY;
-    st.l = 0.f;
+    st.l4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < DPL; ++n) st.acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -678,7 +689,7 @@ struct MfmaDecode {
       }
     }
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
-    const float l_tot = lanes4_sum(st.l);
+    const float l_tot = st.l4[0];
     if constexpr (kLocalMerge) {
       if (nparts > 1 && lm.counter >= 0) {
         merge_local(p, st.acc, st.m, l_tot, s, kvh, part, nparts, lm);

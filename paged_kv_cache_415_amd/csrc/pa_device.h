@@ -164,24 +164,26 @@ __device__ __forceinline__ void wave_lds_acquire() {
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
 
-// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48, with gfx950's
+// Maximum that propagates NaN (v_maximum / v_maximum3_f32): unlike fmaxf it
+// needs no canonicalisation of operands that come from lane moves.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48, with gfx950's
 // row-swapping lane permutes: vector-ALU operations that, unlike the LDS
 // path of __shfl_xor, add nothing to the LDS / scalar-memory counter, so a
-// wait for them never waits for scalar loads in flight.  Both lanes of a
-// pair add the same two values (commutative), so every lane gets the same
-// bits as the __shfl_xor form.
+// wait for them never waits for scalar loads in flight.
 __device__ __forceinline__ float lanes4_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float lanes4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+
+// Two 1.0 values of a 16-bit type, packed: the all-ones matrix operand whose
+// product with a probability operand sums it.
+template <typename T> inline constexpr uint32_t kOnes = 0;
+template <> inline constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
+template <> inline constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;
 
 // Byte permute: result byte k = sel byte k picks from {lo bytes 0-3 (0..3),
 // hi bytes 0-3 (4..7)}; 0x0C gives a zero byte.

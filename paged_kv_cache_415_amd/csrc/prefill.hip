@@ -36,15 +36,6 @@ namespace pa {
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(4))) int* ctab_ptr;   // block table, read-only
 
-// Maximum that propagates NaN (v_maximum3_f32; no operand canonicalisation).
-__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (lane swaps, no LDS).
-__device__ __forceinline__ float max_over_groups(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 // ds_read_b64_tr_b16 at LDS byte address `addr` + OFF.  Issued as inline
 // assembly: the compiler treats the builtin as possibly aliasing the LDS-DMA
@@ -266,10 +257,6 @@ struct TileSrc8 {
     }
   }
 };
-
-template <typename T> constexpr uint32_t kOnes = 0;                  // two 1.0 values
-template <> constexpr uint32_t kOnes<__bf16> = 0x3F803F80u;
-template <> constexpr uint32_t kOnes<_Float16> = 0x3C003C00u;
 
 // Value product of a tile held in the stage at LDS address `stage`:
 // acc[b][nb] += V^T(dims 16 nb .., keys) P^T(keys, rows of column tile b),
@@ -516,7 +503,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
           if (a + i > 0) mx[b] = fmax_nan(mx[b], s[a][b][i]);
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) mx[b] = max_over_groups(mx[b]) * cscale;   // cscale > 0: -inf stays -inf
+    for (int b = 0; b < 2; ++b) mx[b] = lanes4_max(mx[b]) * cscale;   // cscale > 0: -inf stays -inf
     // Lazy rescaling (as in decode): the reference max moves only when a
     // row's max exceeds it by more than kSlack, so p <= 2^kSlack; when it
     // moves for some row, every row of the wave takes its exact new max.  A
