@@ -559,3 +559,35 @@ def test_int8_f16_queries_large_value_scales(partition):
     # relative to the values' size: f16 keeps 11 significant bits
     err = max_abs(out, ref)
     assert err <= TOL["f16"] * float(np.abs(ref).max()) / 4, err
+
+
+LONG = [("bf16", "bf16", 32, 8), ("bf16", "fp8_e4m3", 64, 8)]
+_LONG_CASES = {}
+
+
+def _long_case(q_dt, c_dt, hq, hkv):
+    """Contexts of 131,072 and 70,001 tokens beside two short ones (D 128,
+    block 16); built and checked against the oracle once per format."""
+    key = (q_dt, c_dt, hq, hkv)
+    if key not in _LONG_CASES:
+        spec = custom_spec(f"long_{c_dt}_{hq}_{hkv}", hq, hkv, 128, 16, q_dt, c_dt)
+        case = W.make_decode_case(spec, lens=[131072, 70001, 1, 4097])
+        ref, _, _ = oracle_step(case)
+        _LONG_CASES[key] = (case, ref)
+    return _LONG_CASES[key]
+
+
+@pytest.mark.parametrize("q_dt,c_dt,hq,hkv", LONG)
+@pytest.mark.parametrize("partition", [0, 512, -1])
+def test_long_contexts(q_dt, c_dt, hq, hkv, partition):
+    """The split planning at its largest: the balanced cut's shortest range
+    grows with the longest context (256 steps here, 17 partials at most),
+    512-token partitions give 256 partials for the longest pair, and a whole
+    pair is one wave streaming 131,072 tokens."""
+    print(f"[decode parity] long contexts {c_dt} {hq}/{hkv} partition {partition}", flush=True)
+    case, ref = _long_case(q_dt, c_dt, hq, hkv)
+    run = DecodeRun(case)
+    run.scatter()
+    torch.cuda.synchronize()
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL[q_dt]
