@@ -143,6 +143,61 @@ __device__ void build_plan(const DecodeParams& p, int* lens, int* pre) {
   __syncthreads();
 }
 
+// Workgroup share of the fixed and whole cuts' item list: whole items, the
+// bounds at the item starts nearest to equal fractions of the batch's
+// 32-token units.  Items differ in length (a pair's last partition is
+// short), so equal item counts leave the shares' bytes up to ~20 % apart.
+// Bound i of workgroup b is the same function of (b + i) in every
+// workgroup, so neighbouring shares meet exactly.
+template <int NW>
+__device__ void unit_share(const DecodeParams& p, const int* lens, const int* pre, int* k0, int* k1) {
+  constexpr int NT = 64 * NW;
+  __shared__ int wave_units[NW];
+  __shared__ int bounds[2];
+  const int S = p.num_seqs, H = p.num_kv_heads;
+  const int per = (S + NT - 1) / NT;
+  const int b = min(S, (int)threadIdx.x * per), e = min(S, b + per);
+  int sum = 0;
+  for (int s = b; s < e; ++s) sum += (lens[s] + kStep - 1) / kStep;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wave_units[wave] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) run += wave_units[w];
+    total += wave_units[w];
+  }
+  const int64_t tot = (int64_t)total * H;
+  const int64_t x[2] = {tot * blockIdx.x / gridDim.x, tot * (blockIdx.x + 1) / gridDim.x};
+  int64_t o = (int64_t)run * H;
+  for (int s = b; s < e; ++s) {
+    const int U = (lens[s] + kStep - 1) / kStep;
+    const int64_t end = o + (int64_t)U * H;
+    for (int i = 0; i < 2; ++i) {
+      if (x[i] >= o && x[i] < end) {
+        const int64_t rem = x[i] - o;
+        const int h = (int)(rem / U), r = (int)(rem - (int64_t)h * U);
+        const int c = p.mode == kSplitNone ? U : p.chunk;   // units per item of this pair
+        const int q = pre[s + 1] - pre[s];
+        bounds[i] = pre[s] * H + h * q + min(q, (r + c / 2) / c);
+      }
+    }
+    o = end;
+  }
+  if (threadIdx.x == 0)
+    for (int i = 0; i < 2; ++i)
+      if (x[i] >= tot) bounds[i] = pre[S] * H;
+  __syncthreads();
+  *k0 = uni(bounds[0]);
+  *k1 = uni(bounds[1]);
+}
+
 // Largest s in [0, S) with pre[s] <= x, for 0 <= x < pre[S].
 __device__ __forceinline__ int find_seq(const int* pre, int S, int x) {
   int lo = 0, hi = S;
@@ -939,8 +994,13 @@ __global__ __launch_bounds__(Seg::kWaves * 64) void decode_kernel(DecodeParams p
     chunk = chunk < p.chunk ? p.chunk : chunk;
     nwork = (T + chunk - 1) / chunk;
   }
-  const int k0 = (int)((int64_t)nwork * blockIdx.x / gridDim.x);
-  const int k1 = (int)((int64_t)nwork * (blockIdx.x + 1) / gridDim.x);
+  int k0, k1;
+  if (p.mode == kSplitBalanced) {
+    k0 = (int)((int64_t)nwork * blockIdx.x / gridDim.x);
+    k1 = (int)((int64_t)nwork * (blockIdx.x + 1) / gridDim.x);
+  } else {
+    unit_share<NW>(p, lens, pre, &k0, &k1);
+  }
   // local merging needs a slot for every partial of the share
   LocalMerge lm;
   const int need = p.mode == kSplitBalanced ? 2 * (k1 - k0) : k1 - k0;
