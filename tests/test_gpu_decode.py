@@ -255,6 +255,39 @@ def test_zero_length_sequence_gives_zeros():
     assert max_abs(out[[0, 2]], ref[[0, 2]]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_gqa_bf16", "llama3_70b_fp8kv"])
+@pytest.mark.parametrize("partition", [0, 32, 512, -1])
+def test_runs_of_empty_sequences(name, partition):
+    """Empty sequences first, last and in runs, with every cut: their outputs
+    are zero, and the work shares of the others (cut by units, which empty
+    sequences do not have) and their merges are unaffected."""
+    lens = [1, 700, 1, 1, 45, 1300, 1, 33, 1, 1, 2049, 1]
+    empty = [0, 2, 3, 6, 8, 9, 11]
+    keep = [i for i in range(len(lens)) if i not in empty]
+    case = W.make_decode_case(name, lens=lens)
+    print(f"[decode parity] {name}, empty sequences {empty}, partition {partition}", flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    dl = np.array(lens, np.int32)
+    dl[empty] = 0
+    run.lens = up_int(dl)
+    out = run.decode(partition_size=partition)
+    ref, _, _ = oracle_step(case)
+    assert torch.count_nonzero(out[empty]) == 0
+    assert max_abs(out[keep], ref[keep]) <= TOL[case.spec.q_dtype]
+
+
+def test_all_sequences_empty():
+    """A batch whose sequences are all empty: every output is zero, every cut."""
+    case = W.make_decode_case("llama3_8b_gqa_bf16", lens=[1, 1, 1, 1])
+    run = DecodeRun(case)
+    run.scatter()
+    run.lens = up_int(np.zeros(4, np.int32))
+    for partition in (0, 32, -1):
+        out = run.decode(partition_size=partition)
+        assert torch.count_nonzero(out) == 0
+
+
 SWEEP = [
     # (q, cache, Hq, Hkv, D, bs)
     ("bf16", "bf16", 8, 8, 128, 16),
