@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--config", default="all",
                     help="all (headline llama3_8b_gqa_bf16 plus the other workloads) | "
                          "llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
-                         "| llama3_8b_int8kv "
+                         "| llama3_8b_int8kv | llama3_70b_fp8kv_tp8 "
                          "| tiny_f32 "
                          "| mixed_prefix_bf16")
     ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
@@ -816,7 +816,8 @@ def main():
         sys.exit(2)
     import torch
     if args.config != "all" and args.config not in SUB_CONFIGS + [HEADLINE, "llama3_8b_int8kv",
-                                                                   "llama3_8b_kfp8_vbf16"]:
+                                                                   "llama3_8b_kfp8_vbf16",
+                                                                   "llama3_70b_fp8kv_tp8"]:
         print(f"unknown --config {args.config}", file=sys.stderr)
         sys.exit(2)
     # the CPU baseline forks oracle processes, so it runs before the GPU is initialised

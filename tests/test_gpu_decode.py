@@ -16,7 +16,7 @@ from gpu_cases import TOL, DecodeRun, as_f64, custom_spec, lib, max_abs, oracle_
 pytestmark = pytest.mark.gpu
 
 FULL_CONFIGS = ["tiny_f32", "llama2_7b_mha_f16", "llama3_8b_gqa_bf16", "llama3_70b_fp8kv",
-                "llama3_8b_kfp8_vbf16", "llama3_8b_int8kv"]
+                "llama3_8b_kfp8_vbf16", "llama3_8b_int8kv", "llama3_70b_fp8kv_tp8"]
 
 
 @pytest.fixture(scope="module")
@@ -253,6 +253,19 @@ def test_zero_length_sequence_gives_zeros():
     ref, _, _ = oracle_step(case)
     assert torch.count_nonzero(out[1]) == 0
     assert max_abs(out[[0, 2]], ref[[0, 2]]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("partition", [0, -1])
+def test_tp8_share_other_cuts(partition, full_cases):
+    """The tensor-parallel share of the 70B-shaped layer (one KV head) with
+    the balanced cut and whole pairs: few pairs, so most waves of a launch
+    have no work."""
+    case, (ref, _, _) = full_cases("llama3_70b_fp8kv_tp8")
+    print(f"[decode parity] llama3_70b_fp8kv_tp8, partition {partition}", flush=True)
+    run = DecodeRun(case)
+    run.scatter()
+    out = run.decode(partition_size=partition)
+    assert max_abs(out, ref) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_gqa_bf16", "llama3_70b_fp8kv"])

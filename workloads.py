@@ -160,6 +160,7 @@ class DecodeSpec:
     per_tensor_fp8_scale: bool = False
     description: str = ""
     v_cache_dtype: str | None = None   # V pool type when it differs from the K pool's
+    seed_name: str | None = None       # draw lengths and block order from another workload's stream
 
     @property
     def v_dtype(self) -> str:
@@ -201,6 +202,17 @@ DECODE_SPECS = {
         description="70B-shaped layer on one GPU: 128 sequences, 64/8 heads, head_dim 128, block 16, "
                     "lens lognormal(median 1500, sigma 0.8) in [16,8192], fp8 e4m3 KV with "
                     "per-tensor scales, bf16 q, 512-token split-KV partitions"),
+    # One GPU's share of the 70B-shaped layer under 8-way tensor parallelism (KV
+    # heads split across GPUs): the same sequences, lengths and block order, one
+    # KV head and its 8 query heads.
+    "llama3_70b_fp8kv_tp8": DecodeSpec(
+        "llama3_70b_fp8kv_tp8", 128, 8, 1, 128, 16, "bf16", "fp8_e4m3",
+        ("lognormal", 1500.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
+        partition_size=512, per_tensor_fp8_scale=True, seed_name="llama3_70b_fp8kv",
+        description="one GPU's share of the 70B-shaped layer under 8-way tensor parallelism: "
+                    "the same 128 sequences and lengths, 1 KV head and its 8 query heads, "
+                    "head_dim 128, block 16, fp8 e4m3 KV with per-tensor scales, bf16 q, "
+                    "512-token split-KV partitions"),
     "llama3_8b_int8kv": DecodeSpec(
         "llama3_8b_int8kv", 256, 32, 8, 128, 16, "bf16", "int8",
         ("lognormal", 1200.0, 0.8, 16, 8192), ("factor", 1.1), 1.0, 8192,
@@ -286,7 +298,7 @@ def make_decode_layout(spec: DecodeSpec | str, rep: int = 0, num_seqs: int | Non
     newest token's slot for every sequence (no element values)."""
     if isinstance(spec, str):
         spec = DECODE_SPECS[spec]
-    rng = _rng(spec.name, rep)
+    rng = _rng(spec.seed_name or spec.name, rep)
     S = spec.num_seqs if num_seqs is None else num_seqs
     bs = spec.block_size
     if lens is None:
