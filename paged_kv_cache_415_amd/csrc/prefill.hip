@@ -342,10 +342,24 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int xq = nwg / kXcds, xr = nwg % kXcds;
   const int xcd = lin % kXcds, slot = lin / kXcds;
-  const int work = xcd * xq + min(xcd, xr) + slot;   // a bijection of [0, nwg)
-  const int qtile = work % gridDim.x;
-  const int kvh = (work / gridDim.x) % gridDim.y;
-  const int seq = work / (gridDim.x * gridDim.y);
+  // Longest first: a later query tile sees more keys, and the long ones
+  // should not be the last to start.  When each XCD's range holds whole
+  // (sequence, KV head) groups, its workgroups start in order of query tile,
+  // last tile first, across the groups; otherwise each group's tiles run
+  // last tile first.
+  const int nq = gridDim.x;
+  int work;
+  int qtile;
+  if (xr == 0 && xq % nq == 0) {
+    const int groups = xq / nq;                      // groups per XCD
+    qtile = nq - 1 - slot / groups;
+    work = xcd * xq + (slot % groups) * nq + qtile;
+  } else {
+    work = xcd * xq + min(xcd, xr) + slot;           // a bijection of [0, nwg)
+    qtile = nq - 1 - work % nq;
+  }
+  const int kvh = (work / nq) % gridDim.y;
+  const int seq = work / (nq * gridDim.y);
   const int g = p.group;
   const int qpos = kRowsPerWG / g;          // chunk positions per workgroup
   const int q0 = p.query_start_loc[seq];
