@@ -18,7 +18,8 @@
 // the others go to the workspace and the reduce kernel merges them.  Two other
 // cuts exist: fixed partitions of a given length from each sequence's start,
 // and whole pairs (no partials at all).  Each workgroup owns an even share of
-// the chunks (or items); its waves take them from an LDS queue.
+// the chunks, or, for the other two cuts, a run of whole items holding about
+// an equal share of the units; its waves take them from an LDS queue.
 //
 // Within a segment a wave walks 32-token steps; K/V are read with 16-byte
 // non-temporal loads (each byte is used once).  Block-table entries are read
