@@ -9,7 +9,9 @@ partials (pa_decode_reduce), all on torch's current stream; for 16-bit caches
 the headline also reports the step with the scatter folded into the decode
 kernel (pa_decode_attention_append + pa_decode_reduce).  For the mixed
 workload a step is copy-on-write (pa_copy_blocks), the scatter of every new
-token, the causal prefill chunks (pa_prefill_chunk) and the decodes.
+token, and the attention of the causal prefill chunks and the decodes in one
+launch (pa_mixed_attention); the same step with separate pa_prefill_chunk,
+pa_decode_attention and pa_decode_reduce launches is timed beside it.
 
 By default (--config all) the headline is the largest single-GPU decode
 workload, the Llama-3-8B-shaped GQA layer (256 sequences, 32/8 heads,
@@ -347,6 +349,16 @@ def run_mixed_bench(args, dev):
     max_len = int(case.decode_lens.max())
     ws = pa.decode_workspace(qd, kp, max_len)
 
+    def fused_step(ev=None):
+        pa.pa_copy_blocks(kp, vp, pairs)
+        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
+        if ev is not None:
+            ev[0].record()
+        pa.pa_mixed_attention(out_c, qc, qsl, ptab, plen, max_q, out_d, qd, dtab, dlen, max_len, kp, vp,
+                              s.scale, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
     def step(ev=None, side=None):
         pa.pa_copy_blocks(kp, vp, pairs)
         pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
@@ -368,16 +380,27 @@ def run_mixed_bench(args, dev):
         if ev is not None:
             ev[2].record()
         pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+        if ev is not None:
+            ev[3].record()
 
     for _ in range(args.warmup):
         step()
+        fused_step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the step with the prefill chunks and the decodes in one launch
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fused_step(fevs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # the same step as separate prefill, decode and reduce launches
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    sep_elapsed = time.perf_counter() - t0
     # the same step captured as one HIP graph with the prefill and the decode
     # on forked streams (timed after the eager measurement above)
     graph_ms = None
@@ -396,7 +419,10 @@ def run_mixed_bench(args, dev):
         graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fevs]))
+    sep_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
     ms_step = elapsed * 1e3 / args.steps
+    sep_ms_step = sep_elapsed * 1e3 / args.steps
     flops = mixed_prefill_flops(case)
     eff = W.effective_kv_bytes(case.decode_lens, s.num_kv_heads, s.head_dim, dt)
     tflops = flops / (pre_ms * 1e-3) / 1e12
@@ -419,6 +445,15 @@ def run_mixed_bench(args, dev):
                             "traffic": decode_traffic_bytes(s.name, "decode"),
                             "traffic_unit": "bytes per launch",
                             "algorithmic_bytes_per_launch": eff, "avg_launch_ms": round(dec_ms, 5)},
+        "fused_attention": {
+            "kernels": "mixed_kernel + lse_reduce_kernel (pa_mixed_attention)",
+            "avg_ms": round(fused_ms, 5),
+            "prefill_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
+            "decode_gbps": round(eff / (fused_ms * 1e-3) / 1e9, 1),
+            "mfma_frac": round(flops / (fused_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "hbm_frac": round(eff / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "separate_launches_ms": round(sep_ms, 5)},
+        "separate_launches_ms_per_step": round(sep_ms_step, 5),
         "prefill_flops": flops, "effective_kv_bytes_per_step": eff,
         "prefill_tflops": round(tflops, 2), "decode_gbps": round(dec_gbps, 1),
         "prefill_tokens_per_s": round(int(case.query_start_loc[-1]) / (pre_ms * 1e-3), 1),
@@ -520,8 +555,10 @@ def run_block_ops_bench(dev, iters: int = 20) -> dict:
 # HBM traffic of the decode kernel from committed rocprofv3 counter runs
 # ---------------------------------------------------------------------------
 
-KERNEL_SOURCES = {"decode": ["decode.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"],
-                  "prefill": ["prefill.hip", "pa_device.h", "pa_launch.h", "pa_api.cpp"]}
+KERNEL_SOURCES = {"decode": ["decode.hip", "decode_dev.h", "pa_device.h", "pa_launch.h", "pa_api.cpp"],
+                  "prefill": ["prefill.hip", "prefill_dev.h", "pa_device.h", "pa_launch.h", "pa_api.cpp"],
+                  "mixed": ["mixed.hip", "decode_dev.h", "prefill_dev.h", "pa_device.h", "pa_launch.h",
+                            "pa_api.cpp"]}
 
 
 def traffic_profile(name: str) -> str:

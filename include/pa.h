@@ -470,6 +470,45 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
                            float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_mixed_attention — the attention of one mixed serving step in one
+ * launch: the prefill chunks of some sequences and the one-token decodes of
+ * others, over the same K/V pools.
+ *
+ * [aieng] "推理引擎内部机制", section "调度器长什么样": each engine step
+ * batches prefill chunks with decodes and runs them as one fused GPU call;
+ * [bogosort] §15 Chunked Prefill for the chunks.  The prefill part computes
+ * pa_prefill_chunk over (prefill_out, prefill_q, query_start_loc,
+ * prefill_block_tables, prefill_seq_lens, num_chunks, total_q_tokens,
+ * max_q_len, prefill_max_blocks_per_seq) and the decode part pa_decode over
+ * (decode_out, decode_q, decode_block_tables, decode_seq_lens, num_decodes,
+ * decode_max_blocks_per_seq, max_seq_len, partition_size, workspace); the
+ * remaining arguments are common to both, with the meaning, layouts, limits
+ * and errors of those two calls.  Either part may be empty (num_chunks or
+ * total_q_tokens 0; num_decodes 0).
+ *
+ * Supported: bf16 or f16 queries over a cache of the same type (cache_dtype
+ * == q_dtype; other pairs return PA_ERR_UNSUPPORTED).  The prefill outputs
+ * equal pa_prefill_chunk's bit for bit; the decode outputs may differ from
+ * a pa_decode call by rounding, since the work is cut for this launch's
+ * waves.  The workspace is pa_decode_workspace_bytes(num_decodes, ...) long
+ * (contents need no initialisation).  Two kernels are enqueued on `stream`:
+ * the mixed one and the log-sum-exp reduce of the decode partials.
+ */
+pa_status pa_mixed_attention(void* prefill_out, const void* prefill_q,
+                             const int32_t* query_start_loc, const int32_t* prefill_block_tables,
+                             const int32_t* prefill_seq_lens, int32_t num_chunks,
+                             int32_t total_q_tokens, int32_t max_q_len,
+                             int32_t prefill_max_blocks_per_seq, void* decode_out,
+                             const void* decode_q, const int32_t* decode_block_tables,
+                             const int32_t* decode_seq_lens, int32_t num_decodes,
+                             int32_t decode_max_blocks_per_seq, int32_t max_seq_len,
+                             const void* k_pool, const void* v_pool, float scale,
+                             int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, pa_dtype q_dtype, pa_dtype cache_dtype,
+                             float k_scale, float v_scale, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Index checks.  The calls above trust device-resident indices (a block id
  * outside the pool is undefined behaviour there, as checking would need a
  * synchronisation).  A caller that wants them checked enqueues these calls

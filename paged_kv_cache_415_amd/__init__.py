@@ -88,6 +88,9 @@ def _load() -> ctypes.CDLL:
         getattr(lib, name).restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, f32, vp]
+    lib.pa_mixed_attention.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
+                                       i32, vp, vp, f32, i32, i32, i32, i32, i32, i32, f32, f32, i32,
+                                       vp, sz, vp]
     lib.pa_check_block_tables.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_check_block_tables.restype = i32
     lib.pa_check_slots.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -99,7 +102,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_probe_read.argtypes = [vp, sz, vp, vp]
     lib.pa_probe_copy.argtypes = [vp, vp, sz, vp]
     for name in ("pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_copy_blocks", "pa_copy_blocks_partial",
-                 "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_probe_read",
+                 "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_mixed_attention",
+                 "pa_probe_read",
                  "pa_probe_copy"):
         getattr(lib, name).restype = i32
     return lib
@@ -483,6 +487,33 @@ def pa_prefill_chunk(out, q, query_start_loc, k_pool, v_pool, block_tables, seq_
                                  bs, num_seqs, t, int(max_q_len), hq, hkv, d,
                                  block_tables.shape[1], _dtype(q), _dtype(k_pool),
                                  float(k_scale), float(v_scale), _stream(stream)))
+
+
+def pa_mixed_attention(prefill_out, prefill_q, query_start_loc, prefill_block_tables, prefill_seq_lens,
+                       max_q_len: int, decode_out, decode_q, decode_block_tables, decode_seq_lens,
+                       max_seq_len: int, k_pool, v_pool, scale: float, k_scale: float = 1.0,
+                       v_scale: float = 1.0, partition_size: int = 0, workspace=None,
+                       stream=None) -> None:
+    """The prefill chunks and the decodes of one step in one launch (see pa.h);
+    the workspace is decode_workspace(decode_q, k_pool, max_seq_len, partition_size)."""
+    t, hq, d = prefill_q.shape
+    s, hq_d, d_d = decode_q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if (hq_d, d_d) != (hq, d) or _dtype(decode_q) != _dtype(prefill_q):
+        raise ValueError("prefill and decode queries differ in heads, head size or type")
+    if _dtype(v_pool) != _dtype(k_pool) or v_pool.shape[1:] != k_pool.shape[1:]:
+        raise ValueError("K and V pools must have one type and block shape")
+    for a in (query_start_loc, prefill_block_tables, prefill_seq_lens, decode_block_tables, decode_seq_lens):
+        if a.dtype != torch.int32:
+            raise TypeError("offsets, block tables and lengths must be int32")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_mixed_attention(
+        _ptr(prefill_out), _ptr(prefill_q), _ptr(query_start_loc), _ptr(prefill_block_tables),
+        _ptr(prefill_seq_lens), query_start_loc.shape[0] - 1, t, int(max_q_len),
+        prefill_block_tables.shape[1], _ptr(decode_out), _ptr(decode_q), _ptr(decode_block_tables),
+        _ptr(decode_seq_lens), s, decode_block_tables.shape[1], int(max_seq_len), _ptr(k_pool),
+        _ptr(v_pool), float(scale), bs, hq, hkv, d, _dtype(prefill_q), _dtype(k_pool), float(k_scale),
+        float(v_scale), int(partition_size), _ptr(workspace), wbytes, _stream(stream)))
 
 
 CHECK_FLAGS = {"block_id": 1, "length": 2, "slot": 4, "chunk": 8}

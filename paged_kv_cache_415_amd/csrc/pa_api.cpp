@@ -183,17 +183,19 @@ pa_status scratch_address(void** out) {
 
 enum class Stage { kBoth, kAttention, kReduce };
 
-pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
-                      const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
-                      float scale, int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
-                      int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
-                      pa_dtype v_cache_dtype, float k_scale, float v_scale,
-                      int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      void* stream, const float* k_scales = nullptr,
-                      const float* v_scales = nullptr, const void* new_k = nullptr,
-                      const void* new_v = nullptr, int64_t new_k_stride = 0,
-                      int64_t new_v_stride = 0, bool use_scratch = false) {
+// Checks a decode call and fills its kernel parameters; *work is false when
+// there is nothing to enqueue (no sequences).
+pa_status decode_setup(pa::DecodeParams* params, bool* work, void* out, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                       const int32_t* seq_lens, float scale, int32_t block_size, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_blocks_per_seq, int32_t max_seq_len, pa_dtype q_dtype,
+                       pa_dtype cache_dtype, pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       const float* k_scales, const float* v_scales, const void* new_k,
+                       const void* new_v, int64_t new_k_stride, int64_t new_v_stride,
+                       bool use_scratch) {
+  *work = false;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs < 0");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
@@ -225,7 +227,7 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   st = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                    max_seq_len, partition_size, &plan);
   if (st != PA_OK) return st;
-  if (num_seqs == 0) return ok();
+  if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
@@ -249,7 +251,8 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
     if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   }
 
-  pa::DecodeParams p{};
+  pa::DecodeParams& p = *params;
+  p = pa::DecodeParams{};
   p.out = out;
   p.q = q;
   p.k_pool = k_pool;
@@ -288,6 +291,31 @@ pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
   p.new_v = append ? new_v : nullptr;
   p.new_k_stride = new_k_stride;
   p.new_v_stride = new_v_stride;
+  *work = true;
+  return PA_OK;
+}
+
+pa_status decode_impl(Stage stage, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                      float scale, int32_t block_size, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_seq_len, pa_dtype q_dtype, pa_dtype cache_dtype,
+                      pa_dtype v_cache_dtype, float k_scale, float v_scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream, const float* k_scales = nullptr,
+                      const float* v_scales = nullptr, const void* new_k = nullptr,
+                      const void* new_v = nullptr, int64_t new_k_stride = 0,
+                      int64_t new_v_stride = 0, bool use_scratch = false) {
+  pa::DecodeParams p;
+  bool work = false;
+  const pa_status st = decode_setup(&p, &work, out, q, k_pool, v_pool, block_tables, seq_lens, scale,
+                                    block_size, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype,
+                                    v_cache_dtype, k_scale, v_scale, partition_size, workspace,
+                                    workspace_bytes, k_scales, v_scales, new_k, new_v, new_k_stride,
+                                    new_v_stride, use_scratch);
+  if (st != PA_OK) return st;
+  if (!work) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stage != Stage::kReduce) {
     hipError_t e = pa::launch_decode_attention(p, s);
@@ -673,13 +701,18 @@ PA_DECODE_APPEND(pa_decode_append, Stage::kBoth)
 PA_DECODE_APPEND(pa_decode_attention_append, Stage::kAttention)
 #undef PA_DECODE_APPEND
 
-pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
-                           const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                           const int32_t* seq_lens, float scale, int32_t block_size,
-                           int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
-                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t max_blocks_per_seq, pa_dtype q_dtype, pa_dtype cache_dtype,
-                           float k_scale, float v_scale, void* stream) {
+namespace {
+
+// Checks a prefill call and fills its kernel parameters; *work is false when
+// there is nothing to enqueue (no sequences or no query tokens).
+pa_status prefill_setup(pa::PrefillParams* params, bool* work, void* out, const void* q,
+                        const int32_t* query_start_loc, const void* k_pool, const void* v_pool,
+                        const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                        int32_t block_size, int32_t num_seqs, int32_t total_q_tokens,
+                        int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_blocks_per_seq, pa_dtype q_dtype,
+                        pa_dtype cache_dtype, float k_scale, float v_scale) {
+  *work = false;
   if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0)
     return fail(PA_ERR_INVALID_ARG, "negative size");
   if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs > 65535");
@@ -699,7 +732,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
     return fail(PA_ERR_UNSUPPORTED, "block table too wide");
   if (pa::prefill_smem_bytes(head_dim) > 160 * 1024)
     return fail(PA_ERR_UNSUPPORTED, "K/V tile stages do not fit in LDS");
-  if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return ok();
+  if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !query_start_loc || !k_pool || !v_pool || !block_tables || !seq_lens)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
@@ -707,7 +740,8 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
     return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
   const int qpos = 128 / group;
   if ((max_q_len + qpos - 1) / qpos > 0x7FFFFFFF / 2) return fail(PA_ERR_UNSUPPORTED, "grid too large");
-  pa::PrefillParams p{};
+  pa::PrefillParams& p = *params;
+  p = pa::PrefillParams{};
   p.out = out;
   p.q = q;
   p.query_start_loc = query_start_loc;
@@ -728,7 +762,73 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
   p.max_blocks = max_blocks_per_seq;
   p.q_dtype = q_dtype;
   p.cache_dtype = cache_dtype;
+  *work = true;
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_loc,
+                           const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                           const int32_t* seq_lens, float scale, int32_t block_size,
+                           int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           float k_scale, float v_scale, void* stream) {
+  pa::PrefillParams p;
+  bool work = false;
+  const pa_status st = prefill_setup(&p, &work, out, q, query_start_loc, k_pool, v_pool, block_tables,
+                                     seq_lens, scale, block_size, num_seqs, total_q_tokens,
+                                     max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                     max_blocks_per_seq, q_dtype, cache_dtype, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (!work) return ok();
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+pa_status pa_mixed_attention(void* prefill_out, const void* prefill_q,
+                             const int32_t* query_start_loc, const int32_t* prefill_block_tables,
+                             const int32_t* prefill_seq_lens, int32_t num_chunks,
+                             int32_t total_q_tokens, int32_t max_q_len,
+                             int32_t prefill_max_blocks_per_seq, void* decode_out,
+                             const void* decode_q, const int32_t* decode_block_tables,
+                             const int32_t* decode_seq_lens, int32_t num_decodes,
+                             int32_t decode_max_blocks_per_seq, int32_t max_seq_len,
+                             const void* k_pool, const void* v_pool, float scale,
+                             int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, pa_dtype q_dtype, pa_dtype cache_dtype,
+                             float k_scale, float v_scale, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (cache_dtype != q_dtype || (q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16))
+    return fail(PA_ERR_UNSUPPORTED,
+                "the mixed-step launch supports bf16/f16 queries over a cache of the same type");
+  pa::PrefillParams pf{};
+  bool pf_work = false;
+  pa_status st = prefill_setup(&pf, &pf_work, prefill_out, prefill_q, query_start_loc, k_pool,
+                               v_pool, prefill_block_tables, prefill_seq_lens, scale, block_size,
+                               num_chunks, total_q_tokens, max_q_len, num_q_heads, num_kv_heads,
+                               head_dim, prefill_max_blocks_per_seq, q_dtype, cache_dtype, k_scale,
+                               v_scale);
+  if (st != PA_OK) return st;
+  pa::DecodeParams d{};
+  bool d_work = false;
+  st = decode_setup(&d, &d_work, decode_out, decode_q, k_pool, v_pool, decode_block_tables,
+                    decode_seq_lens, scale, block_size, num_decodes, num_q_heads, num_kv_heads,
+                    head_dim, decode_max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype,
+                    cache_dtype, k_scale, v_scale, partition_size, workspace, workspace_bytes,
+                    nullptr, nullptr, nullptr, nullptr, 0, 0, false);
+  if (st != PA_OK) return st;
+  if (!pf_work) pf.num_seqs = 0;   // no query tokens: no prefill tiles
+  if (!d_work) d.num_seqs = 0;
+  if (!pf_work && !d_work) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pa::launch_mixed(pf, d, s);
+  if (e != hipSuccess) return hip_status(e, "mixed-step launch");
+  if (d_work) {
+    e = pa::launch_decode_reduce(d, s);
+    if (e != hipSuccess) return hip_status(e, "decode reduce launch");
+  }
+  return ok();
 }
 
 pa_status pa_check_block_tables(const int32_t* block_tables, const int32_t* seq_lens,

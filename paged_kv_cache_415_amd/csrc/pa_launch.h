@@ -170,6 +170,14 @@ hipError_t launch_swap_blocks(const SwapParams& p, hipStream_t stream);
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// One launch over a mixed step's prefill query tiles and decode work (16-bit
+// caches of the query type; same pools, head shape and block size in both).
+// The decode partials it leaves are merged by launch_decode_reduce(d).
+hipError_t launch_mixed(const PrefillParams& pf, const DecodeParams& d, hipStream_t stream);
+// Compute units of the current device.
+int cu_count();
+// Upper bound of the decode waves that can have work, from host-known sizes.
+int64_t wave_work_bound(const DecodeParams& p);
 // LDS bytes the prefill kernel needs (two stages of a K and a V tile).
 size_t prefill_smem_bytes(int head_dim);
 hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, hipStream_t stream);

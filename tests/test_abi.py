@@ -104,6 +104,34 @@ def test_decode_batch_limits(lib):
     assert _decode(lib, S=8000, hkv=64, hq=64, mb=1 << 16, msl=1 << 20, part=-1) == UNSUPPORTED
 
 
+def _mixed(lib, **kw):
+    a = dict(nc=2, tq=64, mq=32, S=3, qdt=BF16, cdt=BF16, part=0, hq=8, hkv=2, d=128, bs=16,
+             ptr=None, ws=None, wsb=0)
+    a.update(kw)
+    p = a["ptr"]
+    return lib.pa_mixed_attention(p, p, p, p, p, a["nc"], a["tq"], a["mq"], 8, p, p, p, p, a["S"], 8, 128,
+                                  p, p, 0.1, a["bs"], a["hq"], a["hkv"], a["d"], a["qdt"], a["cdt"], 1.0,
+                                  1.0, a["part"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cdt=FP8), UNSUPPORTED),                 # the mixed launch takes 16-bit caches only
+    (dict(qdt=F32, cdt=F32), UNSUPPORTED),
+    (dict(hq=12, hkv=4), UNSUPPORTED),            # prefill needs a power-of-two group
+    (dict(d=96), UNSUPPORTED),
+    (dict(part=48), INVALID),
+    (dict(nc=-1), INVALID),
+    (dict(), INVALID),                            # null pointers
+])
+def test_mixed_rejects_before_launch(lib, kw, code):
+    assert _mixed(lib, **kw) == code
+    assert lib.pa_last_error() != b""
+
+
+def test_mixed_empty_step_is_ok(lib):
+    assert _mixed(lib, nc=0, tq=0, mq=0, S=0) == OK
+
+
 def test_partition_planning(pa):
     assert pa.pa_decode_partition_size(256, 8, 16, 8192, 512) == 512
     assert pa.pa_decode_partition_size(256, 8, 16, 8192, 48) < 0

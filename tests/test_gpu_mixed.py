@@ -1,0 +1,197 @@
+"""GPU parity of pa_mixed_attention, the mixed step's prefill chunks and decodes
+in one launch: every output against the oracle (max-abs 2e-2), the prefill
+outputs bit for bit against pa_prefill_chunk, and HIP-graph replays bit for
+bit against the eager call."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_cases import TOL, lib, max_abs, up, up_int
+
+pytestmark = pytest.mark.gpu
+
+
+class MixedRun:
+    """Device copies of a MixedCase after its copy-on-write and scatter."""
+
+    def __init__(self, case, decode_lens=None):
+        pa = lib()
+        self.case = case
+        s = case.spec
+        dt = s.dtype
+        self.kp, self.vp = up(case.k_pool, dt), up(case.v_pool, dt)
+        pa.pa_copy_blocks(self.kp, self.vp, up_int(case.cow_pairs))
+        pa.pa_reshape_and_cache(up(case.new_k, dt), up(case.new_v, dt), self.kp, self.vp,
+                                up_int(case.slot_mapping))
+        self.qc, self.qd = up(case.q_chunk, dt), up(case.q_decode, dt)
+        self.qsl = up_int(case.query_start_loc)
+        self.ptab, self.plen = up_int(case.prefill_tables), up_int(case.prefill_lens)
+        self.dlens = case.decode_lens if decode_lens is None else np.asarray(decode_lens, np.int32)
+        self.dtab, self.dlen = up_int(case.decode_tables), up_int(self.dlens)
+        self.max_q = int(np.diff(case.query_start_loc).max()) if len(case.query_start_loc) > 1 else 0
+        self.max_len = max(int(self.dlens.max()), 1) if len(self.dlens) else 1
+
+    def fused(self, partition_size=0, out=None):
+        pa = lib()
+        s = self.case.spec
+        out_c, out_d = out if out is not None else (torch.empty_like(self.qc), torch.empty_like(self.qd))
+        ws = pa.decode_workspace(self.qd, self.kp, self.max_len, partition_size)
+        pa.pa_mixed_attention(out_c, self.qc, self.qsl, self.ptab, self.plen, self.max_q, out_d, self.qd,
+                              self.dtab, self.dlen, self.max_len, self.kp, self.vp, s.scale,
+                              partition_size=partition_size, workspace=ws)
+        return out_c, out_d
+
+    def separate(self):
+        pa = lib()
+        s = self.case.spec
+        out_c, out_d = torch.empty_like(self.qc), torch.empty_like(self.qd)
+        if self.max_q > 0:
+            pa.pa_prefill_chunk(out_c, self.qc, self.qsl, self.kp, self.vp, self.ptab, self.plen, s.scale,
+                                self.max_q)
+        ws = pa.decode_workspace(self.qd, self.kp, self.max_len)
+        pa.pa_decode(out_d, self.qd, self.kp, self.vp, self.dtab, self.dlen, s.scale,
+                     max_seq_len=self.max_len, workspace=ws)
+        return out_c, out_d
+
+    def oracle(self):
+        c, s = self.case, self.case.spec
+        okp, ovp = oracle.copy_blocks(c.k_pool, c.v_pool, c.cow_pairs)
+        okp, ovp = oracle.reshape_and_cache(okp, ovp, s.dtype, c.new_k, c.new_v, s.dtype, c.slot_mapping,
+                                            s.block_size)
+        ref_c = oracle.prefill_chunk_attention(c.q_chunk, s.dtype, c.query_start_loc, okp, ovp, s.dtype,
+                                               c.prefill_tables, c.prefill_lens, s.scale, s.block_size,
+                                               s.num_kv_heads)
+        ref_d = oracle.decode_attention(c.q_decode, s.dtype, okp, ovp, s.dtype, c.decode_tables,
+                                        self.dlens, s.scale, s.block_size, s.num_kv_heads)
+        return ref_c, ref_d
+
+
+def _bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+SMALL = [
+    # (spec overrides, forks, prefix, chunk, decode lengths)
+    ({}, 4, 96, 40, [33, 64, 65, 300, 1000]),
+    ({}, 3, 64, 70, [1, 2, 31, 32, 4096, 777, 129, 64, 5]),        # ragged chunk tiles, 1-token decodes
+    ({"dtype": "f16"}, 2, 128, 33, [100, 2000, 31]),
+    ({"head_dim": 64, "num_q_heads": 8, "num_kv_heads": 2}, 3, 40, 55, [7, 500, 1500, 64]),
+    ({"block_size": 16, "num_q_heads": 16, "num_kv_heads": 1}, 2, 48, 90, [300, 17, 1024]),
+    ({"block_size": 8, "num_q_heads": 8, "num_kv_heads": 8}, 2, 24, 20, [9, 250, 64]),
+    ({"block_size": 64, "num_q_heads": 32, "num_kv_heads": 2}, 2, 128, 64, [65, 1, 1200]),
+]
+
+
+@pytest.mark.parametrize("over,forks,prefix,chunk,dlens", SMALL)
+@pytest.mark.parametrize("partition", [0, 64, -1])
+def test_fused_step_matches_oracle(over, forks, prefix, chunk, dlens, partition):
+    spec = dataclasses.replace(W.MIXED_SPEC, **over)
+    case = W.make_mixed_case(spec, num_forks=forks, prefix_len=prefix, chunk_len=chunk, decode_lens=dlens)
+    run = MixedRun(case)
+    out_c, out_d = run.fused(partition)
+    sep_c, _ = run.separate()
+    torch.cuda.synchronize()
+    ref_c, ref_d = run.oracle()
+    assert max_abs(out_c, ref_c) <= TOL[spec.dtype]
+    assert max_abs(out_d, ref_d) <= TOL[spec.dtype]
+    assert _bits_equal(out_c, sep_c), "prefill part differs from pa_prefill_chunk"
+
+
+def test_fused_step_empty_decode_sequences():
+    """Decode sequences of length 0 get zero outputs, beside live ones."""
+    case = W.make_mixed_case(num_forks=2, prefix_len=64, chunk_len=50, decode_lens=[40, 300, 90, 1000, 5])
+    run = MixedRun(case, decode_lens=[40, 0, 90, 0, 5])
+    out_c, out_d = run.fused()
+    torch.cuda.synchronize()
+    ref_c, ref_d = run.oracle()
+    assert not ref_d[1].any() and not ref_d[3].any()
+    assert max_abs(out_c, ref_c) <= TOL["bf16"]
+    assert max_abs(out_d, ref_d) <= TOL["bf16"]
+
+
+def test_fused_step_without_prefill_or_decode():
+    """One part empty: the launch holds only the other kind of workgroup."""
+    case = W.make_mixed_case(num_forks=2, prefix_len=64, chunk_len=48, decode_lens=[100, 2000, 33])
+    run = MixedRun(case)
+    ref_c, ref_d = run.oracle()
+    pa = lib()
+    s = case.spec
+    # decodes only: no query tokens
+    out_d = torch.empty_like(run.qd)
+    empty_q = run.qc[:0]
+    ws = pa.decode_workspace(run.qd, run.kp, run.max_len)
+    pa.pa_mixed_attention(torch.empty_like(empty_q), empty_q, up_int(np.zeros(1, np.int32)), run.ptab[:0],
+                          run.plen[:0], 0, out_d, run.qd, run.dtab, run.dlen, run.max_len, run.kp, run.vp,
+                          s.scale, workspace=ws)
+    # prefill chunks only: no decode sequences
+    out_c = torch.empty_like(run.qc)
+    pa.pa_mixed_attention(out_c, run.qc, run.qsl, run.ptab, run.plen, run.max_q, run.qd[:0], run.qd[:0],
+                          run.dtab[:0], run.dlen[:0], 1, run.kp, run.vp, s.scale)
+    torch.cuda.synchronize()
+    assert max_abs(out_d, ref_d) <= TOL["bf16"]
+    assert max_abs(out_c, ref_c) <= TOL["bf16"]
+
+
+def test_fused_full_size_step():
+    """The full mixed workload (16 chunks of 512 tokens over a 1,536-token
+    context, 112 decodes): every decode output against the oracle, every
+    prefill output bit for bit against pa_prefill_chunk (which the prefill
+    tests compare with the oracle at this size), and against the oracle on
+    the first and last chunk."""
+    case = W.make_mixed_case()
+    print(f"[fused] forks={len(case.prefill_lens)} decode={len(case.decode_lens)}", flush=True)
+    run = MixedRun(case)
+    out_c, out_d = run.fused()
+    sep_c, sep_d = run.separate()
+    torch.cuda.synchronize()
+    assert _bits_equal(out_c, sep_c), "prefill part differs from pa_prefill_chunk"
+    s = case.spec
+    okp, ovp = oracle.copy_blocks(case.k_pool, case.v_pool, case.cow_pairs)
+    okp, ovp = oracle.reshape_and_cache(okp, ovp, s.dtype, case.new_k, case.new_v, s.dtype,
+                                        case.slot_mapping, s.block_size)
+    ref_d = oracle.decode_attention(case.q_decode, s.dtype, okp, ovp, s.dtype, case.decode_tables,
+                                    case.decode_lens, s.scale, s.block_size, s.num_kv_heads)
+    err_d = max_abs(out_d, ref_d)
+    print(f"[fused] decode max-abs {err_d:.3e}", flush=True)
+    assert err_d <= TOL["bf16"]
+    qsl = case.query_start_loc
+    for f in (0, len(qsl) - 2):
+        sub_qsl = np.array([0, qsl[f + 1] - qsl[f]], np.int32)
+        ref = oracle.prefill_chunk_attention(case.q_chunk[qsl[f]:qsl[f + 1]], s.dtype, sub_qsl, okp, ovp,
+                                             s.dtype, case.prefill_tables[f:f + 1], case.prefill_lens[f:f + 1],
+                                             s.scale, s.block_size, s.num_kv_heads)
+        assert max_abs(out_c[qsl[f]:qsl[f + 1]], ref) <= TOL["bf16"]
+
+
+def test_fused_step_graph_replays_equal_eager():
+    """The call captured in a HIP graph: each replay (with eager work and a
+    synchronisation between replays) gives the eager call's bits."""
+    case = W.make_mixed_case(num_forks=3, prefix_len=96, chunk_len=70, decode_lens=[40, 300, 2000, 65, 1])
+    run = MixedRun(case)
+    eager_c, eager_d = run.fused()
+    torch.cuda.synchronize()
+    out_c, out_d = torch.empty_like(run.qc), torch.empty_like(run.qd)
+    pa = lib()
+    s = case.spec
+    ws = pa.decode_workspace(run.qd, run.kp, run.max_len)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.pa_mixed_attention(out_c, run.qc, run.qsl, run.ptab, run.plen, run.max_q, out_d, run.qd,
+                                  run.dtab, run.dlen, run.max_len, run.kp, run.vp, s.scale, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        out_c.fill_(0)
+        out_d.fill_(0)
+        ws.fill_(0xFF)          # stale workspace contents must not matter
+        g.replay()
+        torch.cuda.synchronize()
+        assert _bits_equal(out_c, eager_c), f"prefill, replay {rep}"
+        assert _bits_equal(out_d, eager_d), f"decode, replay {rep}"
