@@ -452,7 +452,8 @@ def run_mixed_bench(args, dev):
             "decode_gbps": round(eff / (fused_ms * 1e-3) / 1e9, 1),
             "mfma_frac": round(flops / (fused_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "hbm_frac": round(eff / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "separate_launches_ms": round(sep_ms, 5)},
+            "separate_launches_ms": round(sep_ms, 5),
+            "traffic": decode_traffic_bytes(s.name, "mixed"), "traffic_unit": "bytes per launch of mixed_kernel"},
         "separate_launches_ms_per_step": round(sep_ms_step, 5),
         "prefill_flops": flops, "effective_kv_bytes_per_step": eff,
         "prefill_tflops": round(tflops, 2), "decode_gbps": round(dec_gbps, 1),
