@@ -486,11 +486,12 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
  * and errors of those two calls.  Either part may be empty (num_chunks or
  * total_q_tokens 0; num_decodes 0).
  *
- * Supported: bf16 or f16 queries over a cache of the same type (cache_dtype
- * == q_dtype; other pairs return PA_ERR_UNSUPPORTED).  The prefill outputs
- * equal pa_prefill_chunk's bit for bit; the decode outputs may differ from
- * a pa_decode call by rounding, since the work is cut for this launch's
- * waves.  The workspace is pa_decode_workspace_bytes(num_decodes, ...) long
+ * Supported: bf16 or f16 queries over a cache of the same type, or over an
+ * fp8 E4M3 cache with per-tensor k_scale / v_scale as in pa_decode and
+ * pa_prefill_chunk ([ybb] §6.2); other pairs return PA_ERR_UNSUPPORTED.  The
+ * prefill outputs equal pa_prefill_chunk's bit for bit; the decode outputs
+ * may differ from a pa_decode call by rounding, since the work is cut for
+ * this launch's waves.  The workspace is pa_decode_workspace_bytes(num_decodes, ...) long
  * (contents need no initialisation).  Two kernels are enqueued on `stream`:
  * the mixed one and the log-sum-exp reduce of the decode partials.
  */

@@ -36,11 +36,16 @@ constexpr int kMixedWaves = kPThreads / 64;   // waves per workgroup, both kinds
 // Rates of the two kinds of workgroup running side by side on MI355X,
 // measured on the mixed workload (16 chunks of 512 tokens over 1,536-token
 // contexts beside 112 decodes of 256-4,096 tokens, 32/8 heads, head size
-// 128, bf16): a decode workgroup streams about 24.5 KB of K/V per
-// microsecond, a prefill slot does about 1.34 Mflop per microsecond.  Only
-// their ratio matters; it sets how many slots the decode part takes.
-constexpr double kDecodeWgBytesPerUs = 24.5e3;
-constexpr double kPrefillSlotFlopsPerUs = 1.34e6;
+// 128): with a bf16 cache a decode workgroup streams about 24.5 KB of K/V
+// per microsecond and a prefill slot does about 1.34 Mflop per microsecond.
+// [1] is the fp8 E4M3 cache: the decode rate scaled by the fp8 decode
+// kernel's byte rate against the bf16 one, the prefill rate by the fp8
+// prefill tiles' (codes decoded into LDS through registers); on that
+// workload over an fp8 cache any split from 96 to 256 decode workgroups
+// lands within 2 % of the best.  Only the ratio of a pair matters; it sets
+// how many slots the decode part takes.
+constexpr double kDecodeWgBytesPerUs[2] = {24.5e3, 21.2e3};
+constexpr double kPrefillSlotFlopsPerUs[2] = {1.34e6, 1.30e6};
 
 // Sum over the workgroup (every thread gets it); ends with a barrier.
 __device__ __forceinline__ double wg_sum(double v) {
@@ -68,6 +73,7 @@ struct MixedPick {
   const int* prefill_lens;
   int num_chunks, cap;          // cap: longest context a prefill table row holds
   int num_q_heads, num_kv_heads, head_dim, elem_bytes, slots;
+  double decode_rate, prefill_rate;   // bytes per µs per decode workgroup, flops per µs per prefill slot
   __device__ int operator()(const int* lens, int S, int nwg) const {
     double units = 0.0, pairs = 0.0;
     for (int s = threadIdx.x; s < S; s += kPThreads) units += (double)((lens[s] + 31) / 32);
@@ -81,46 +87,54 @@ struct MixedPick {
     if (pairs <= 0.0) return nwg;                  // no prefill work: every slot decodes
     const double bytes = units * 32.0 * num_kv_heads * head_dim * 2.0 * elem_bytes;
     const double flops = 4.0 * head_dim * num_q_heads * pairs;
-    const double k = (bytes / kDecodeWgBytesPerUs) / (flops / kPrefillSlotFlopsPerUs);
+    const double k = (bytes / decode_rate) / (flops / prefill_rate);
     int n = (int)fmin((double)nwg, ceil((double)slots * k / (1.0 + k)));
     n = (n + kXcds - 1) / kXcds * kXcds;           // whole rounds over the XCDs
     return n < kXcds ? kXcds : (n > nwg ? nwg : n);
   }
 };
 
-template <typename T, int D, int BS>
+// The decode program of a cache format: the query type (KV8 false) or fp8
+// E4M3 codes for K and V.
+template <typename T, int D, int BS, bool KV8>
+using MixedSeg = MfmaDecode<T, KV8 ? kFmtFp8 : kFmtQ, KV8 ? kFmtFp8 : kFmtQ, D, BS>;
+
+template <typename T, int D, int BS, bool KV8>
 __global__ __launch_bounds__(kPThreads) void mixed_kernel(PrefillParams pf, DecodeParams d, int npf, int ndec,
                                                           int nq, int slots) {
   const int b = blockIdx.x;
   if (b < ndec) {
     const MixedPick pick{pf.query_start_loc, pf.seq_lens, npf > 0 ? pf.num_seqs : 0, pf.max_blocks * BS,
-                         d.num_q_heads, d.num_kv_heads, D, (int)sizeof(T), slots};
-    decode_share<MfmaDecode<T, kFmtQ, kFmtQ, D, BS>, T, kMixedWaves>(d, b, ndec, pick);
+                         d.num_q_heads, d.num_kv_heads, D, KV8 ? 1 : (int)sizeof(T), slots,
+                         kDecodeWgBytesPerUs[KV8], kPrefillSlotFlopsPerUs[KV8]};
+    decode_share<MixedSeg<T, D, BS, KV8>, T, kMixedWaves>(d, b, ndec, pick);
     return;
   }
   // ndec is a multiple of the XCD count, so tile lin runs on XCD lin % kXcds
   // as in a prefill launch
   int seq, kvh, qtile;
   prefill_work(b - ndec, npf, nq, pf.num_kv_heads, seq, kvh, qtile);
-  prefill_tile<T, D, BS, false>(pf, seq, kvh, qtile);
+  prefill_tile<T, D, BS, KV8>(pf, seq, kvh, qtile);
 }
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, bool KV8>
 hipError_t launch_mixed_t(const PrefillParams& pf, const DecodeParams& d0, hipStream_t stream) {
-  auto kernel = mixed_kernel<T, D, BS>;
+  auto kernel = mixed_kernel<T, D, BS, KV8>;
   DecodeParams d = d0;
   const int qpos = pf.num_seqs > 0 ? kRowsPerWG / pf.group : 1;   // chunk positions per tile
   const int nq = (pf.num_seqs > 0 && pf.max_q_len > 0) ? (pf.max_q_len + qpos - 1) / qpos : 0;
   const int64_t npf = (int64_t)nq * pf.num_kv_heads * pf.num_seqs;
-  // LDS: the prefill tile's two K/V stages; a decode workgroup's plan and
-  // merge slots (up to three per wave) fit in the same bytes
+  // LDS: the prefill tile's two K/V stages; a decode workgroup's plan,
+  // merge slots (up to three per wave) and, for 8-bit K, each wave's 4 KB K
+  // staging fit in the same bytes
   const size_t stages = prefill_smem_bytes(D);
   size_t lds = npf > 0 ? stages : 0;
   d.local_slots = 0;
   if (d.num_seqs > 0) {
     const size_t plan = (size_t)((2 * d.num_seqs + 1 + 3) & ~3) * sizeof(int);
     const size_t per_slot = (size_t)d.group * D * sizeof(float) + 33 * sizeof(float);
-    const size_t room = stages > plan + 64 ? stages : plan + 64;
+    const size_t kstage = MixedSeg<T, D, BS, KV8>::kStageK ? (size_t)kMixedWaves * 4096 : 0;
+    const size_t room = stages > plan + 64 + kstage ? stages - kstage : plan + 64;
     int slots = 0;
     if (d.mode != kSplitNone && plan + 64 < room)
       slots = (int)std::min<size_t>((size_t)3 * kMixedWaves, (room - plan - 64) / per_slot);
@@ -128,7 +142,7 @@ hipError_t launch_mixed_t(const PrefillParams& pf, const DecodeParams& d0, hipSt
     const size_t merge_end = plan + (size_t)((slots + 3) & ~3) * sizeof(int) + (size_t)slots * 32 * sizeof(float) +
                              (size_t)slots * d.group * D * sizeof(float);
     d.kstage_off = (int)merge_end;
-    lds = lds > merge_end ? lds : merge_end;
+    lds = lds > merge_end + kstage ? lds : merge_end + kstage;
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), kPThreads,
@@ -154,21 +168,25 @@ hipError_t launch_mixed_t(const PrefillParams& pf, const DecodeParams& d0, hipSt
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool KV8>
 hipError_t launch_mixed_bs(const PrefillParams& pf, const DecodeParams& d, int block_size, hipStream_t s) {
   switch (block_size) {
-    case 8: return launch_mixed_t<T, D, 8>(pf, d, s);
-    case 16: return launch_mixed_t<T, D, 16>(pf, d, s);
-    case 32: return launch_mixed_t<T, D, 32>(pf, d, s);
-    default: return launch_mixed_t<T, D, 64>(pf, d, s);
+    case 8: return launch_mixed_t<T, D, 8, KV8>(pf, d, s);
+    case 16: return launch_mixed_t<T, D, 16, KV8>(pf, d, s);
+    case 32: return launch_mixed_t<T, D, 32, KV8>(pf, d, s);
+    default: return launch_mixed_t<T, D, 64, KV8>(pf, d, s);
   }
 }
 
 template <typename T>
-hipError_t launch_mixed_d(const PrefillParams& pf, const DecodeParams& d, int head_dim, int block_size,
+hipError_t launch_mixed_d(const PrefillParams& pf, const DecodeParams& d, int head_dim, int block_size, bool kv8,
                           hipStream_t s) {
-  if (head_dim == 128) return launch_mixed_bs<T, 128>(pf, d, block_size, s);
-  return launch_mixed_bs<T, 64>(pf, d, block_size, s);
+  if (kv8) {
+    if (head_dim == 128) return launch_mixed_bs<T, 128, true>(pf, d, block_size, s);
+    return launch_mixed_bs<T, 64, true>(pf, d, block_size, s);
+  }
+  if (head_dim == 128) return launch_mixed_bs<T, 128, false>(pf, d, block_size, s);
+  return launch_mixed_bs<T, 64, false>(pf, d, block_size, s);
 }
 
 }  // namespace
@@ -176,19 +194,21 @@ hipError_t launch_mixed_d(const PrefillParams& pf, const DecodeParams& d, int he
 hipError_t launch_mixed(const PrefillParams& pf, const DecodeParams& d, hipStream_t stream) {
   const bool has_pf = pf.num_seqs > 0, has_d = d.num_seqs > 0;
   if (!has_pf && !has_d) return hipSuccess;
-  // 16-bit caches of the query type; with both parts present they share the
-  // pools, the head shape and the block size
-  if (has_pf && pf.cache_dtype != pf.q_dtype) return hipErrorInvalidValue;
-  if (has_d && (d.cache_dtype != d.q_dtype || d.v_cache_dtype != d.q_dtype)) return hipErrorInvalidValue;
+  // K and V pools of the query type or both fp8; with both parts present
+  // they share the pools, the head shape and the block size
+  if (has_pf && pf.cache_dtype != pf.q_dtype && pf.cache_dtype != kFP8) return hipErrorInvalidValue;
+  if (has_d && (d.v_cache_dtype != d.cache_dtype || (d.cache_dtype != d.q_dtype && d.cache_dtype != kFP8)))
+    return hipErrorInvalidValue;
   if (has_pf && has_d &&
       (pf.head_dim != d.head_dim || pf.block_size != d.block_size || pf.num_kv_heads != d.num_kv_heads ||
-       pf.group != d.group || pf.q_dtype != d.q_dtype))
+       pf.group != d.group || pf.q_dtype != d.q_dtype || pf.cache_dtype != d.cache_dtype))
     return hipErrorInvalidValue;
   const int q_dtype = has_d ? d.q_dtype : pf.q_dtype;
   const int head_dim = has_d ? d.head_dim : pf.head_dim;
   const int block_size = has_d ? d.block_size : pf.block_size;
-  if (q_dtype == kBF16) return launch_mixed_d<__bf16>(pf, d, head_dim, block_size, stream);
-  if (q_dtype == kF16) return launch_mixed_d<_Float16>(pf, d, head_dim, block_size, stream);
+  const bool kv8 = (has_d ? d.cache_dtype : pf.cache_dtype) == kFP8;
+  if (q_dtype == kBF16) return launch_mixed_d<__bf16>(pf, d, head_dim, block_size, kv8, stream);
+  if (q_dtype == kF16) return launch_mixed_d<_Float16>(pf, d, head_dim, block_size, kv8, stream);
   return hipErrorInvalidValue;
 }
 

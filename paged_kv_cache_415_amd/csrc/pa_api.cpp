@@ -799,9 +799,10 @@ pa_status pa_mixed_attention(void* prefill_out, const void* prefill_q,
                              int32_t head_dim, pa_dtype q_dtype, pa_dtype cache_dtype,
                              float k_scale, float v_scale, int32_t partition_size,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (cache_dtype != q_dtype || (q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16))
+  if ((q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16) ||
+      (cache_dtype != q_dtype && cache_dtype != PA_DTYPE_FP8_E4M3))
     return fail(PA_ERR_UNSUPPORTED,
-                "the mixed-step launch supports bf16/f16 queries over a cache of the same type");
+                "the mixed-step launch supports bf16/f16 queries over a cache of the same type or fp8");
   pa::PrefillParams pf{};
   bool pf_work = false;
   pa_status st = prefill_setup(&pf, &pf_work, prefill_out, prefill_q, query_start_loc, k_pool,

@@ -115,8 +115,9 @@ def _mixed(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(cdt=FP8), UNSUPPORTED),                 # the mixed launch takes 16-bit caches only
+    (dict(cdt=4), UNSUPPORTED),                   # int8 caches: not in the mixed launch
     (dict(qdt=F32, cdt=F32), UNSUPPORTED),
+    (dict(cdt=FP8), INVALID),                     # fp8 is taken; the null pointers are not
     (dict(hq=12, hkv=4), UNSUPPORTED),            # prefill needs a power-of-two group
     (dict(d=96), UNSUPPORTED),
     (dict(part=48), INVALID),

@@ -1,7 +1,7 @@
 """GPU parity of pa_mixed_attention, the mixed step's prefill chunks and decodes
-in one launch: every output against the oracle (max-abs 2e-2), the prefill
-outputs bit for bit against pa_prefill_chunk, and HIP-graph replays bit for
-bit against the eager call."""
+in one launch (16-bit and fp8 E4M3 caches): every output against the oracle
+(max-abs 2e-2), the prefill outputs bit for bit against pa_prefill_chunk, and
+HIP-graph replays bit for bit against the eager call."""
 
 import dataclasses
 
@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_cases import TOL, lib, max_abs, up, up_int
+from gpu_cases import TOL, lib, max_abs, random_chunks, up, up_int
 
 pytestmark = pytest.mark.gpu
 
@@ -195,3 +195,73 @@ def test_fused_step_graph_replays_equal_eager():
         torch.cuda.synchronize()
         assert _bits_equal(out_c, eager_c), f"prefill, replay {rep}"
         assert _bits_equal(out_d, eager_d), f"decode, replay {rep}"
+
+
+def _fp8_step(rng, pchunks, pctx, dctx, hq, hkv, d, bs, q_dt, partition):
+    """Prefill chunks and decodes over one fp8 pool with per-tensor scales: a
+    decode is a one-token chunk at the end of its context, so one pool from
+    random_chunks holds both; the sequences are then split into the two parts."""
+    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks(rng, list(pchunks) + [1] * len(dctx),
+                                                          list(pctx) + list(dctx), hq, hkv, d, bs, "fp8_e4m3",
+                                                          q_dtype=q_dt)
+    P = len(pchunks)
+    qsl_p, q_p, tab_p, len_p = qsl[:P + 1], q[:qsl[P]], tables[:P], lens[:P]
+    q_d, tab_d, len_d = q[qsl[P]:], tables[P:], lens[P:]
+    scale = 1.0 / np.sqrt(d)
+    pa = lib()
+    gk, gv = up(kp, "fp8_e4m3"), up(vp, "fp8_e4m3")
+    gq_p, gq_d = up(q_p, q_dt), up(q_d, q_dt)
+    out_p, out_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
+    max_len = int(len_d.max())
+    ws = pa.decode_workspace(gq_d, gk, max_len, partition)
+    pa.pa_mixed_attention(out_p, gq_p, up_int(qsl_p), up_int(tab_p), up_int(len_p), int(max(pchunks)), out_d,
+                          gq_d, up_int(tab_d), up_int(len_d), max_len, gk, gv, scale, k_scale=ks, v_scale=vs,
+                          partition_size=partition, workspace=ws)
+    sep_p = torch.empty_like(gq_p)
+    pa.pa_prefill_chunk(sep_p, gq_p, up_int(qsl_p), gk, gv, up_int(tab_p), up_int(len_p), scale,
+                        int(max(pchunks)), k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ref_p = oracle.prefill_chunk_attention(q_p, q_dt, qsl_p, kp, vp, "fp8_e4m3", tab_p, len_p, scale, bs, hkv,
+                                           k_scale=ks, v_scale=vs)
+    ref_d = oracle.decode_attention(q_d, q_dt, kp, vp, "fp8_e4m3", tab_d, len_d, scale, bs, hkv,
+                                    k_scale=ks, v_scale=vs)
+    return out_p, out_d, sep_p, ref_p, ref_d
+
+
+FP8_SHAPES = [
+    # (Hq, Hkv, D, bs, query type)
+    (64, 8, 128, 16, "bf16"),
+    (32, 8, 128, 32, "bf16"),
+    (8, 2, 64, 16, "f16"),
+    (16, 1, 128, 64, "bf16"),
+    (4, 4, 64, 8, "f16"),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,q_dt", FP8_SHAPES)
+@pytest.mark.parametrize("partition", [0, 512, -1])
+def test_fused_fp8_step_matches_oracle(hq, hkv, d, bs, q_dt, partition):
+    """fp8 E4M3 K/V with per-tensor scales ([ybb] 6.2): ragged chunks and decodes
+    of 1 to 2,049 tokens in one launch."""
+    rng = np.random.default_rng(hq * 7 + d + bs + (partition % 97))
+    out_p, out_d, sep_p, ref_p, ref_d = _fp8_step(rng, [40, 70, 17], [300, 170, 17],
+                                                  [1, 33, 500, 1200, 64, 2049, 16, 17], hq, hkv, d, bs, q_dt,
+                                                  partition)
+    assert max_abs(out_p, ref_p) <= TOL[q_dt]
+    assert max_abs(out_d, ref_d) <= TOL[q_dt]
+    assert _bits_equal(out_p, sep_p), "prefill part differs from pa_prefill_chunk"
+
+
+def test_fused_fp8_70b_shaped_step():
+    """A 70B-shaped layer with an fp8 cache (64 query / 8 KV heads, head_dim 128,
+    block 16, bf16 activations): four 512-token chunks over 1,536-token contexts
+    beside 128 decodes of lognormal lengths (median 1,500, clipped to
+    [16, 8,192]), 512-token decode partitions; every output against the oracle."""
+    rng = np.random.default_rng(415)
+    dctx = np.clip(np.round(rng.lognormal(np.log(1500.0), 0.8, 128)), 16, 8192).astype(int)
+    print(f"[fused fp8] decode tokens {int(dctx.sum())}", flush=True)
+    out_p, out_d, sep_p, ref_p, ref_d = _fp8_step(rng, [512] * 4, [1536] * 4, dctx, 64, 8, 128, 16, "bf16", 512)
+    err_p, err_d = max_abs(out_p, ref_p), max_abs(out_d, ref_d)
+    print(f"[fused fp8] prefill max-abs {err_p:.3e}, decode max-abs {err_d:.3e}", flush=True)
+    assert err_p <= TOL["bf16"] and err_d <= TOL["bf16"]
+    assert _bits_equal(out_p, sep_p)

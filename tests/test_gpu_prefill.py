@@ -7,49 +7,9 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_cases import TOL, as_f64, lib, max_abs, up, up_int
+from gpu_cases import TOL, as_f64, lib, max_abs, random_chunks as _random_chunks, up, up_int
 
 pytestmark = pytest.mark.gpu
-
-
-def _random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype, q_dtype=None):
-    """Pool holding each sequence's whole context (chunk included) + packed queries.
-    An fp8 pool holds the values / a per-tensor scale (amax / 448); the scales
-    are returned as the last two items."""
-    need = [-(-n // bs) for n in ctxs]
-    nb = sum(need) + 2
-    ids = rng.permutation(nb)
-    poison = int(ids[-1])
-    nan = W.NAN_BITS[dtype]
-    kp = np.full((nb, hkv, bs, d), nan, W.BITS_DTYPE[dtype])
-    vp = np.full((nb, hkv, bs, d), nan, W.BITS_DTYPE[dtype])
-    tables = np.full((len(ctxs), max(need)), poison, np.int32)
-    cur = 0
-    vals = {0: [], 1: []}
-    for s, n in enumerate(ctxs):
-        for b in range(need[s]):
-            tables[s, b] = ids[cur]
-            cur += 1
-        for i in (0, 1):
-            vals[i].append(rng.standard_normal((need[s], hkv, bs, d)).astype(np.float32))
-    scales = [1.0, 1.0]
-    if dtype == "fp8_e4m3":
-        for i in (0, 1):
-            amax = max(float(np.abs(v.transpose(1, 0, 2, 3).reshape(hkv, -1, d)[:, :n]).max())
-                       for v, n in zip(vals[i], ctxs))
-            scales[i] = float(np.float32(amax / W.FP8_MAX))
-    for s, n in enumerate(ctxs):
-        for i, pool in ((0, kp), (1, vp)):
-            x = vals[i][s] / np.float32(scales[i]) if dtype == "fp8_e4m3" else vals[i][s]
-            bits = W.to_bits(x, dtype)
-            flat = bits.transpose(1, 0, 2, 3).reshape(hkv, -1, d)
-            flat[:, n:, :] = nan
-            pool[tables[s, :need[s]]] = flat.reshape(hkv, need[s], bs, d).transpose(1, 0, 2, 3)
-    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
-    q = W.to_bits(rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32), q_dtype or dtype)
-    if dtype == "fp8_e4m3":
-        return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32), scales[0], scales[1]
-    return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32)
 
 
 CASES = [
