@@ -417,6 +417,20 @@ def run_mixed_bench(args, dev):
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    # the one-launch step captured as a HIP graph (one stream)
+    fused_graph_ms = None
+    if not args.no_graph:
+        gf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf):
+            fused_step()
+        for _ in range(3):
+            gf.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            gf.replay()
+        torch.cuda.synchronize()
+        fused_graph_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fevs]))
@@ -452,6 +466,9 @@ def run_mixed_bench(args, dev):
             "decode_gbps": round(eff / (fused_ms * 1e-3) / 1e9, 1),
             "mfma_frac": round(flops / (fused_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "hbm_frac": round(eff / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            # time both parts would take at their peaks, one after the other, over the fused time
+            "combined_frac": round((flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) + eff / (HBM_PEAK_GBPS * 1e9))
+                                   / (fused_ms * 1e-3), 4),
             "separate_launches_ms": round(sep_ms, 5),
             "traffic": decode_traffic_bytes(s.name, "mixed"), "traffic_unit": "bytes per launch of mixed_kernel"},
         "separate_launches_ms_per_step": round(sep_ms_step, 5),
@@ -459,6 +476,7 @@ def run_mixed_bench(args, dev):
         "prefill_tflops": round(tflops, 2), "decode_gbps": round(dec_gbps, 1),
         "prefill_tokens_per_s": round(int(case.query_start_loc[-1]) / (pre_ms * 1e-3), 1),
         "hipgraph_two_stream_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "hipgraph_fused_ms_per_step": None if fused_graph_ms is None else round(fused_graph_ms, 5),
         "decode_tokens_per_s_per_layer": round(len(case.decode_lens) / (ms_step * 1e-3), 1),
     }
 
