@@ -265,3 +265,39 @@ def test_fused_fp8_70b_shaped_step():
     print(f"[fused fp8] prefill max-abs {err_p:.3e}, decode max-abs {err_d:.3e}", flush=True)
     assert err_p <= TOL["bf16"] and err_d <= TOL["bf16"]
     assert _bits_equal(out_p, sep_p)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+def test_fused_step_at_the_plan_limit(cache):
+    """8,000 decodes of 1-64 tokens (the most a call plans: the lengths and
+    their prefix sums fill 64 KB of LDS, with the fp8 K staging on top) beside
+    two prefill chunks; every output against the oracle."""
+    rng = np.random.default_rng(8000)
+    dctx = rng.integers(1, 65, 8000)
+    hq, hkv, d, bs = 8, 2, 128, 16
+    pchunks, pctx = [33, 64], [100, 64]
+    chunks, ctxs = pchunks + [1] * len(dctx), pctx + list(dctx)
+    if cache == "fp8_e4m3":
+        q, qsl, kp, vp, tables, lens, ks, vs = random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, cache,
+                                                              q_dtype="bf16")
+    else:
+        q, qsl, kp, vp, tables, lens = random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, cache)
+        ks = vs = 1.0
+    P = len(pchunks)
+    scale = 1.0 / np.sqrt(d)
+    pa = lib()
+    gk, gv = up(kp, cache), up(vp, cache)
+    gq_p, gq_d = up(q[:qsl[P]], "bf16"), up(q[qsl[P]:], "bf16")
+    out_p, out_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
+    for partition in (0, 512, -1):
+        ws = pa.decode_workspace(gq_d, gk, 64, partition)
+        pa.pa_mixed_attention(out_p, gq_p, up_int(qsl[:P + 1]), up_int(tables[:P]), up_int(lens[:P]), 64, out_d,
+                              gq_d, up_int(tables[P:]), up_int(lens[P:]), 64, gk, gv, scale, k_scale=ks,
+                              v_scale=vs, partition_size=partition, workspace=ws)
+        torch.cuda.synchronize()
+        ref_p = oracle.prefill_chunk_attention(q[:qsl[P]], "bf16", qsl[:P + 1], kp, vp, cache, tables[:P],
+                                               lens[:P], scale, bs, hkv, k_scale=ks, v_scale=vs)
+        ref_d = oracle.decode_attention(q[qsl[P]:], "bf16", kp, vp, cache, tables[P:], lens[P:], scale, bs, hkv,
+                                        k_scale=ks, v_scale=vs)
+        assert max_abs(out_p, ref_p) <= TOL["bf16"], partition
+        assert max_abs(out_d, ref_d) <= TOL["bf16"], partition
