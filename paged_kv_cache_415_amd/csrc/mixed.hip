@@ -9,7 +9,7 @@
 // the decode work list; the rest are the prefill query tiles, each running
 // the prefill kernel's program.  MI355X dispatches workgroups in index order
 // as resources free up, so the decode workgroups spread over the CUs first
-// and the prefill tiles fill every other slot: the HBM-bound decode streams
+// and the prefill tiles fill the other slots: the HBM-bound decode streams
 // its K/V beside the matrix-core-bound prefill instead of after it.  How many
 // decode workgroups take shares is decided on the device from the step's
 // actual sizes (decode bytes against prefill flops) so that both parts end
