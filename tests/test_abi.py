@@ -133,6 +133,12 @@ def test_mixed_empty_step_is_ok(lib):
     assert _mixed(lib, nc=0, tq=0, mq=0, S=0) == OK
 
 
+def test_mixed_workspace_required(lib):
+    fake = ctypes.c_void_p(256)           # never dereferenced: the check fails first
+    assert _mixed(lib, ptr=fake, part=512) == WORKSPACE
+    assert b"workspace" in lib.pa_last_error()
+
+
 def test_partition_planning(pa):
     assert pa.pa_decode_partition_size(256, 8, 16, 8192, 512) == 512
     assert pa.pa_decode_partition_size(256, 8, 16, 8192, 48) < 0
