@@ -955,9 +955,10 @@ __device__ __forceinline__ int take_ticket(int* counter) {
 // Plan, zero outputs of empty sequences (every nwg-th sequence from wg),
 // then the waves take the workgroup's share of the work list from an LDS
 // queue.  `pick` may lower nwg once the plan (the clamped lengths in LDS)
-// is known; it must return the same count in every workgroup.  The decode kernel runs it as one persistent workgroup per CU
-// holding all the waves the CU keeps resident; the mixed-step kernel runs
-// it in workgroups of four waves beside prefill tiles.
+// is known; it must return the same count in every workgroup.  The decode
+// kernel runs it as one persistent workgroup per CU holding all the waves
+// the CU keeps resident; the mixed-step kernel runs it in workgroups of four
+// waves beside prefill tiles.
 //
 // Finer chunks (several per wave, so that fast waves could take more of
 // them) were measured slower on MI355X: each extra chunk adds a segment
