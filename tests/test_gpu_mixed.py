@@ -301,3 +301,44 @@ def test_fused_step_at_the_plan_limit(cache):
                                         k_scale=ks, v_scale=vs)
         assert max_abs(out_p, ref_p) <= TOL["bf16"], partition
         assert max_abs(out_d, ref_d) <= TOL["bf16"], partition
+
+
+def test_fused_fp8_step_graph_replays_equal_eager():
+    """The fp8 one-launch step captured in a HIP graph: each of four replays
+    (eager fills and a stale workspace between them) gives the eager bits."""
+    rng = np.random.default_rng(88)
+    hq, hkv, d, bs = 32, 8, 128, 16
+    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks(rng, [70, 33] + [1] * 6, [300, 33, 1, 64, 500, 1200, 17, 2049],
+                                                          hq, hkv, d, bs, "fp8_e4m3", q_dtype="bf16")
+    P = 2
+    scale = 1.0 / np.sqrt(d)
+    pa = lib()
+    gk, gv = up(kp, "fp8_e4m3"), up(vp, "fp8_e4m3")
+    gq_p, gq_d = up(q[:qsl[P]], "bf16"), up(q[qsl[P]:], "bf16")
+    args = (up_int(qsl[:P + 1]), up_int(tables[:P]), up_int(lens[:P]), 70)
+    dargs = (up_int(tables[P:]), up_int(lens[P:]), 2049)
+    ws = pa.decode_workspace(gq_d, gk, 2049)
+
+    def call(out_p, out_d):
+        pa.pa_mixed_attention(out_p, gq_p, *args, out_d, gq_d, *dargs, gk, gv, scale, k_scale=ks, v_scale=vs,
+                              workspace=ws)
+
+    eager_p, eager_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
+    call(eager_p, eager_d)
+    torch.cuda.synchronize()
+    out_p, out_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            call(out_p, out_d)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        out_p.fill_(0)
+        out_d.fill_(0)
+        ws.fill_(0xFF)
+        g.replay()
+        torch.cuda.synchronize()
+        assert _bits_equal(out_p, eager_p), f"prefill, replay {rep}"
+        assert _bits_equal(out_d, eager_d), f"decode, replay {rep}"
