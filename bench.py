@@ -68,7 +68,7 @@ def parse():
                          "llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
                          "| llama3_8b_int8kv | llama3_70b_fp8kv_tp8 "
                          "| tiny_f32 "
-                         "| mixed_prefix_bf16")
+                         "| mixed_prefix_bf16 | mixed_70b_fp8kv")
     ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size override (default: the workload's)")
@@ -327,18 +327,19 @@ def run_decode_bench(args, dev, name: str, extras: bool = True):
 # Mixed chunked-prefill + decode step (copy-on-write, scatter, prefill, decode)
 # ---------------------------------------------------------------------------
 
-def run_mixed_bench(args, dev):
+def run_mixed_bench(args, dev, spec=None):
     import numpy as np
     import torch
     import paged_kv_cache_415_amd as pa
     import workloads as W
 
-    case = W.make_mixed_case()
+    case = W.make_mixed_case(spec or W.MIXED_SPEC)
     s = case.spec
-    dt = s.dtype
+    dt, cdt = s.dtype, s.pool_dtype
+    ks, vs = case.k_scale, case.v_scale
     up = lambda a: W.bits_to_device(a, dt, dev)
     upi = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    kp, vp = up(case.k_pool), up(case.v_pool)
+    kp, vp = W.bits_to_device(case.k_pool, cdt, dev), W.bits_to_device(case.v_pool, cdt, dev)
     pairs = upi(case.cow_pairs)
     nk, nv, slots = up(case.new_k), up(case.new_v), upi(case.slot_mapping)
     qc, qd = up(case.q_chunk), up(case.q_decode)
@@ -349,37 +350,39 @@ def run_mixed_bench(args, dev):
     max_len = int(case.decode_lens.max())
     ws = pa.decode_workspace(qd, kp, max_len)
 
+    sc = dict(k_scale=ks, v_scale=vs)
+
     def fused_step(ev=None):
         pa.pa_copy_blocks(kp, vp, pairs)
-        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
+        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots, ks, vs)
         if ev is not None:
             ev[0].record()
         pa.pa_mixed_attention(out_c, qc, qsl, ptab, plen, max_q, out_d, qd, dtab, dlen, max_len, kp, vp,
-                              s.scale, workspace=ws)
+                              s.scale, workspace=ws, **sc)
         if ev is not None:
             ev[1].record()
 
     def step(ev=None, side=None):
         pa.pa_copy_blocks(kp, vp, pairs)
-        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots)
+        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots, ks, vs)
         if side is not None:
             # prefill chunks and decodes on two streams (joined at the end)
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
-                pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
-                pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
-            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
+                pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
+                pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
+            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q, **sc)
             torch.cuda.current_stream().wait_stream(side)
             return
         if ev is not None:
             ev[0].record()
-        pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q)
+        pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q, **sc)
         if ev is not None:
             ev[1].record()
-        pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+        pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
         if ev is not None:
             ev[2].record()
-        pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws)
+        pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
         if ev is not None:
             ev[3].record()
 
@@ -438,12 +441,12 @@ def run_mixed_bench(args, dev):
     ms_step = elapsed * 1e3 / args.steps
     sep_ms_step = sep_elapsed * 1e3 / args.steps
     flops = mixed_prefill_flops(case)
-    eff = W.effective_kv_bytes(case.decode_lens, s.num_kv_heads, s.head_dim, dt)
+    eff = W.effective_kv_bytes(case.decode_lens, s.num_kv_heads, s.head_dim, cdt)
     tflops = flops / (pre_ms * 1e-3) / 1e12
     dec_gbps = eff / (dec_ms * 1e-3) / 1e9
     return {
         "metric": METRIC, "value": round(eff / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
-        "ms_per_step": round(ms_step, 5), "dtype": dt,
+        "ms_per_step": round(ms_step, 5), "dtype": dt if cdt == dt else f"{dt}+{cdt}",
         "config": {"workload": s.description, "name": s.name,
                    "prefill_tokens": int(case.query_start_loc[-1]),
                    "decode_seqs": int(len(case.decode_lens)), "cow_pairs": int(len(case.cow_pairs))},
@@ -873,7 +876,8 @@ def main():
     import torch
     if args.config != "all" and args.config not in SUB_CONFIGS + [HEADLINE, "llama3_8b_int8kv",
                                                                    "llama3_8b_kfp8_vbf16",
-                                                                   "llama3_70b_fp8kv_tp8"]:
+                                                                   "llama3_70b_fp8kv_tp8",
+                                                                   "mixed_70b_fp8kv"]:
         print(f"unknown --config {args.config}", file=sys.stderr)
         sys.exit(2)
     # the CPU baseline forks oracle processes, so it runs before the GPU is initialised
@@ -888,6 +892,9 @@ def main():
     if name == "mixed_prefix_bf16":
         res = run_mixed_bench(args, dev)
         res["block_ops"] = run_block_ops_bench(dev)
+    elif name == "mixed_70b_fp8kv":
+        import workloads as W
+        res = run_mixed_bench(args, dev, W.MIXED_70B_FP8)
     else:
         res = run_decode_bench(args, dev, name)
     gpu_by_name = {name: res}

@@ -23,11 +23,12 @@ class MixedRun:
         pa = lib()
         self.case = case
         s = case.spec
-        dt = s.dtype
-        self.kp, self.vp = up(case.k_pool, dt), up(case.v_pool, dt)
+        dt, cdt = s.dtype, s.pool_dtype
+        self.sc = dict(k_scale=case.k_scale, v_scale=case.v_scale)
+        self.kp, self.vp = up(case.k_pool, cdt), up(case.v_pool, cdt)
         pa.pa_copy_blocks(self.kp, self.vp, up_int(case.cow_pairs))
         pa.pa_reshape_and_cache(up(case.new_k, dt), up(case.new_v, dt), self.kp, self.vp,
-                                up_int(case.slot_mapping))
+                                up_int(case.slot_mapping), case.k_scale, case.v_scale)
         self.qc, self.qd = up(case.q_chunk, dt), up(case.q_decode, dt)
         self.qsl = up_int(case.query_start_loc)
         self.ptab, self.plen = up_int(case.prefill_tables), up_int(case.prefill_lens)
@@ -43,7 +44,7 @@ class MixedRun:
         ws = pa.decode_workspace(self.qd, self.kp, self.max_len, partition_size)
         pa.pa_mixed_attention(out_c, self.qc, self.qsl, self.ptab, self.plen, self.max_q, out_d, self.qd,
                               self.dtab, self.dlen, self.max_len, self.kp, self.vp, s.scale,
-                              partition_size=partition_size, workspace=ws)
+                              partition_size=partition_size, workspace=ws, **self.sc)
         return out_c, out_d
 
     def separate(self):
@@ -52,22 +53,27 @@ class MixedRun:
         out_c, out_d = torch.empty_like(self.qc), torch.empty_like(self.qd)
         if self.max_q > 0:
             pa.pa_prefill_chunk(out_c, self.qc, self.qsl, self.kp, self.vp, self.ptab, self.plen, s.scale,
-                                self.max_q)
+                                self.max_q, **self.sc)
         ws = pa.decode_workspace(self.qd, self.kp, self.max_len)
         pa.pa_decode(out_d, self.qd, self.kp, self.vp, self.dtab, self.dlen, s.scale,
-                     max_seq_len=self.max_len, workspace=ws)
+                     max_seq_len=self.max_len, workspace=ws, **self.sc)
         return out_c, out_d
+
+    def oracle_pools(self):
+        c, s = self.case, self.case.spec
+        okp, ovp = oracle.copy_blocks(c.k_pool, c.v_pool, c.cow_pairs)
+        return oracle.reshape_and_cache(okp, ovp, s.pool_dtype, c.new_k, c.new_v, s.dtype, c.slot_mapping,
+                                        s.block_size, c.k_scale, c.v_scale)
 
     def oracle(self):
         c, s = self.case, self.case.spec
-        okp, ovp = oracle.copy_blocks(c.k_pool, c.v_pool, c.cow_pairs)
-        okp, ovp = oracle.reshape_and_cache(okp, ovp, s.dtype, c.new_k, c.new_v, s.dtype, c.slot_mapping,
-                                            s.block_size)
-        ref_c = oracle.prefill_chunk_attention(c.q_chunk, s.dtype, c.query_start_loc, okp, ovp, s.dtype,
+        okp, ovp = self.oracle_pools()
+        ref_c = oracle.prefill_chunk_attention(c.q_chunk, s.dtype, c.query_start_loc, okp, ovp, s.pool_dtype,
                                                c.prefill_tables, c.prefill_lens, s.scale, s.block_size,
-                                               s.num_kv_heads)
-        ref_d = oracle.decode_attention(c.q_decode, s.dtype, okp, ovp, s.dtype, c.decode_tables,
-                                        self.dlens, s.scale, s.block_size, s.num_kv_heads)
+                                               s.num_kv_heads, k_scale=c.k_scale, v_scale=c.v_scale)
+        ref_d = oracle.decode_attention(c.q_decode, s.dtype, okp, ovp, s.pool_dtype, c.decode_tables,
+                                        self.dlens, s.scale, s.block_size, s.num_kv_heads,
+                                        k_scale=c.k_scale, v_scale=c.v_scale)
         return ref_c, ref_d
 
 
@@ -342,3 +348,27 @@ def test_fused_fp8_step_graph_replays_equal_eager():
         torch.cuda.synchronize()
         assert _bits_equal(out_p, eager_p), f"prefill, replay {rep}"
         assert _bits_equal(out_d, eager_d), f"decode, replay {rep}"
+
+
+def test_fused_70b_fp8_serving_step_full_size():
+    """The 70B-shaped serving step over an fp8 cache (4 chunks of 512 tokens
+    after a shared 1,024-token prefix, 128 decodes of 256-4,096 tokens, 64/8
+    heads, block 16, per-tensor scales): copy-on-write and the quantising
+    scatter byte-exact against the oracle, every decode output and every
+    prefill output against the oracle, prefill bits equal to pa_prefill_chunk's."""
+    case = W.make_mixed_case(W.MIXED_70B_FP8)
+    print(f"[fused fp8 70b] decode tokens {int(case.decode_lens.sum())}, pool {case.k_pool.shape[0]} blocks",
+          flush=True)
+    run = MixedRun(case)
+    out_c, out_d = run.fused()
+    sep_c, _ = run.separate()
+    torch.cuda.synchronize()
+    assert _bits_equal(out_c, sep_c), "prefill part differs from pa_prefill_chunk"
+    okp, ovp = run.oracle_pools()
+    cdt = case.spec.pool_dtype
+    assert np.array_equal(W.torch_to_bits(run.kp, cdt), okp)
+    assert np.array_equal(W.torch_to_bits(run.vp, cdt), ovp)
+    ref_c, ref_d = run.oracle()
+    err_c, err_d = max_abs(out_c, ref_c), max_abs(out_d, ref_d)
+    print(f"[fused fp8 70b] prefill max-abs {err_c:.3e}, decode max-abs {err_d:.3e}", flush=True)
+    assert err_c <= TOL["bf16"] and err_d <= TOL["bf16"]

@@ -103,3 +103,23 @@ def test_mixed_case_structure():
     assert case.slot_mapping.shape == (4 * 16 + 3,)
     assert len(set(case.slot_mapping.tolist())) == len(case.slot_mapping)
     assert list(case.query_start_loc) == [0, 16, 32, 48, 64]
+
+
+def test_mixed_case_over_an_fp8_cache():
+    """The fp8 mixed step: pools hold E4M3 codes, its bf16 activations and new
+    rows are unchanged, and each per-tensor scale makes the largest magnitude
+    the pool will hold (stored values or quantised new rows) code to 448."""
+    import dataclasses
+    import oracle
+    spec = dataclasses.replace(W.MIXED_70B_FP8, num_q_heads=8, num_kv_heads=2, head_dim=64)
+    case = W.make_mixed_case(spec, num_forks=2, prefix_len=32, chunk_len=16, decode_lens=[20, 50, 1])
+    assert case.k_pool.dtype == np.uint8 and case.q_chunk.dtype == np.uint16
+    assert 0 < case.k_scale and 0 < case.v_scale and case.k_scale != case.v_scale
+    kp, vp = oracle.copy_blocks(case.k_pool, case.v_pool, case.cow_pairs)
+    kp, vp = oracle.reshape_and_cache(kp, vp, "fp8_e4m3", case.new_k, case.new_v, "bf16", case.slot_mapping,
+                                      spec.block_size, case.k_scale, case.v_scale)
+    for pool in (kp, vp):
+        vals = oracle.decode_elements(pool, "fp8_e4m3")
+        finite = vals[np.isfinite(vals)]
+        assert np.abs(finite).max() == 448.0
+

@@ -434,12 +434,18 @@ class MixedSpec:
     num_kv_heads: int = 8
     head_dim: int = 128
     block_size: int = 32
-    dtype: str = "bf16"
+    dtype: str = "bf16"              # queries and new K/V rows
     pool_factor: float = 1.1
     description: str = ("16 sequences share a 1024-token prefix (ref-counted blocks) and each "
                         "appends a 512-token causal chunk; 112 others decode one token at lens "
                         "U[256,4096]; 32/8 heads, head_dim 128, block 32, bf16; copy-on-write "
                         "of the first divergent block")
+    cache_dtype: str | None = None   # K/V pools: the same as dtype, or "fp8_e4m3" with
+                                     # per-tensor scales (amax of the values / 448)
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.cache_dtype or self.dtype
 
     @property
     def scale(self) -> float:
@@ -447,6 +453,20 @@ class MixedSpec:
 
 
 MIXED_SPEC = MixedSpec()
+
+# A 70B-shaped serving step over an fp8 cache ([ybb] 6.2, KV cache in FP8; the
+# pages' throughput figure is for Llama 3.3 70B FP8): four sequences share a
+# 1,024-token prefix and each prefills a 512-token chunk while 128 others
+# decode one token; 64 query / 8 KV heads, head_dim 128, block 16, bf16
+# activations, fp8 E4M3 K/V with per-tensor scales.
+MIXED_70B_FP8 = MixedSpec(
+    name="mixed_70b_fp8kv", num_forks=4, num_decode=128, num_q_heads=64, num_kv_heads=8,
+    block_size=16, cache_dtype="fp8_e4m3",
+    description=("70B-shaped serving step over an fp8 cache: 4 sequences share a 1024-token "
+                 "prefix and each appends a 512-token causal chunk; 128 others decode one "
+                 "token at lens U[256,4096]; 64/8 heads, head_dim 128, block 16, bf16 "
+                 "activations, fp8 e4m3 K/V with per-tensor scales; copy-on-write of the "
+                 "first divergent block"))
 
 
 @dataclass
@@ -470,6 +490,8 @@ class MixedCase:
     decode_tables: np.ndarray        # int32 [Sd][MBd]
     decode_lens: np.ndarray          # int32 [Sd]
     poison_block: int
+    k_scale: float = 1.0             # per-tensor scales of an fp8 pool (1.0 otherwise)
+    v_scale: float = 1.0
 
 
 def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int | None = None,
@@ -515,29 +537,48 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
     dec_tables = [mgr.allocate(int(n)) for n in dlens]
     poison_block = mgr._take()
 
-    nan = NAN_BITS[dt]
-    k_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[dt])
-    v_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[dt])
+    cdt = spec.pool_dtype
+    nan = NAN_BITS[cdt]
+    k_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[cdt])
+    v_pool = np.full((nb, H, bs, D), nan, dtype=BITS_DTYPE[cdt])
 
-    def fill(pool, ids, ntok):
+    # Values are drawn first and stored once the scales are known (an fp8
+    # pool's per-tensor scale is the amax of everything it will hold).
+    drawn = {"k": [], "v": []}
+
+    def fill(which, ids, ntok):
         vals = rng.standard_normal((len(ids), H, bs, D), dtype=np.float32)
-        bits = to_bits(vals, dt)
-        flat = bits.transpose(1, 0, 2, 3).reshape(H, -1, D)
-        flat[:, ntok:, :] = nan
-        pool[np.asarray(ids, dtype=np.int64)] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
+        drawn[which].append((ids, ntok, vals))
 
     # prefix contents (the chunk's own K/V come through the scatter)
-    fill(k_pool, prefix_ids, P)
-    fill(v_pool, prefix_ids, P)
+    fill("k", prefix_ids, P)
+    fill("v", prefix_ids, P)
     # decode sequences: everything but the newest token
     for t, n in zip(dec_tables, dlens):
-        fill(k_pool, t, int(n) - 1)
-        fill(v_pool, t, int(n) - 1)
+        fill("k", t, int(n) - 1)
+        fill("v", t, int(n) - 1)
 
     # New tokens: F*C chunk tokens then Sd decode tokens.
     T = F * C + Sd
     new_k = to_bits(rng.standard_normal((T, H, D), dtype=np.float32), dt)
     new_v = to_bits(rng.standard_normal((T, H, D), dtype=np.float32), dt)
+
+    scales = {"k": 1.0, "v": 1.0}
+    if cdt == "fp8_e4m3":
+        for which, new in (("k", new_k), ("v", new_v)):
+            m = float(np.abs(bits_to_torch(new, dt).float().numpy()).max()) if T else 0.0
+            for ids, ntok, vals in drawn[which]:
+                flat = vals.transpose(1, 0, 2, 3).reshape(H, -1, D)[:, :ntok, :]
+                if flat.size:
+                    m = max(m, float(np.abs(flat).max()))
+            scales[which] = float(np.float32(m / FP8_MAX)) if m > 0 else 1.0
+    for which, pool in (("k", k_pool), ("v", v_pool)):
+        for ids, ntok, vals in drawn[which]:
+            x = vals / np.float32(scales[which]) if cdt == "fp8_e4m3" else vals
+            bits = to_bits(x, cdt)
+            flat = bits.transpose(1, 0, 2, 3).reshape(H, -1, D)
+            flat[:, ntok:, :] = nan
+            pool[np.asarray(ids, dtype=np.int64)] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
     slot_mapping = np.zeros(T, dtype=np.int64)
     for f, t in enumerate(forks):
         for i in range(C):
@@ -568,7 +609,8 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
                      prefill_tables_shared=prefill_shared,
                      prefill_lens=np.full(F, P + C, dtype=np.int32),
                      q_decode=q_decode, decode_tables=decode_tables,
-                     decode_lens=dlens.astype(np.int32), poison_block=poison_block)
+                     decode_lens=dlens.astype(np.int32), poison_block=poison_block,
+                     k_scale=scales["k"], v_scale=scales["v"])
 
 
 # ---------------------------------------------------------------------------
