@@ -150,7 +150,7 @@ def prefill_chunk_attention(q_bits, q_dtype: str, query_start_loc, k_pool, v_poo
                             cache_dtype: str, block_tables, seq_lens, scale: float,
                             block_size: int, num_kv_heads: int,
                             k_scale: float = 1.0, v_scale: float = 1.0,
-                            rows=None) -> np.ndarray:
+                            rows=None, k_block_scales=None, v_block_scales=None) -> np.ndarray:
     """Causal attention of one prefill chunk per sequence over its paged context.
 
     bogosort page §15 "Chunked Prefill" and ai-engineering page "分块预填充保护
@@ -164,6 +164,9 @@ def prefill_chunk_attention(q_bits, q_dtype: str, query_start_loc, k_pool, v_poo
     query_start_loc[s] .. query_start_loc[s+1]-1.  With ``rows`` (a list of
     (token_row, head) pairs) only those outputs are evaluated and the result
     is [len(rows)][D]; otherwise it is float64 [total_q_tokens][Hq][D].
+    Scales apply as in decode_attention: per-tensor k_scale / v_scale, and for
+    an int8 cache the per-(block, KV head) k_block_scales / v_block_scales
+    before them.
     """
     q = decode_elements(q_bits, q_dtype)
     total, num_q_heads, head_dim = q.shape
@@ -176,8 +179,10 @@ def prefill_chunk_attention(q_bits, q_dtype: str, query_start_loc, k_pool, v_poo
         if s not in gathered:
             n = int(seq_lens[s])
             gathered[s] = (
-                gather_sequence(k_pool, cache_dtype, block_tables[s], n, block_size) * float(k_scale),
-                gather_sequence(v_pool, cache_dtype, block_tables[s], n, block_size) * float(v_scale),
+                gather_sequence(k_pool, cache_dtype, block_tables[s], n, block_size,
+                                k_block_scales) * float(k_scale),
+                gather_sequence(v_pool, cache_dtype, block_tables[s], n, block_size,
+                                v_block_scales) * float(v_scale),
             )
         return gathered[s]
 

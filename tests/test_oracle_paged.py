@@ -382,6 +382,35 @@ def test_int8_per_block_scales_match_sdpa_of_dequantised_cache():
         np.testing.assert_allclose(got[s], ref, rtol=0, atol=1e-12)
 
 
+def test_int8_prefill_per_block_scales_match_sdpa_of_dequantised_cache():
+    # a chunk over an int8 context: each key and value is its code times its
+    # block's scale, looked up token by token here; chunk query i at position
+    # n - L + i sees keys 0 .. n - L + i
+    rng = np.random.default_rng(33)
+    lens, chunks = [23, 50], [5, 17]
+    bs, hkv, d, hq = 8, 2, 16, 4
+    kc, vc, ks, vs, tables = _int8_pools(rng, lens, hkv, d, bs)
+    qsl = np.array([0, 5, 22], np.int32)
+    qf = rng.standard_normal((22, hq, d)).astype(np.float32)
+    got = oracle.prefill_chunk_attention(_f32_bits(qf), "f32", qsl, kc.view(np.uint8), vc.view(np.uint8),
+                                         "int8", tables, lens, 0.3, bs, hkv, k_block_scales=ks,
+                                         v_block_scales=vs)
+    for s, (n, L) in enumerate(zip(lens, chunks)):
+        keys = np.zeros((hkv, n, d))
+        vals = np.zeros((hkv, n, d))
+        for p in range(n):
+            b = tables[s, p // bs]
+            for h in range(hkv):
+                keys[h, p] = kc[b, h, p % bs].astype(np.float64) * np.float64(ks[b, h])
+                vals[h, p] = vc[b, h, p % bs].astype(np.float64) * np.float64(vs[b, h])
+        for i in range(L):
+            vis = n - L + i + 1
+            for h in range(hq):
+                ref = _sdpa(qf[qsl[s] + i, h][None, None, :], keys[h // 2:h // 2 + 1, :vis],
+                            vals[h // 2:h // 2 + 1, :vis], 0.3)[0, 0]
+                np.testing.assert_allclose(got[qsl[s] + i, h], ref, rtol=0, atol=1e-12)
+
+
 def test_int8_scatter_uses_each_blocks_scale():
     key = np.array([[[1.0, -2.0, 0.3, 100.0]], [[0.5, 0.25, -0.75, 3.0]]], np.float32)
     pool = np.zeros((3, 1, 2, 4), np.uint8)
