@@ -470,6 +470,26 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
                            float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_prefill_chunk_int8 — pa_prefill_chunk over an INT8 cache with
+ * per-block scales (see pa_reshape_and_cache_int8): for key j in block b,
+ *   logit = scale * k_scales[b][kv] * (q . Kcode[j])
+ *   out = sum_j softmax(logit)_j * v_scales[b][kv] * Vcode[j]
+ * the formula of pa_decode_int8 applied to each chunk query over its causal
+ * context.  q_dtype bf16 or f16 (codes enter the matrix products exactly as
+ * that type; each probability of the value product carries its key's V
+ * scale, the row sums do not).  Other arguments, layouts and limits are
+ * those of pa_prefill_chunk; an int8 cache given to pa_prefill_chunk without
+ * scales returns PA_ERR_INVALID_ARG.
+ */
+pa_status pa_prefill_chunk_int8(void* out, const void* q, const int32_t* query_start_loc,
+                                const void* k_pool, const void* v_pool, const float* k_scales,
+                                const float* v_scales, const int32_t* block_tables,
+                                const int32_t* seq_lens, float scale, int32_t block_size,
+                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, pa_dtype q_dtype, void* stream);
+
+/*
  * pa_mixed_attention — the attention of one mixed serving step in one
  * launch: the prefill chunks of some sequences and the one-token decodes of
  * others, over the same K/V pools.

@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
         getattr(lib, name).restype = i32
     lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, f32, vp]
+    lib.pa_prefill_chunk_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, vp]
     lib.pa_mixed_attention.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
                                        i32, vp, vp, f32, i32, i32, i32, i32, i32, i32, f32, f32, i32,
                                        vp, sz, vp]
@@ -102,7 +104,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_probe_read.argtypes = [vp, sz, vp, vp]
     lib.pa_probe_copy.argtypes = [vp, vp, sz, vp]
     for name in ("pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_copy_blocks", "pa_copy_blocks_partial",
-                 "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_mixed_attention",
+                 "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_prefill_chunk_int8",
+                 "pa_mixed_attention",
                  "pa_probe_read",
                  "pa_probe_copy"):
         getattr(lib, name).restype = i32
@@ -487,6 +490,21 @@ def pa_prefill_chunk(out, q, query_start_loc, k_pool, v_pool, block_tables, seq_
                                  bs, num_seqs, t, int(max_q_len), hq, hkv, d,
                                  block_tables.shape[1], _dtype(q), _dtype(k_pool),
                                  float(k_scale), float(v_scale), _stream(stream)))
+
+
+def pa_prefill_chunk_int8(out, q, query_start_loc, k_pool, v_pool, k_scales, v_scales, block_tables,
+                          seq_lens, scale: float, max_q_len: int, stream=None) -> None:
+    """pa_prefill_chunk over an INT8 cache with per-(block, KV head) scales (see pa.h)."""
+    t, hq, d = q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8 or v_pool.shape[1:] != k_pool.shape[1:]:
+        raise ValueError("K and V pools must be int8 with one block shape")
+    _scales(k_scales, k_pool)
+    _scales(v_scales, k_pool)
+    _check(_lib.pa_prefill_chunk_int8(_ptr(out), _ptr(q), _ptr(query_start_loc), _ptr(k_pool), _ptr(v_pool),
+                                      _ptr(k_scales), _ptr(v_scales), _ptr(block_tables), _ptr(seq_lens),
+                                      float(scale), bs, query_start_loc.shape[0] - 1, t, int(max_q_len), hq,
+                                      hkv, d, block_tables.shape[1], _dtype(q), _stream(stream)))
 
 
 def pa_mixed_attention(prefill_out, prefill_q, query_start_loc, prefill_block_tables, prefill_seq_lens,

@@ -711,7 +711,8 @@ pa_status prefill_setup(pa::PrefillParams* params, bool* work, void* out, const 
                         int32_t block_size, int32_t num_seqs, int32_t total_q_tokens,
                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t max_blocks_per_seq, pa_dtype q_dtype,
-                        pa_dtype cache_dtype, float k_scale, float v_scale) {
+                        pa_dtype cache_dtype, float k_scale, float v_scale,
+                        const float* k_scales = nullptr, const float* v_scales = nullptr) {
   *work = false;
   if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0)
     return fail(PA_ERR_INVALID_ARG, "negative size");
@@ -719,10 +720,16 @@ pa_status prefill_setup(pa::PrefillParams* params, bool* work, void* out, const 
   pa_status st = check_attention_shape(num_q_heads, num_kv_heads, head_dim, block_size,
                                        max_blocks_per_seq, q_dtype, cache_dtype, cache_dtype);
   if (st != PA_OK) return st;
-  if (cache_dtype != q_dtype && cache_dtype != PA_DTYPE_FP8_E4M3)
+  if (cache_dtype != q_dtype && cache_dtype != PA_DTYPE_FP8_E4M3 && cache_dtype != PA_DTYPE_INT8)
     return fail(PA_ERR_UNSUPPORTED,
-                "prefill supports a cache of the query's type (f32, f16, bf16) or an fp8 cache beside "
-                "bf16/f16 queries");
+                "prefill supports a cache of the query's type (f32, f16, bf16) or an fp8 or int8 cache "
+                "beside bf16/f16 queries");
+  if (cache_dtype == PA_DTYPE_INT8) {
+    if (!k_scales || !v_scales)
+      return fail(PA_ERR_INVALID_ARG, "an int8 cache needs its per-block scales (pa_prefill_chunk_int8)");
+    if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
+      return fail(PA_ERR_INVALID_ARG, "misaligned per-block scales");
+  }
   const int group = num_q_heads / num_kv_heads;
   if (q_dtype != PA_DTYPE_F32 && (group & (group - 1)))
     return fail(PA_ERR_UNSUPPORTED, "prefill over 16-bit or fp8 caches needs a power-of-two group");
@@ -762,6 +769,8 @@ pa_status prefill_setup(pa::PrefillParams* params, bool* work, void* out, const 
   p.max_blocks = max_blocks_per_seq;
   p.q_dtype = q_dtype;
   p.cache_dtype = cache_dtype;
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
   *work = true;
   return PA_OK;
 }
@@ -781,6 +790,27 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
                                      seq_lens, scale, block_size, num_seqs, total_q_tokens,
                                      max_q_len, num_q_heads, num_kv_heads, head_dim,
                                      max_blocks_per_seq, q_dtype, cache_dtype, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  if (!work) return ok();
+  return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+pa_status pa_prefill_chunk_int8(void* out, const void* q, const int32_t* query_start_loc,
+                                const void* k_pool, const void* v_pool, const float* k_scales,
+                                const float* v_scales, const int32_t* block_tables,
+                                const int32_t* seq_lens, float scale, int32_t block_size,
+                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, pa_dtype q_dtype, void* stream) {
+  if (q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16)
+    return fail(PA_ERR_UNSUPPORTED, "an int8 cache takes bf16 or f16 queries");
+  pa::PrefillParams p;
+  bool work = false;
+  const pa_status st = prefill_setup(&p, &work, out, q, query_start_loc, k_pool, v_pool, block_tables,
+                                     seq_lens, scale, block_size, num_seqs, total_q_tokens,
+                                     max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                     max_blocks_per_seq, q_dtype, PA_DTYPE_INT8, 1.0f, 1.0f, k_scales,
+                                     v_scales);
   if (st != PA_OK) return st;
   if (!work) return ok();
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");

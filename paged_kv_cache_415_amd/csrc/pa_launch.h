@@ -141,7 +141,9 @@ struct PrefillParams {
   int block_size;
   int max_blocks;
   int q_dtype;
-  int cache_dtype;     // K and V pools: q_dtype, or fp8 beside 16-bit queries
+  int cache_dtype;     // K and V pools: q_dtype, or fp8 / int8 beside 16-bit queries
+  const float* k_scales;   // int8 cache: [num_blocks][num_kv_heads] per-block scales
+  const float* v_scales;
 };
 
 // Index checks (flags numerically equal to the public pa_check_flag values).

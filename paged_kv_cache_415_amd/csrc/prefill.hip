@@ -7,12 +7,12 @@ namespace pa {
 // Two stages of (K tile, V tile).
 size_t prefill_smem_bytes(int head_dim) { return (size_t)2 * 2 * kKeyTile * head_dim * 2; }
 
-template <typename T, int D, int BS, bool KV8 = false>
+template <typename T, int D, int BS, bool KV8 = false, bool I8 = false>
 __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillParams p) {
   int seq, kvh, qtile;
   prefill_work(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x * gridDim.y * gridDim.z,
                gridDim.x, gridDim.y, seq, kvh, qtile);
-  prefill_tile<T, D, BS, KV8>(p, seq, kvh, qtile);
+  prefill_tile<T, D, BS, KV8, I8>(p, seq, kvh, qtile);
 }
 
 // ---------------------------------------------------------------------------
@@ -117,10 +117,11 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int qpos = kRowsPerWG / p.group;
   const dim3 grid((p.max_q_len + qpos - 1) / qpos, p.num_kv_heads, p.num_seqs);
   const size_t smem = prefill_smem_bytes(p.head_dim);
-  const bool kv8 = p.cache_dtype == kFP8;
+  const bool kv8 = p.cache_dtype == kFP8, i8 = p.cache_dtype == kI8;
 #define PA_PREFILL(T, D, BS)                                                                          \
   do {                                                                                               \
     if (kv8) hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS, true>), grid, dim3(kPThreads), smem, stream, p); \
+    else if (i8) hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS, true, true>), grid, dim3(kPThreads), smem, stream, p); \
     else hipLaunchKernelGGL((prefill_mfma_kernel<T, D, BS, false>), grid, dim3(kPThreads), smem, stream, p); \
   } while (0)
 #define PA_PREFILL_BS(T, D)                      \

@@ -37,6 +37,7 @@ namespace pa {
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(4))) int* ctab_ptr;   // block table, read-only
+typedef const __attribute__((address_space(4))) float* cscale_ptr;   // per-block scales, read-only
 
 
 // ds_read_b64_tr_b16 at LDS byte address `addr` + OFF.  Issued as inline
@@ -86,6 +87,18 @@ constexpr int kRowsPerWG = 128;
 constexpr int kKeyTile = 64;
 constexpr float kSlack = 8.0f;   // log2 units
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// The two 16-bit values of a packed pair, as float32 (exact).
+template <typename T>
+__device__ __forceinline__ float lo_of(uint32_t w) {
+  if constexpr (__is_same(T, __bf16)) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <typename T>
+__device__ __forceinline__ float hi_of(uint32_t w) {
+  if constexpr (__is_same(T, __bf16)) return __builtin_bit_cast(float, w & 0xffff0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
 
 // Tiles are stored row-major (one 2D-byte row per key) with the 16-byte
 // chunks of each row XOR-swizzled, so that the LDS reads of the matrix
@@ -192,14 +205,15 @@ struct TileSrc {
   }
 };
 
-// fp8 K/V tiles staged through registers.  Thread t of the workgroup owns
+// 8-bit K/V tiles (fp8 E4M3, or int8 with per-block scales) staged through
+// registers.  Thread t of the workgroup owns
 // key row t / 4 of every tile and bytes [D/4 (t % 4), D/4 (t % 4 + 1)) of it
 // (two 16-byte loads per pool at D = 128, one at D = 64); the 16 rows of a
 // wave lie in one cache block (two for 8-token blocks), whose ids come from
 // TileSrc::block_of.  store() decodes the codes to T (exact: every E4M3 value
-// is a bf16 and an f16 value) and writes them where the 16-bit copy would
-// have put them.
-template <typename T, int D, int BS>
+// and every int8 code is a bf16 and an f16 value) and writes them where the
+// 16-bit copy would have put them.
+template <typename T, int D, int BS, bool I8 = false>
 struct TileSrc8 {
   static constexpr int NL = D / 64;             // 16-byte loads per pool and thread
   static constexpr int TILE = kKeyTile * D * 2; // bytes of one 16-bit K or V tile in LDS
@@ -242,6 +256,12 @@ struct TileSrc8 {
     }
   }
 
+  // Two codes -> a packed pair of T, exactly (fp8 E4M3 or int8 codes).
+  static __device__ __forceinline__ uint32_t cvt(uint32_t w, bool hi) {
+    if constexpr (I8) return i8x2_to<T>(w, hi);
+    else return fp8x2_to<T>(w, hi);
+  }
+
   // Decode and store into a stage (K tile, then V tile).
   __device__ __forceinline__ void store(char* stage) const {
 #pragma unroll
@@ -249,10 +269,10 @@ struct TileSrc8 {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {        // 8 codes -> one 16-byte chunk of 8 values
         const int chunk = sub * (D / 32) + 2 * i + h;
-        const u32x4 kc = {fp8x2_to<T>(h ? k[i].z : k[i].x, false), fp8x2_to<T>(h ? k[i].z : k[i].x, true),
-                          fp8x2_to<T>(h ? k[i].w : k[i].y, false), fp8x2_to<T>(h ? k[i].w : k[i].y, true)};
-        const u32x4 vc = {fp8x2_to<T>(h ? v[i].z : v[i].x, false), fp8x2_to<T>(h ? v[i].z : v[i].x, true),
-                          fp8x2_to<T>(h ? v[i].w : v[i].y, false), fp8x2_to<T>(h ? v[i].w : v[i].y, true)};
+        const u32x4 kc = {cvt(h ? k[i].z : k[i].x, false), cvt(h ? k[i].z : k[i].x, true),
+                          cvt(h ? k[i].w : k[i].y, false), cvt(h ? k[i].w : k[i].y, true)};
+        const u32x4 vc = {cvt(h ? v[i].z : v[i].x, false), cvt(h ? v[i].z : v[i].x, true),
+                          cvt(h ? v[i].w : v[i].y, false), cvt(h ? v[i].w : v[i].y, true)};
         *reinterpret_cast<u32x4*>(stage + row * D * 2 + 16 * (chunk ^ k_swz<D>(row))) = kc;
         *reinterpret_cast<u32x4*>(stage + TILE + row * D * 2 + 16 * (chunk ^ v_swz<D>(row))) = vc;
       }
@@ -291,9 +311,12 @@ __device__ __forceinline__ void pv_mma(f32x4 (&acc)[2][D / 16], const u32x2 (&h)
     for (int b = 0; b < 2; ++b) acc[b][NB0 + j] = PMma<T>::mma(va, pop[b], acc[b][NB0 + j]);
   }
 }
+// popl: the probabilities whose row sums normalise the output (pop itself,
+// or for an int8 cache the same probabilities without the V block scales)
 template <typename T, int D>
 __device__ __forceinline__ void pv_tile(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[2], const u32x4 (&pop)[2][2],
-                                        uint32_t stage, const uint32_t (&voff)[D / 16]) {
+                                        const u32x4 (&popl)[2][2], uint32_t stage,
+                                        const uint32_t (&voff)[D / 16]) {
   const u32x4 ones = {kOnes<T>, kOnes<T>, kOnes<T>, kOnes<T>};
   u32x2 h0[8], h1[8];
   if constexpr (D == 128) {
@@ -320,7 +343,7 @@ __device__ __forceinline__ void pv_tile(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[
 #pragma unroll
   for (int ap = 0; ap < 2; ++ap)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[ap][b], acc_l[b]);
+    for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, popl[ap][b], acc_l[b]);
 }
 
 // Work item `lin` of `nwg` (the workgroup's linear index in a launch whose
@@ -351,8 +374,12 @@ __device__ __forceinline__ void prefill_work(int lin, int nwg, int nq, int nkv, 
 
 // One workgroup's query tile: rows qtile * 128 .. of the chunk of sequence
 // `seq`, the query heads of KV head `kvh`.
-template <typename T, int D, int BS, bool KV8 = false>
+template <typename T, int D, int BS, bool KV8 = false, bool I8 = false>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, int kvh, int qtile) {
+  static_assert(KV8 || !I8, "int8 codes are staged like fp8 codes");
+  // an int8 cache's V scale enters the 16-bit probability operand, so with
+  // f16 queries the reference max moves with every larger logit (p <= 1)
+  constexpr float kSl = (I8 && __is_same(T, _Float16)) ? 0.0f : kSlack;
   extern __shared__ __align__(16) char smem_raw[];
   constexpr int NC = D / 32;
   constexpr int NB = D / 16;                 // 16-dimension blocks of the output
@@ -444,7 +471,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
 
   TileSrc<D, BS> src;
   src.init(kpool, vpool, trow, p.num_kv_heads, kvh, kend, wave, lane);
-  TileSrc8<T, D, BS> src8;
+  TileSrc8<T, D, BS, I8> src8;
   if constexpr (KV8) {
     src8.init(kpool, vpool, trow, p.num_kv_heads, kvh, kend);
     src8.load(0, src.block_of(0));
@@ -464,6 +491,21 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
       if constexpr (KV8) src8.load(kt + 1, blk_next);   // into registers
       else src.copy(kt + 1, blk_next, smem_raw + ((kt + 1) & 1) * 2 * TILE);
       blk_next = src.block_of(kt + 2);   // in flight while this tile is computed
+    }
+
+    // int8: the K and V scales of the cache block holding this lane's four
+    // key rows of each 16-row block (rows 4G .. 4G + 3; the block ids of keys
+    // past the context are those of the last key, whose scores are masked)
+    float ksc[4], vsc[4];
+    if constexpr (I8) {
+      const cscale_ptr ksp = (cscale_ptr)p.k_scales, vsp = (cscale_ptr)p.v_scales;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int key = min(kt * kKeyTile + 16 * a + (BS < 16 ? 8 * (G >> 1) : 0), kend - 1);
+        const int64_t sidx = (int64_t)((ctab_ptr)trow)[key / BS] * p.num_kv_heads + kvh;
+        ksc[a] = ksp[sidx];
+        vsc[a] = vsp[sidx];
+      }
     }
 
     // ---- raw products q.k for 4 key row-tiles x 2 query column-tiles
@@ -494,7 +536,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[a][b][i] = sc[a][b][i];
+        for (int i = 0; i < 4; ++i) s[a][b][i] = I8 ? sc[a][b][i] * ksc[a] : sc[a][b][i];
     if (diag) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -524,7 +566,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
     // row's max exceeds it by more than kSlack, so p <= 2^kSlack; when it
     // moves for some row, every row of the wave takes its exact new max.  A
     // row whose keys are all masked in this tile has mx = -inf and keeps it.
-    if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kSlack || mx[1] > m_run[1] + kSlack) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kSl || mx[1] > m_run[1] + kSl) != 0) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const float m_new = fmaxf(m_run[b], mx[b]);
@@ -535,24 +577,39 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
         for (int nn = 0; nn < NB; ++nn) acc[b][nn] = acc[b][nn] * alpha;
       }
     }
-    // p = 2^(c * (q.k) - m): one fused multiply-add per score
+    // p = 2^(c * (q.k) - m): one fused multiply-add per score.  int8: the
+    // value product takes p times the key's block V scale, the row sums p.
     u32x4 pop[2][2];   // [key pair][column tile]
+    u32x4 popl[I8 ? 2 : 1][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const float nm = -m_run[b];
-      uint32_t w[4][2];
+      uint32_t w[4][2], wl[4][2];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; i += 2)
-          w[a][i / 2] = pack2<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i], cscale, nm)),
-                                 __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i + 1], cscale, nm)));
+        for (int i = 0; i < 4; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i], cscale, nm));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i + 1], cscale, nm));
+          if constexpr (I8) {
+            // the rounded probabilities, then each times its V scale: a row
+            // dominated by one key keeps that key's value to one rounding
+            const uint32_t pl = pack2<T>(e0, e1);
+            wl[a][i / 2] = pl;
+            w[a][i / 2] = pack2<T>(lo_of<T>(pl) * vsc[a], hi_of<T>(pl) * vsc[a]);
+          } else {
+            w[a][i / 2] = pack2<T>(e0, e1);
+          }
+        }
 #pragma unroll
-      for (int ap = 0; ap < 2; ++ap)
+      for (int ap = 0; ap < 2; ++ap) {
         pop[ap][b] = u32x4{w[2 * ap][0], w[2 * ap][1], w[2 * ap + 1][0], w[2 * ap + 1][1]};
+        if constexpr (I8) popl[ap][b] = u32x4{wl[2 * ap][0], wl[2 * ap][1], wl[2 * ap + 1][0], wl[2 * ap + 1][1]};
+      }
     }
     __builtin_amdgcn_s_setprio(1);
-    pv_tile<T, D>(acc, acc_l, pop, v_base, voff);
+    if constexpr (I8) pv_tile<T, D>(acc, acc_l, pop, popl, v_base, voff);
+    else pv_tile<T, D>(acc, acc_l, pop, pop, v_base, voff);
     __builtin_amdgcn_s_setprio(0);
     if (more) {
       // this wave's copy of the next tile has landed (8-bit: decoded and

@@ -165,3 +165,31 @@ def random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, dtype, q_dtype=None):
     if dtype == "fp8_e4m3":
         return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32), scales[0], scales[1]
     return q, qsl, kp, vp, tables, np.asarray(ctxs, np.int32)
+
+
+def random_chunks_int8(rng, chunks, ctxs, hq, hkv, d, bs, q_dtype, v_scale_mul=1.0):
+    """As random_chunks, over an int8 cache: codes uniform in [-127, 127], one
+    float32 scale per (block, KV head) per pool (V scales times v_scale_mul);
+    rows past each context hold code 127.  Returns q, qsl, kp, vp, tables,
+    lens, k_scales, v_scales (pools as raw bytes)."""
+    need = [-(-n // bs) for n in ctxs]
+    nb = sum(need) + 2
+    ids = rng.permutation(nb)
+    poison = int(ids[-1])
+    kp = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+    vp = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+    ks = (rng.uniform(0.5, 2.0, (nb, hkv)) / 32).astype(np.float32)
+    vs = (rng.uniform(0.5, 2.0, (nb, hkv)) / 64 * v_scale_mul).astype(np.float32)
+    tables = np.full((len(ctxs), max(need)), poison, np.int32)
+    cur = 0
+    for s_, n in enumerate(ctxs):
+        tables[s_, :need[s_]] = ids[cur:cur + need[s_]]
+        cur += need[s_]
+        for pool in (kp, vp):
+            flat = pool[tables[s_, :need[s_]]].transpose(1, 0, 2, 3).reshape(hkv, -1, d)
+            flat[:, n:, :] = 127
+            pool[tables[s_, :need[s_]]] = flat.reshape(hkv, need[s_], bs, d).transpose(1, 0, 2, 3)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = W.to_bits(rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32), q_dtype)
+    return q, qsl, kp.view(np.uint8), vp.view(np.uint8), tables, np.asarray(ctxs, np.int32), ks, vs
+

@@ -232,10 +232,17 @@ def test_int8_cache_needs_its_scales(lib):
                                          128, 16, BF16, None) == OK              # nothing to do
     assert lib.pa_reshape_and_cache_int8(None, None, None, None, fake, fake, None, 0, 0, 0, 4, 2,
                                          128, 16, INT8, None) == UNSUPPORTED     # int8 source
-    # prefill reads 16-bit caches only
+    # an int8 cache reaches prefill only through pa_prefill_chunk_int8, with its scales
     st = lib.pa_prefill_chunk(None, None, None, None, None, None, None, 0.1, 16, 1, 4, 4, 8, 2, 128,
                               8, BF16, INT8, 1.0, 1.0, None)
-    assert st == UNSUPPORTED
+    assert st == INVALID and b"pa_prefill_chunk_int8" in lib.pa_last_error()
+    prefill8 = lambda ks, vs, qdt: lib.pa_prefill_chunk_int8(None, None, None, None, None, ks, vs, None, None,
+                                                             0.1, 16, 1, 4, 4, 8, 2, 128, 8, qdt, None)
+    assert prefill8(None, None, BF16) == INVALID                                # no scales
+    assert prefill8(fake, fake, F32) == UNSUPPORTED                             # f32 queries
+    assert prefill8(fake, fake, BF16) == INVALID                                # null tensors
+    assert lib.pa_prefill_chunk_int8(None, None, None, None, None, fake, fake, None, None, 0.1, 16, 0, 0,
+                                     0, 8, 2, 128, 8, F16, None) == OK          # nothing to do
 
 
 def test_append_checks(lib):

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_cases import TOL, as_f64, lib, max_abs, random_chunks as _random_chunks, up, up_int
+from gpu_cases import TOL, as_f64, lib, max_abs, random_chunks as _random_chunks, random_chunks_int8, up, up_int
 
 pytestmark = pytest.mark.gpu
 
@@ -288,3 +288,74 @@ def test_prefill_f32_matches_oracle(chunks, ctxs, hq, hkv, d, bs):
                            up_int(lens), scale, max(chunks))
     torch.cuda.synchronize()
     assert max_abs(out, ref) <= TOL["f32"]
+
+
+INT8_CASES = [
+    # (chunks, contexts, Hq, Hkv, D, bs, query type)
+    ([5, 16, 1], [5, 40, 70], 4, 1, 128, 16, "bf16"),
+    ([33, 100], [33, 300], 8, 2, 128, 32, "bf16"),
+    ([64, 7], [200, 7], 32, 8, 128, 16, "f16"),
+    ([20, 9], [85, 9], 8, 2, 128, 8, "bf16"),
+    ([70], [300], 4, 4, 64, 64, "f16"),
+    ([17, 50], [60, 99], 16, 1, 64, 16, "bf16"),
+    ([100], [130], 4, 1, 64, 8, "f16"),
+    ([40, 130], [555, 131], 64, 8, 128, 16, "bf16"),
+]
+
+
+def _prefill_int8(q, qsl, kp, vp, tables, lens, ks, vs, hkv, d, bs, q_dt, scale, max_q):
+    gq = up(q, q_dt)
+    out = torch.empty_like(gq)
+    lib().pa_prefill_chunk_int8(out, gq, up_int(qsl), up(kp, "int8"), up(vp, "int8"),
+                                torch.from_numpy(ks).to(gq.device), torch.from_numpy(vs).to(gq.device),
+                                up_int(tables), up_int(lens), scale, max_q)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_chunk_attention(q, q_dt, qsl, kp, vp, "int8", tables, lens, scale, bs, hkv,
+                                         k_block_scales=ks, v_block_scales=vs)
+    return out, ref
+
+
+@pytest.mark.parametrize("chunks,ctxs,hq,hkv,d,bs,q_dt", INT8_CASES)
+def test_prefill_int8_cache_matches_oracle(chunks, ctxs, hq, hkv, d, bs, q_dt):
+    """Prefill over an INT8 cache with per-(block, KV head) scales ([ybb] 6.2):
+    codes exact in the 16-bit operands, each key's block K scale on its score
+    and V scale on its probability."""
+    rng = np.random.default_rng(sum(chunks) + 5 * hq + d + bs)
+    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks_int8(rng, chunks, ctxs, hq, hkv, d, bs, q_dt)
+    out, ref = _prefill_int8(q, qsl, kp, vp, tables, lens, ks, vs, hkv, d, bs, q_dt, 1.0 / np.sqrt(d),
+                             max(chunks))
+    assert max_abs(out, ref) <= TOL[q_dt]
+
+
+def test_prefill_int8_last_row_matches_int8_decode():
+    """The last row of each chunk over an int8 cache equals the int8 decode of
+    its sequence (two kernels, one formula)."""
+    rng = np.random.default_rng(808)
+    chunks, ctxs, hq, hkv, d, bs = [9, 30], [100, 64], 8, 2, 128, 16
+    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks_int8(rng, chunks, ctxs, hq, hkv, d, bs, "bf16")
+    out, _ = _prefill_int8(q, qsl, kp, vp, tables, lens, ks, vs, hkv, d, bs, "bf16", 0.1, 30)
+    pa = lib()
+    gq = up(q, "bf16")
+    last = gq[torch.tensor([8, 38], device=gq.device)].contiguous()
+    dec = torch.empty_like(last)
+    pa.pa_decode_int8(dec, last, up(kp, "int8"), up(vp, "int8"), torch.from_numpy(ks).to(gq.device),
+                      torch.from_numpy(vs).to(gq.device), up_int(tables), up_int(lens), 0.1, max_seq_len=100,
+                      partition_size=-1)
+    torch.cuda.synchronize()
+    assert np.abs(as_f64(out[[8, 38]]) - as_f64(dec)).max() <= TOL["bf16"]
+
+
+def test_prefill_int8_f16_queries_large_value_scales():
+    """f16 queries over an int8 cache whose V values reach about 4e4 (block V
+    scales near 300): the value operand p x scale must stay inside f16's
+    range while the running max moves (queries x 6, logits spread widely)."""
+    rng = np.random.default_rng(909)
+    chunks, ctxs, hq, hkv, d, bs = [64, 33], [300, 700], 8, 2, 128, 16
+    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks_int8(rng, chunks, ctxs, hq, hkv, d, bs, "f16",
+                                                              v_scale_mul=1.5e4)
+    q = W.to_bits(W.bits_to_torch(q, "f16").float().numpy() * 6, "f16")
+    assert float(vs.max()) > 300
+    out, ref = _prefill_int8(q, qsl, kp, vp, tables, lens, ks, vs, hkv, d, bs, "f16", 1.0 / np.sqrt(d), 64)
+    err = max_abs(out, ref)
+    assert err <= TOL["f16"] * float(np.abs(ref).max()) / 4, err
+
