@@ -375,8 +375,9 @@ pa_status pa_decode_reduce_kv(void* out, const void* q, const void* k_pool, cons
  *   logit_j = scale * k_scales[b][kv] * (q . Kcode[j])
  *   out = sum_j softmax(logit)_j * v_scales[b][kv] * Vcode[j]
  * q_dtype bf16 or f16 (codes enter the matrix products exactly as that
- * type).  Other arguments, limits, workspace and partition rules are those
- * of pa_decode; the attention / reduce stages are split as for pa_decode.
+ * type; p * v_scales is rounded once to it for the value product, the sums
+ * of p stay float32).  Other arguments, limits, workspace and partition
+ * rules are those of pa_decode; the attention / reduce stages are split as for pa_decode.
  */
 pa_status pa_decode_int8(void* out, const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scales, const float* v_scales, const int32_t* block_tables,
@@ -477,7 +478,8 @@ pa_status pa_prefill_chunk(void* out, const void* q, const int32_t* query_start_
  * the formula of pa_decode_int8 applied to each chunk query over its causal
  * context.  q_dtype bf16 or f16 (codes enter the matrix products exactly as
  * that type; each probability of the value product carries its key's V
- * scale, the row sums do not).  Other arguments, layouts and limits are
+ * scale and is rounded once to the query type, the row sums add the float32
+ * probabilities without it).  Other arguments, layouts and limits are
  * those of pa_prefill_chunk; an int8 cache given to pa_prefill_chunk without
  * scales returns PA_ERR_INVALID_ARG.
  */
@@ -508,7 +510,9 @@ pa_status pa_prefill_chunk_int8(void* out, const void* q, const int32_t* query_s
  *
  * Supported: bf16 or f16 queries over a cache of the same type, or over an
  * fp8 E4M3 cache with per-tensor k_scale / v_scale as in pa_decode and
- * pa_prefill_chunk ([ybb] §6.2); other pairs return PA_ERR_UNSUPPORTED.  The
+ * pa_prefill_chunk ([ybb] §6.2); an int8 cache goes through
+ * pa_mixed_attention_int8 (here it returns PA_ERR_INVALID_ARG); other pairs
+ * return PA_ERR_UNSUPPORTED.  The
  * prefill outputs equal pa_prefill_chunk's bit for bit; the decode outputs
  * may differ from a pa_decode call by rounding, since the work is cut for
  * this launch's waves.  The workspace is pa_decode_workspace_bytes(num_decodes, ...) long
@@ -528,6 +532,30 @@ pa_status pa_mixed_attention(void* prefill_out, const void* prefill_q,
                              int32_t head_dim, pa_dtype q_dtype, pa_dtype cache_dtype,
                              float k_scale, float v_scale, int32_t partition_size,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_mixed_attention_int8 — pa_mixed_attention over an INT8 cache with
+ * per-(block, KV head) scales (layout and meaning of pa_reshape_and_cache_int8;
+ * [ybb] §6.2, KV cache quantisation): the prefill part computes
+ * pa_prefill_chunk_int8, the decode part pa_decode_int8, in one launch.
+ * k_scales / v_scales: float32 [num_blocks, num_kv_heads] device arrays,
+ * caller-owned, read only (null returns PA_ERR_INVALID_ARG).  q_dtype bf16 or
+ * f16.  Other arguments, limits, outputs and errors are pa_mixed_attention's;
+ * the prefill outputs equal pa_prefill_chunk_int8's bit for bit.
+ */
+pa_status pa_mixed_attention_int8(void* prefill_out, const void* prefill_q,
+                                  const int32_t* query_start_loc, const int32_t* prefill_block_tables,
+                                  const int32_t* prefill_seq_lens, int32_t num_chunks,
+                                  int32_t total_q_tokens, int32_t max_q_len,
+                                  int32_t prefill_max_blocks_per_seq, void* decode_out,
+                                  const void* decode_q, const int32_t* decode_block_tables,
+                                  const int32_t* decode_seq_lens, int32_t num_decodes,
+                                  int32_t decode_max_blocks_per_seq, int32_t max_seq_len,
+                                  const void* k_pool, const void* v_pool, const float* k_scales,
+                                  const float* v_scales, float scale, int32_t block_size,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  pa_dtype q_dtype, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Index checks.  The calls above trust device-resident indices (a block id

@@ -93,6 +93,9 @@ def _load() -> ctypes.CDLL:
     lib.pa_mixed_attention.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
                                        i32, vp, vp, f32, i32, i32, i32, i32, i32, i32, f32, f32, i32,
                                        vp, sz, vp]
+    lib.pa_mixed_attention_int8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
+                                            i32, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, vp, sz,
+                                            vp]
     lib.pa_check_block_tables.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_check_block_tables.restype = i32
     lib.pa_check_slots.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -105,7 +108,7 @@ def _load() -> ctypes.CDLL:
     lib.pa_probe_copy.argtypes = [vp, vp, sz, vp]
     for name in ("pa_reshape_and_cache", "pa_reshape_and_cache_kv", "pa_copy_blocks", "pa_copy_blocks_partial",
                  "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill_chunk", "pa_prefill_chunk_int8",
-                 "pa_mixed_attention",
+                 "pa_mixed_attention", "pa_mixed_attention_int8",
                  "pa_probe_read",
                  "pa_probe_copy"):
         getattr(lib, name).restype = i32
@@ -534,6 +537,33 @@ def pa_mixed_attention(prefill_out, prefill_q, query_start_loc, prefill_block_ta
         float(v_scale), int(partition_size), _ptr(workspace), wbytes, _stream(stream)))
 
 
+def pa_mixed_attention_int8(prefill_out, prefill_q, query_start_loc, prefill_block_tables, prefill_seq_lens,
+                            max_q_len: int, decode_out, decode_q, decode_block_tables, decode_seq_lens,
+                            max_seq_len: int, k_pool, v_pool, k_scales, v_scales, scale: float,
+                            partition_size: int = 0, workspace=None, stream=None) -> None:
+    """pa_mixed_attention over an INT8 cache with per-(block, KV head) scales (see pa.h)."""
+    t, hq, d = prefill_q.shape
+    s, hq_d, d_d = decode_q.shape
+    _, hkv, bs, _ = k_pool.shape
+    if (hq_d, d_d) != (hq, d) or _dtype(decode_q) != _dtype(prefill_q):
+        raise ValueError("prefill and decode queries differ in heads, head size or type")
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8 or v_pool.shape[1:] != k_pool.shape[1:]:
+        raise ValueError("K and V pools must be int8 with one block shape")
+    _scales(k_scales, k_pool)
+    _scales(v_scales, k_pool)
+    for a in (query_start_loc, prefill_block_tables, prefill_seq_lens, decode_block_tables, decode_seq_lens):
+        if a.dtype != torch.int32:
+            raise TypeError("offsets, block tables and lengths must be int32")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pa_mixed_attention_int8(
+        _ptr(prefill_out), _ptr(prefill_q), _ptr(query_start_loc), _ptr(prefill_block_tables),
+        _ptr(prefill_seq_lens), query_start_loc.shape[0] - 1, t, int(max_q_len),
+        prefill_block_tables.shape[1], _ptr(decode_out), _ptr(decode_q), _ptr(decode_block_tables),
+        _ptr(decode_seq_lens), s, decode_block_tables.shape[1], int(max_seq_len), _ptr(k_pool),
+        _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), float(scale), bs, hq, hkv, d, _dtype(prefill_q),
+        int(partition_size), _ptr(workspace), wbytes, _stream(stream)))
+
+
 CHECK_FLAGS = {"block_id": 1, "length": 2, "slot": 4, "chunk": 8}
 
 
@@ -582,7 +612,8 @@ __all__ = [
     "layer_pool_pointers",
     "pa_swap_blocks", "pa_decode", "pa_decode_noalloc", "pa_decode_noalloc_max_workspace_bytes",
     "pa_decode_attention",
-    "pa_decode_reduce", "pa_prefill_chunk", "pa_decode_partition_size",
+    "pa_decode_reduce", "pa_prefill_chunk", "pa_prefill_chunk_int8", "pa_mixed_attention",
+    "pa_mixed_attention_int8", "pa_decode_partition_size",
     "pa_decode_workspace_bytes", "decode_workspace", "pa_probe_read", "pa_probe_copy",
     "pa_check_block_tables", "pa_check_slots", "CHECK_FLAGS",
     "PagedAttentionError", "library", "LIB_PATH",

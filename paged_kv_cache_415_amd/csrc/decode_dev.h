@@ -391,7 +391,9 @@ struct MfmaDecode {
   // m: the reference max (log2 units); l4: the sums of the rounded
   // probabilities, formed on the matrix cores by a value product against an
   // all-ones operand (every element of a lane's l4 holds its head's sum over
-  // all the tokens so far); acc: the unnormalised output.
+  // all the tokens so far), or for an int8 cache the float32 probabilities
+  // summed per lane in l4[0] (the head's four lanes are added at the end);
+  // acc: the unnormalised output.
   struct State {
     float m;
     f32x4 l4;
@@ -505,23 +507,32 @@ struct MfmaDecode {
 #pragma unroll
       for (int n = 0; n < DPL; ++n) st.acc[n] = st.acc[n] * alpha;
     }
-    uint32_t pw[4], pr[4];
+    uint32_t pw[4];
+    float ls = 0.f;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         const float a = __builtin_amdgcn_exp2f(s[tau][i] - st.m);
         const float b = __builtin_amdgcn_exp2f(s[tau][i + 1] - st.m);
-        pr[tau * 2 + i / 2] = pack2<QT>(a, b);
-        // int8: the value operand carries the block's V scale; the sum does not
-        pw[tau * 2 + i / 2] = kBlockScales ? pack2<QT>(a * buf.vs[tau], b * buf.vs[tau]) : pr[tau * 2 + i / 2];
+        // int8: the value operand carries the block's V scale, rounded once
+        // with the probability; the sum takes the float32 probabilities, so
+        // each weight of the normalised output carries a single rounding
+        if constexpr (kBlockScales) {
+          pw[tau * 2 + i / 2] = pack2<QT>(a * buf.vs[tau], b * buf.vs[tau]);
+          ls += a + b;
+        } else {
+          pw[tau * 2 + i / 2] = pack2<QT>(a, b);
+        }
       }
     }
     const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]};
-    // the sum of the rounded probabilities (so that the weights stay
-    // normalised): their product with an all-ones operand
-    st.l4 = Mma<QT>::mma(u32x4{kOnes<QT>, kOnes<QT>, kOnes<QT>, kOnes<QT>},
-                         u32x4{pr[0], pr[1], pr[2], pr[3]}, st.l4);
+    // 16-bit and fp8: the sum of the rounded probabilities (so that the
+    // weights stay normalised), their product with an all-ones operand
+    if constexpr (kBlockScales)
+      st.l4[0] += ls;
+    else
+      st.l4 = Mma<QT>::mma(u32x4{kOnes<QT>, kOnes<QT>, kOnes<QT>, kOnes<QT>}, pop, st.l4);
 
     // Values: A operand for dim DPL*c16 + n holds tokens 4G+0..3 of tile 0
     // then 4G+0..3 of tile 1.
@@ -746,7 +757,7 @@ struct MfmaDecode {
       }
     }
     // lane (G, c16) holds head c16, dims DPL*(4G+i) + n
-    const float l_tot = st.l4[0];
+    const float l_tot = kBlockScales ? lanes4_sum(st.l4[0]) : st.l4[0];
     if constexpr (kLocalMerge) {
       if (nparts > 1 && lm.counter >= 0) {
         merge_local(p, st.acc, st.m, l_tot, s, kvh, part, nparts, lm);

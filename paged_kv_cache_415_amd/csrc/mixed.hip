@@ -42,10 +42,12 @@ constexpr int kMixedWaves = kPThreads / 64;   // waves per workgroup, both kinds
 // kernel's byte rate against the bf16 one, the prefill rate by the fp8
 // prefill tiles' (codes decoded into LDS through registers); on that
 // workload over an fp8 cache any split from 96 to 256 decode workgroups
-// lands within 2 % of the best.  Only the ratio of a pair matters; it sets
-// how many slots the decode part takes.
-constexpr double kDecodeWgBytesPerUs[2] = {24.5e3, 21.2e3};
-constexpr double kPrefillSlotFlopsPerUs[2] = {1.34e6, 1.30e6};
+// lands within 2 % of the best.  [2], the int8 cache with per-block scales,
+// is scaled the same way from the int8 decode kernel's byte rate and the
+// int8 prefill tiles' flop rate.  Only the
+// ratio of a pair matters; it sets how many slots the decode part takes.
+constexpr double kDecodeWgBytesPerUs[3] = {24.5e3, 21.2e3, 22.1e3};
+constexpr double kPrefillSlotFlopsPerUs[3] = {1.34e6, 1.30e6, 1.25e6};
 
 // Sum over the workgroup (every thread gets it); ends with a barrier.
 __device__ __forceinline__ double wg_sum(double v) {
@@ -94,32 +96,36 @@ struct MixedPick {
   }
 };
 
-// The decode program of a cache format: the query type (KV8 false) or fp8
-// E4M3 codes for K and V.
-template <typename T, int D, int BS, bool KV8>
-using MixedSeg = MfmaDecode<T, KV8 ? kFmtFp8 : kFmtQ, KV8 ? kFmtFp8 : kFmtQ, D, BS>;
+// Cache formats of the mixed step: the query type, fp8 E4M3 codes, int8
+// codes with per-(block, KV head) scales.
+enum : int { kMixQ = 0, kMixFp8 = 1, kMixI8 = 2 };
 
-template <typename T, int D, int BS, bool KV8>
+// The decode program of a cache format.
+template <typename T, int D, int BS, int FMT>
+using MixedSeg = MfmaDecode<T, FMT == kMixFp8 ? kFmtFp8 : (FMT == kMixI8 ? kFmtI8 : kFmtQ),
+                            FMT == kMixFp8 ? kFmtFp8 : (FMT == kMixI8 ? kFmtI8 : kFmtQ), D, BS>;
+
+template <typename T, int D, int BS, int FMT>
 __global__ __launch_bounds__(kPThreads) void mixed_kernel(PrefillParams pf, DecodeParams d, int npf, int ndec,
                                                           int nq, int slots) {
   const int b = blockIdx.x;
   if (b < ndec) {
     const MixedPick pick{pf.query_start_loc, pf.seq_lens, npf > 0 ? pf.num_seqs : 0, pf.max_blocks * BS,
-                         d.num_q_heads, d.num_kv_heads, D, KV8 ? 1 : (int)sizeof(T), slots,
-                         kDecodeWgBytesPerUs[KV8], kPrefillSlotFlopsPerUs[KV8]};
-    decode_share<MixedSeg<T, D, BS, KV8>, T, kMixedWaves>(d, b, ndec, pick);
+                         d.num_q_heads, d.num_kv_heads, D, FMT == kMixQ ? (int)sizeof(T) : 1, slots,
+                         kDecodeWgBytesPerUs[FMT], kPrefillSlotFlopsPerUs[FMT]};
+    decode_share<MixedSeg<T, D, BS, FMT>, T, kMixedWaves>(d, b, ndec, pick);
     return;
   }
   // ndec is a multiple of the XCD count, so tile lin runs on XCD lin % kXcds
   // as in a prefill launch
   int seq, kvh, qtile;
   prefill_work(b - ndec, npf, nq, pf.num_kv_heads, seq, kvh, qtile);
-  prefill_tile<T, D, BS, KV8>(pf, seq, kvh, qtile);
+  prefill_tile<T, D, BS, FMT != kMixQ, FMT == kMixI8>(pf, seq, kvh, qtile);
 }
 
-template <typename T, int D, int BS, bool KV8>
+template <typename T, int D, int BS, int FMT>
 hipError_t launch_mixed_t(const PrefillParams& pf, const DecodeParams& d0, hipStream_t stream) {
-  auto kernel = mixed_kernel<T, D, BS, KV8>;
+  auto kernel = mixed_kernel<T, D, BS, FMT>;
   DecodeParams d = d0;
   const int qpos = pf.num_seqs > 0 ? kRowsPerWG / pf.group : 1;   // chunk positions per tile
   const int nq = (pf.num_seqs > 0 && pf.max_q_len > 0) ? (pf.max_q_len + qpos - 1) / qpos : 0;
@@ -133,7 +139,7 @@ hipError_t launch_mixed_t(const PrefillParams& pf, const DecodeParams& d0, hipSt
   if (d.num_seqs > 0) {
     const size_t plan = (size_t)((2 * d.num_seqs + 1 + 3) & ~3) * sizeof(int);
     const size_t per_slot = (size_t)d.group * D * sizeof(float) + 33 * sizeof(float);
-    const size_t kstage = MixedSeg<T, D, BS, KV8>::kStageK ? (size_t)kMixedWaves * 4096 : 0;
+    const size_t kstage = MixedSeg<T, D, BS, FMT>::kStageK ? (size_t)kMixedWaves * 4096 : 0;
     const size_t room = stages > plan + 64 + kstage ? stages - kstage : plan + 64;
     int slots = 0;
     if (d.mode != kSplitNone && plan + 64 < room)
@@ -168,25 +174,29 @@ hipError_t launch_mixed_t(const PrefillParams& pf, const DecodeParams& d0, hipSt
   return hipGetLastError();
 }
 
-template <typename T, int D, bool KV8>
+template <typename T, int D, int FMT>
 hipError_t launch_mixed_bs(const PrefillParams& pf, const DecodeParams& d, int block_size, hipStream_t s) {
   switch (block_size) {
-    case 8: return launch_mixed_t<T, D, 8, KV8>(pf, d, s);
-    case 16: return launch_mixed_t<T, D, 16, KV8>(pf, d, s);
-    case 32: return launch_mixed_t<T, D, 32, KV8>(pf, d, s);
-    default: return launch_mixed_t<T, D, 64, KV8>(pf, d, s);
+    case 8: return launch_mixed_t<T, D, 8, FMT>(pf, d, s);
+    case 16: return launch_mixed_t<T, D, 16, FMT>(pf, d, s);
+    case 32: return launch_mixed_t<T, D, 32, FMT>(pf, d, s);
+    default: return launch_mixed_t<T, D, 64, FMT>(pf, d, s);
   }
 }
 
-template <typename T>
-hipError_t launch_mixed_d(const PrefillParams& pf, const DecodeParams& d, int head_dim, int block_size, bool kv8,
+template <typename T, int FMT>
+hipError_t launch_mixed_f(const PrefillParams& pf, const DecodeParams& d, int head_dim, int block_size,
                           hipStream_t s) {
-  if (kv8) {
-    if (head_dim == 128) return launch_mixed_bs<T, 128, true>(pf, d, block_size, s);
-    return launch_mixed_bs<T, 64, true>(pf, d, block_size, s);
-  }
-  if (head_dim == 128) return launch_mixed_bs<T, 128, false>(pf, d, block_size, s);
-  return launch_mixed_bs<T, 64, false>(pf, d, block_size, s);
+  if (head_dim == 128) return launch_mixed_bs<T, 128, FMT>(pf, d, block_size, s);
+  return launch_mixed_bs<T, 64, FMT>(pf, d, block_size, s);
+}
+
+template <typename T>
+hipError_t launch_mixed_d(const PrefillParams& pf, const DecodeParams& d, int head_dim, int block_size, int fmt,
+                          hipStream_t s) {
+  if (fmt == kMixFp8) return launch_mixed_f<T, kMixFp8>(pf, d, head_dim, block_size, s);
+  if (fmt == kMixI8) return launch_mixed_f<T, kMixI8>(pf, d, head_dim, block_size, s);
+  return launch_mixed_f<T, kMixQ>(pf, d, head_dim, block_size, s);
 }
 
 }  // namespace
@@ -194,10 +204,14 @@ hipError_t launch_mixed_d(const PrefillParams& pf, const DecodeParams& d, int he
 hipError_t launch_mixed(const PrefillParams& pf, const DecodeParams& d, hipStream_t stream) {
   const bool has_pf = pf.num_seqs > 0, has_d = d.num_seqs > 0;
   if (!has_pf && !has_d) return hipSuccess;
-  // K and V pools of the query type or both fp8; with both parts present
-  // they share the pools, the head shape and the block size
-  if (has_pf && pf.cache_dtype != pf.q_dtype && pf.cache_dtype != kFP8) return hipErrorInvalidValue;
-  if (has_d && (d.v_cache_dtype != d.cache_dtype || (d.cache_dtype != d.q_dtype && d.cache_dtype != kFP8)))
+  // K and V pools of the query type, or both fp8, or both int8 with block
+  // scales; with both parts present they share the pools, the head shape and
+  // the block size
+  const auto pool_ok = [](int q, int c) { return c == q || c == kFP8 || c == kI8; };
+  if (has_pf && (!pool_ok(pf.q_dtype, pf.cache_dtype) || (pf.cache_dtype == kI8 && !pf.k_scales)))
+    return hipErrorInvalidValue;
+  if (has_d && (d.v_cache_dtype != d.cache_dtype || !pool_ok(d.q_dtype, d.cache_dtype) ||
+                (d.cache_dtype == kI8 && !d.k_scales)))
     return hipErrorInvalidValue;
   if (has_pf && has_d &&
       (pf.head_dim != d.head_dim || pf.block_size != d.block_size || pf.num_kv_heads != d.num_kv_heads ||
@@ -206,9 +220,10 @@ hipError_t launch_mixed(const PrefillParams& pf, const DecodeParams& d, hipStrea
   const int q_dtype = has_d ? d.q_dtype : pf.q_dtype;
   const int head_dim = has_d ? d.head_dim : pf.head_dim;
   const int block_size = has_d ? d.block_size : pf.block_size;
-  const bool kv8 = (has_d ? d.cache_dtype : pf.cache_dtype) == kFP8;
-  if (q_dtype == kBF16) return launch_mixed_d<__bf16>(pf, d, head_dim, block_size, kv8, stream);
-  if (q_dtype == kF16) return launch_mixed_d<_Float16>(pf, d, head_dim, block_size, kv8, stream);
+  const int cache = has_d ? d.cache_dtype : pf.cache_dtype;
+  const int fmt = cache == kFP8 ? kMixFp8 : (cache == kI8 ? kMixI8 : kMixQ);
+  if (q_dtype == kBF16) return launch_mixed_d<__bf16>(pf, d, head_dim, block_size, fmt, stream);
+  if (q_dtype == kF16) return launch_mixed_d<_Float16>(pf, d, head_dim, block_size, fmt, stream);
   return hipErrorInvalidValue;
 }
 

@@ -816,6 +816,51 @@ pa_status pa_prefill_chunk_int8(void* out, const void* q, const int32_t* query_s
   return hip_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
+static pa_status mixed_impl(void* prefill_out, const void* prefill_q, const int32_t* query_start_loc,
+                            const int32_t* prefill_block_tables, const int32_t* prefill_seq_lens,
+                            int32_t num_chunks, int32_t total_q_tokens, int32_t max_q_len,
+                            int32_t prefill_max_blocks_per_seq, void* decode_out, const void* decode_q,
+                            const int32_t* decode_block_tables, const int32_t* decode_seq_lens,
+                            int32_t num_decodes, int32_t decode_max_blocks_per_seq, int32_t max_seq_len,
+                            const void* k_pool, const void* v_pool, float scale, int32_t block_size,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, pa_dtype q_dtype,
+                            pa_dtype cache_dtype, float k_scale, float v_scale, const float* k_scales,
+                            const float* v_scales, int32_t partition_size, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if ((q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16) ||
+      (cache_dtype != q_dtype && cache_dtype != PA_DTYPE_FP8_E4M3 && cache_dtype != PA_DTYPE_INT8))
+    return fail(PA_ERR_UNSUPPORTED,
+                "the mixed-step launch supports bf16/f16 queries over a cache of the same type, fp8 or "
+                "int8");
+  pa::PrefillParams pf{};
+  bool pf_work = false;
+  pa_status st = prefill_setup(&pf, &pf_work, prefill_out, prefill_q, query_start_loc, k_pool,
+                               v_pool, prefill_block_tables, prefill_seq_lens, scale, block_size,
+                               num_chunks, total_q_tokens, max_q_len, num_q_heads, num_kv_heads,
+                               head_dim, prefill_max_blocks_per_seq, q_dtype, cache_dtype, k_scale,
+                               v_scale, k_scales, v_scales);
+  if (st != PA_OK) return st;
+  pa::DecodeParams d{};
+  bool d_work = false;
+  st = decode_setup(&d, &d_work, decode_out, decode_q, k_pool, v_pool, decode_block_tables,
+                    decode_seq_lens, scale, block_size, num_decodes, num_q_heads, num_kv_heads,
+                    head_dim, decode_max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype,
+                    cache_dtype, k_scale, v_scale, partition_size, workspace, workspace_bytes,
+                    k_scales, v_scales, nullptr, nullptr, 0, 0, false);
+  if (st != PA_OK) return st;
+  if (!pf_work) pf.num_seqs = 0;   // no query tokens: no prefill tiles
+  if (!d_work) d.num_seqs = 0;
+  if (!pf_work && !d_work) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pa::launch_mixed(pf, d, s);
+  if (e != hipSuccess) return hip_status(e, "mixed-step launch");
+  if (d_work) {
+    e = pa::launch_decode_reduce(d, s);
+    if (e != hipSuccess) return hip_status(e, "decode reduce launch");
+  }
+  return ok();
+}
+
 pa_status pa_mixed_attention(void* prefill_out, const void* prefill_q,
                              const int32_t* query_start_loc, const int32_t* prefill_block_tables,
                              const int32_t* prefill_seq_lens, int32_t num_chunks,
@@ -829,37 +874,36 @@ pa_status pa_mixed_attention(void* prefill_out, const void* prefill_q,
                              int32_t head_dim, pa_dtype q_dtype, pa_dtype cache_dtype,
                              float k_scale, float v_scale, int32_t partition_size,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if ((q_dtype != PA_DTYPE_BF16 && q_dtype != PA_DTYPE_F16) ||
-      (cache_dtype != q_dtype && cache_dtype != PA_DTYPE_FP8_E4M3))
-    return fail(PA_ERR_UNSUPPORTED,
-                "the mixed-step launch supports bf16/f16 queries over a cache of the same type or fp8");
-  pa::PrefillParams pf{};
-  bool pf_work = false;
-  pa_status st = prefill_setup(&pf, &pf_work, prefill_out, prefill_q, query_start_loc, k_pool,
-                               v_pool, prefill_block_tables, prefill_seq_lens, scale, block_size,
-                               num_chunks, total_q_tokens, max_q_len, num_q_heads, num_kv_heads,
-                               head_dim, prefill_max_blocks_per_seq, q_dtype, cache_dtype, k_scale,
-                               v_scale);
-  if (st != PA_OK) return st;
-  pa::DecodeParams d{};
-  bool d_work = false;
-  st = decode_setup(&d, &d_work, decode_out, decode_q, k_pool, v_pool, decode_block_tables,
-                    decode_seq_lens, scale, block_size, num_decodes, num_q_heads, num_kv_heads,
-                    head_dim, decode_max_blocks_per_seq, max_seq_len, q_dtype, cache_dtype,
-                    cache_dtype, k_scale, v_scale, partition_size, workspace, workspace_bytes,
-                    nullptr, nullptr, nullptr, nullptr, 0, 0, false);
-  if (st != PA_OK) return st;
-  if (!pf_work) pf.num_seqs = 0;   // no query tokens: no prefill tiles
-  if (!d_work) d.num_seqs = 0;
-  if (!pf_work && !d_work) return ok();
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pa::launch_mixed(pf, d, s);
-  if (e != hipSuccess) return hip_status(e, "mixed-step launch");
-  if (d_work) {
-    e = pa::launch_decode_reduce(d, s);
-    if (e != hipSuccess) return hip_status(e, "decode reduce launch");
-  }
-  return ok();
+  if (cache_dtype == PA_DTYPE_INT8)
+    return fail(PA_ERR_INVALID_ARG, "an int8 cache needs its per-block scales (pa_mixed_attention_int8)");
+  return mixed_impl(prefill_out, prefill_q, query_start_loc, prefill_block_tables, prefill_seq_lens,
+                    num_chunks, total_q_tokens, max_q_len, prefill_max_blocks_per_seq, decode_out, decode_q,
+                    decode_block_tables, decode_seq_lens, num_decodes, decode_max_blocks_per_seq,
+                    max_seq_len, k_pool, v_pool, scale, block_size, num_q_heads, num_kv_heads, head_dim,
+                    q_dtype, cache_dtype, k_scale, v_scale, nullptr, nullptr, partition_size, workspace,
+                    workspace_bytes, stream);
+}
+
+pa_status pa_mixed_attention_int8(void* prefill_out, const void* prefill_q,
+                                  const int32_t* query_start_loc, const int32_t* prefill_block_tables,
+                                  const int32_t* prefill_seq_lens, int32_t num_chunks,
+                                  int32_t total_q_tokens, int32_t max_q_len,
+                                  int32_t prefill_max_blocks_per_seq, void* decode_out,
+                                  const void* decode_q, const int32_t* decode_block_tables,
+                                  const int32_t* decode_seq_lens, int32_t num_decodes,
+                                  int32_t decode_max_blocks_per_seq, int32_t max_seq_len,
+                                  const void* k_pool, const void* v_pool, const float* k_scales,
+                                  const float* v_scales, float scale, int32_t block_size,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  pa_dtype q_dtype, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!k_scales || !v_scales) return fail(PA_ERR_INVALID_ARG, "an int8 cache needs its per-block scales");
+  return mixed_impl(prefill_out, prefill_q, query_start_loc, prefill_block_tables, prefill_seq_lens,
+                    num_chunks, total_q_tokens, max_q_len, prefill_max_blocks_per_seq, decode_out, decode_q,
+                    decode_block_tables, decode_seq_lens, num_decodes, decode_max_blocks_per_seq,
+                    max_seq_len, k_pool, v_pool, scale, block_size, num_q_heads, num_kv_heads, head_dim,
+                    q_dtype, PA_DTYPE_INT8, 1.0f, 1.0f, k_scales, v_scales, partition_size, workspace,
+                    workspace_bytes, stream);
 }
 
 pa_status pa_check_block_tables(const int32_t* block_tables, const int32_t* seq_lens,

@@ -179,6 +179,15 @@ __device__ __forceinline__ float lanes4_max(float v) {
   return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Sum over the four lanes c16, c16 + 16, c16 + 32, c16 + 48 (every one of
+// them gets the same total: each addition is commutative).
+__device__ __forceinline__ float lanes4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Two 1.0 values of a 16-bit type, packed: the all-ones matrix operand whose
 // product with a probability operand sums it.
 template <typename T> inline constexpr uint32_t kOnes = 0;

@@ -88,18 +88,6 @@ constexpr int kKeyTile = 64;
 constexpr float kSlack = 8.0f;   // log2 units
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
 
-// The two 16-bit values of a packed pair, as float32 (exact).
-template <typename T>
-__device__ __forceinline__ float lo_of(uint32_t w) {
-  if constexpr (__is_same(T, __bf16)) return __builtin_bit_cast(float, w << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-}
-template <typename T>
-__device__ __forceinline__ float hi_of(uint32_t w) {
-  if constexpr (__is_same(T, __bf16)) return __builtin_bit_cast(float, w & 0xffff0000u);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
 // Tiles are stored row-major (one 2D-byte row per key) with the 16-byte
 // chunks of each row XOR-swizzled, so that the LDS reads of the matrix
 // operands hit distinct banks:
@@ -311,12 +299,11 @@ __device__ __forceinline__ void pv_mma(f32x4 (&acc)[2][D / 16], const u32x2 (&h)
     for (int b = 0; b < 2; ++b) acc[b][NB0 + j] = PMma<T>::mma(va, pop[b], acc[b][NB0 + j]);
   }
 }
-// popl: the probabilities whose row sums normalise the output (pop itself,
-// or for an int8 cache the same probabilities without the V block scales)
-template <typename T, int D>
+// kOnesSum: the row sums of pop are formed here too, as its product with an
+// all-ones operand (an int8 cache sums its probabilities on the VALU instead)
+template <typename T, int D, bool kOnesSum>
 __device__ __forceinline__ void pv_tile(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[2], const u32x4 (&pop)[2][2],
-                                        const u32x4 (&popl)[2][2], uint32_t stage,
-                                        const uint32_t (&voff)[D / 16]) {
+                                        uint32_t stage, const uint32_t (&voff)[D / 16]) {
   const u32x4 ones = {kOnes<T>, kOnes<T>, kOnes<T>, kOnes<T>};
   u32x2 h0[8], h1[8];
   if constexpr (D == 128) {
@@ -340,10 +327,12 @@ __device__ __forceinline__ void pv_tile(f32x4 (&acc)[2][D / 16], f32x4 (&acc_l)[
     lds_wait<0>(h1);
     pv_mma<T, D, 0>(acc, h1, pop[1]);
   }
+  if constexpr (kOnesSum) {
 #pragma unroll
-  for (int ap = 0; ap < 2; ++ap)
+    for (int ap = 0; ap < 2; ++ap)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, popl[ap][b], acc_l[b]);
+      for (int b = 0; b < 2; ++b) acc_l[b] = PMma<T>::mma(ones, pop[ap][b], acc_l[b]);
+  }
 }
 
 // Work item `lin` of `nwg` (the workgroup's linear index in a launch whose
@@ -438,9 +427,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
   }
 
   // Running max (in logit units, log2 domain), unnormalised outputs, and the
-  // row sums of the rounded probabilities, formed on the matrix cores by a
+  // row sums: of the rounded probabilities, formed on the matrix cores by a
   // value product against an all-ones operand (every row of acc_l holds the
-  // column's sum).
+  // column's sum), or for an int8 cache of the float32 probabilities, one
+  // partial sum per lane in acc_l[b][0] (its four lanes are added at the end).
   float m_run[2] = {-INFINITY, -INFINITY};
   f32x4 acc[2][NB], acc_l[2];
 #pragma unroll
@@ -578,13 +568,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
       }
     }
     // p = 2^(c * (q.k) - m): one fused multiply-add per score.  int8: the
-    // value product takes p times the key's block V scale, the row sums p.
+    // value product takes p times the key's block V scale, rounded once, and
+    // the row sums add p in float32, so that each weight of the normalised
+    // output carries a single rounding.
     u32x4 pop[2][2];   // [key pair][column tile]
-    u32x4 popl[I8 ? 2 : 1][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const float nm = -m_run[b];
-      uint32_t w[4][2], wl[4][2];
+      uint32_t w[4][2];
+      float ls = 0.f;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -592,24 +584,19 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i], cscale, nm));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b][i + 1], cscale, nm));
           if constexpr (I8) {
-            // the rounded probabilities, then each times its V scale: a row
-            // dominated by one key keeps that key's value to one rounding
-            const uint32_t pl = pack2<T>(e0, e1);
-            wl[a][i / 2] = pl;
-            w[a][i / 2] = pack2<T>(lo_of<T>(pl) * vsc[a], hi_of<T>(pl) * vsc[a]);
+            w[a][i / 2] = pack2<T>(e0 * vsc[a], e1 * vsc[a]);
+            ls += e0 + e1;
           } else {
             w[a][i / 2] = pack2<T>(e0, e1);
           }
         }
+      if constexpr (I8) acc_l[b][0] += ls;
 #pragma unroll
-      for (int ap = 0; ap < 2; ++ap) {
+      for (int ap = 0; ap < 2; ++ap)
         pop[ap][b] = u32x4{w[2 * ap][0], w[2 * ap][1], w[2 * ap + 1][0], w[2 * ap + 1][1]};
-        if constexpr (I8) popl[ap][b] = u32x4{wl[2 * ap][0], wl[2 * ap][1], wl[2 * ap + 1][0], wl[2 * ap + 1][1]};
-      }
     }
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (I8) pv_tile<T, D>(acc, acc_l, pop, popl, v_base, voff);
-    else pv_tile<T, D>(acc, acc_l, pop, pop, v_base, voff);
+    pv_tile<T, D, !I8>(acc, acc_l, pop, v_base, voff);
     __builtin_amdgcn_s_setprio(0);
     if (more) {
       // this wave's copy of the next tile has landed (8-bit: decoded and
@@ -622,6 +609,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, int seq, in
   }
 
   // ---- normalise and store: lane (G, c16) holds dims 16 nn + 4 G + i of its row
+  if constexpr (I8) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc_l[b][0] = lanes4_sum(acc_l[b][0]);
+  }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (!valid[b]) continue;

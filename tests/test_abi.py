@@ -115,7 +115,7 @@ def _mixed(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(cdt=4), UNSUPPORTED),                   # int8 caches: not in the mixed launch
+    (dict(cdt=4), INVALID),                       # int8 caches need pa_mixed_attention_int8
     (dict(qdt=F32, cdt=F32), UNSUPPORTED),
     (dict(cdt=FP8), INVALID),                     # fp8 is taken; the null pointers are not
     (dict(hq=12, hkv=4), UNSUPPORTED),            # prefill needs a power-of-two group
@@ -131,6 +131,21 @@ def test_mixed_rejects_before_launch(lib, kw, code):
 
 def test_mixed_empty_step_is_ok(lib):
     assert _mixed(lib, nc=0, tq=0, mq=0, S=0) == OK
+
+
+def test_mixed_int8_entry(lib):
+    fake = ctypes.c_void_p(256)           # never dereferenced: the checks fail first
+    assert _mixed(lib, cdt=4) == INVALID and b"pa_mixed_attention_int8" in lib.pa_last_error()
+
+    def mixed8(ks, vs, qdt=BF16, nc=2, tq=64, S=3, ptr=None, part=0):
+        p = ptr
+        return lib.pa_mixed_attention_int8(p, p, p, p, p, nc, tq, 32, 8, p, p, p, p, S, 8, 128, p, p, ks, vs,
+                                           0.1, 16, 8, 2, 128, qdt, part, None, 0, None)
+    assert mixed8(None, None) == INVALID                                 # no scales
+    assert mixed8(fake, fake, qdt=F32) == UNSUPPORTED                    # f32 queries
+    assert mixed8(fake, fake) == INVALID                                 # null tensors
+    assert mixed8(fake, fake, ptr=fake, part=512) == WORKSPACE
+    assert mixed8(fake, fake, nc=0, tq=0, S=0) == OK                     # nothing to do
 
 
 def test_mixed_workspace_required(lib):

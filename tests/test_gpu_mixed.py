@@ -1,7 +1,8 @@
-"""GPU parity of pa_mixed_attention, the mixed step's prefill chunks and decodes
-in one launch (16-bit and fp8 E4M3 caches): every output against the oracle
-(max-abs 2e-2), the prefill outputs bit for bit against pa_prefill_chunk, and
-HIP-graph replays bit for bit against the eager call."""
+"""GPU parity of pa_mixed_attention (16-bit and fp8 E4M3 caches) and
+pa_mixed_attention_int8 (INT8 cache with per-block scales), the mixed step's
+prefill chunks and decodes in one launch: every output against the oracle
+(max-abs 2e-2), the prefill outputs bit for bit against the standalone
+prefill call, and HIP-graph replays bit for bit against the eager call."""
 
 import dataclasses
 
@@ -11,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_cases import TOL, lib, max_abs, random_chunks, up, up_int
+from gpu_cases import TOL, lib, max_abs, random_chunks, random_chunks_int8, up, up_int
 
 pytestmark = pytest.mark.gpu
 
@@ -273,7 +274,74 @@ def test_fused_fp8_70b_shaped_step():
     assert _bits_equal(out_p, sep_p)
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+def _int8_step(rng, pchunks, pctx, dctx, hq, hkv, d, bs, q_dt, partition):
+    """As _fp8_step over an INT8 pool with per-(block, KV head) scales."""
+    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks_int8(rng, list(pchunks) + [1] * len(dctx),
+                                                              list(pctx) + list(dctx), hq, hkv, d, bs, q_dt)
+    P = len(pchunks)
+    qsl_p, q_p, tab_p, len_p = qsl[:P + 1], q[:qsl[P]], tables[:P], lens[:P]
+    q_d, tab_d, len_d = q[qsl[P]:], tables[P:], lens[P:]
+    scale = 1.0 / np.sqrt(d)
+    pa = lib()
+    gk, gv = up(kp, "int8"), up(vp, "int8")
+    gq_p, gq_d = up(q_p, q_dt), up(q_d, q_dt)
+    gks, gvs = torch.from_numpy(ks).to(gq_p.device), torch.from_numpy(vs).to(gq_p.device)
+    out_p, out_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
+    max_len = int(len_d.max())
+    ws = pa.decode_workspace(gq_d, gk, max_len, partition)
+    pa.pa_mixed_attention_int8(out_p, gq_p, up_int(qsl_p), up_int(tab_p), up_int(len_p), int(max(pchunks)), out_d,
+                               gq_d, up_int(tab_d), up_int(len_d), max_len, gk, gv, gks, gvs, scale,
+                               partition_size=partition, workspace=ws)
+    sep_p = torch.empty_like(gq_p)
+    pa.pa_prefill_chunk_int8(sep_p, gq_p, up_int(qsl_p), gk, gv, gks, gvs, up_int(tab_p), up_int(len_p), scale,
+                             int(max(pchunks)))
+    torch.cuda.synchronize()
+    ref_p = oracle.prefill_chunk_attention(q_p, q_dt, qsl_p, kp, vp, "int8", tab_p, len_p, scale, bs, hkv,
+                                           k_block_scales=ks, v_block_scales=vs)
+    ref_d = oracle.decode_attention(q_d, q_dt, kp, vp, "int8", tab_d, len_d, scale, bs, hkv,
+                                    k_block_scales=ks, v_block_scales=vs)
+    return out_p, out_d, sep_p, ref_p, ref_d
+
+
+INT8_SHAPES = [
+    # (Hq, Hkv, D, bs, query type)
+    (64, 8, 128, 16, "bf16"),
+    (8, 2, 128, 32, "bf16"),
+    (32, 8, 128, 16, "f16"),
+    (4, 1, 64, 8, "f16"),
+    (4, 4, 64, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,q_dt", INT8_SHAPES)
+@pytest.mark.parametrize("partition", [0, 512, -1])
+def test_fused_int8_step_matches_oracle(hq, hkv, d, bs, q_dt, partition):
+    """INT8 K/V with per-(block, KV head) scales ([ybb] 6.2): ragged chunks and
+    decodes of 1 to 2,049 tokens in one launch."""
+    rng = np.random.default_rng(hq * 11 + d + bs + (partition % 89))
+    out_p, out_d, sep_p, ref_p, ref_d = _int8_step(rng, [40, 70, 17], [300, 170, 17],
+                                                   [1, 33, 500, 1200, 64, 2049, 16, 17], hq, hkv, d, bs, q_dt,
+                                                   partition)
+    assert max_abs(out_p, ref_p) <= TOL[q_dt]
+    assert max_abs(out_d, ref_d) <= TOL[q_dt]
+    assert _bits_equal(out_p, sep_p), "prefill part differs from pa_prefill_chunk_int8"
+
+
+def test_fused_int8_70b_shaped_step():
+    """The 70B-shaped layer of the fp8 case over an INT8 cache: four 512-token
+    chunks over 1,536-token contexts beside 128 lognormal decodes; every output
+    against the oracle."""
+    rng = np.random.default_rng(416)
+    dctx = np.clip(np.round(rng.lognormal(np.log(1500.0), 0.8, 128)), 16, 8192).astype(int)
+    out_p, out_d, sep_p, ref_p, ref_d = _int8_step(rng, [512] * 4, [1536] * 4, dctx, 64, 8, 128, 16, "bf16",
+                                                   512)
+    err_p, err_d = max_abs(out_p, ref_p), max_abs(out_d, ref_d)
+    print(f"[fused int8] prefill max-abs {err_p:.3e}, decode max-abs {err_d:.3e}", flush=True)
+    assert err_p <= TOL["bf16"] and err_d <= TOL["bf16"]
+    assert _bits_equal(out_p, sep_p)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3", "int8"])
 def test_fused_step_at_the_plan_limit(cache):
     """8,000 decodes of 1-64 tokens (the most a call plans: the lengths and
     their prefix sums fill 64 KB of LDS, with the fp8 K staging on top) beside
@@ -283,9 +351,14 @@ def test_fused_step_at_the_plan_limit(cache):
     hq, hkv, d, bs = 8, 2, 128, 16
     pchunks, pctx = [33, 64], [100, 64]
     chunks, ctxs = pchunks + [1] * len(dctx), pctx + list(dctx)
+    bscales = {}
     if cache == "fp8_e4m3":
         q, qsl, kp, vp, tables, lens, ks, vs = random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, cache,
                                                               q_dtype="bf16")
+    elif cache == "int8":
+        q, qsl, kp, vp, tables, lens, bks, bvs = random_chunks_int8(rng, chunks, ctxs, hq, hkv, d, bs, "bf16")
+        ks = vs = 1.0
+        bscales = dict(k_block_scales=bks, v_block_scales=bvs)
     else:
         q, qsl, kp, vp, tables, lens = random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, cache)
         ks = vs = 1.0
@@ -297,37 +370,54 @@ def test_fused_step_at_the_plan_limit(cache):
     out_p, out_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
     for partition in (0, 512, -1):
         ws = pa.decode_workspace(gq_d, gk, 64, partition)
-        pa.pa_mixed_attention(out_p, gq_p, up_int(qsl[:P + 1]), up_int(tables[:P]), up_int(lens[:P]), 64, out_d,
-                              gq_d, up_int(tables[P:]), up_int(lens[P:]), 64, gk, gv, scale, k_scale=ks,
-                              v_scale=vs, partition_size=partition, workspace=ws)
+        common = (out_p, gq_p, up_int(qsl[:P + 1]), up_int(tables[:P]), up_int(lens[:P]), 64, out_d, gq_d,
+                  up_int(tables[P:]), up_int(lens[P:]), 64, gk, gv)
+        if cache == "int8":
+            dev = gq_p.device
+            pa.pa_mixed_attention_int8(*common, torch.from_numpy(bks).to(dev), torch.from_numpy(bvs).to(dev),
+                                       scale, partition_size=partition, workspace=ws)
+        else:
+            pa.pa_mixed_attention(*common, scale, k_scale=ks, v_scale=vs, partition_size=partition, workspace=ws)
         torch.cuda.synchronize()
         ref_p = oracle.prefill_chunk_attention(q[:qsl[P]], "bf16", qsl[:P + 1], kp, vp, cache, tables[:P],
-                                               lens[:P], scale, bs, hkv, k_scale=ks, v_scale=vs)
+                                               lens[:P], scale, bs, hkv, k_scale=ks, v_scale=vs, **bscales)
         ref_d = oracle.decode_attention(q[qsl[P]:], "bf16", kp, vp, cache, tables[P:], lens[P:], scale, bs, hkv,
-                                        k_scale=ks, v_scale=vs)
+                                        k_scale=ks, v_scale=vs, **bscales)
         assert max_abs(out_p, ref_p) <= TOL["bf16"], partition
         assert max_abs(out_d, ref_d) <= TOL["bf16"], partition
 
 
-def test_fused_fp8_step_graph_replays_equal_eager():
-    """The fp8 one-launch step captured in a HIP graph: each of four replays
-    (eager fills and a stale workspace between them) gives the eager bits."""
+@pytest.mark.parametrize("cache", ["fp8_e4m3", "int8"])
+def test_fused_quantised_step_graph_replays_equal_eager(cache):
+    """The one-launch step over an fp8 or int8 cache captured in a HIP graph:
+    each of four replays (eager fills and a stale workspace between them)
+    gives the eager bits."""
     rng = np.random.default_rng(88)
     hq, hkv, d, bs = 32, 8, 128, 16
-    q, qsl, kp, vp, tables, lens, ks, vs = random_chunks(rng, [70, 33] + [1] * 6, [300, 33, 1, 64, 500, 1200, 17, 2049],
-                                                          hq, hkv, d, bs, "fp8_e4m3", q_dtype="bf16")
+    chunks, ctxs = [70, 33] + [1] * 6, [300, 33, 1, 64, 500, 1200, 17, 2049]
+    if cache == "int8":
+        q, qsl, kp, vp, tables, lens, ks, vs = random_chunks_int8(rng, chunks, ctxs, hq, hkv, d, bs, "bf16")
+    else:
+        q, qsl, kp, vp, tables, lens, ks, vs = random_chunks(rng, chunks, ctxs, hq, hkv, d, bs, cache,
+                                                              q_dtype="bf16")
     P = 2
     scale = 1.0 / np.sqrt(d)
     pa = lib()
-    gk, gv = up(kp, "fp8_e4m3"), up(vp, "fp8_e4m3")
+    gk, gv = up(kp, cache), up(vp, cache)
     gq_p, gq_d = up(q[:qsl[P]], "bf16"), up(q[qsl[P]:], "bf16")
     args = (up_int(qsl[:P + 1]), up_int(tables[:P]), up_int(lens[:P]), 70)
     dargs = (up_int(tables[P:]), up_int(lens[P:]), 2049)
     ws = pa.decode_workspace(gq_d, gk, 2049)
+    if cache == "int8":
+        gks, gvs = torch.from_numpy(ks).to(gq_p.device), torch.from_numpy(vs).to(gq_p.device)
 
     def call(out_p, out_d):
-        pa.pa_mixed_attention(out_p, gq_p, *args, out_d, gq_d, *dargs, gk, gv, scale, k_scale=ks, v_scale=vs,
-                              workspace=ws)
+        if cache == "int8":
+            pa.pa_mixed_attention_int8(out_p, gq_p, *args, out_d, gq_d, *dargs, gk, gv, gks, gvs, scale,
+                                       workspace=ws)
+        else:
+            pa.pa_mixed_attention(out_p, gq_p, *args, out_d, gq_d, *dargs, gk, gv, scale, k_scale=ks,
+                                  v_scale=vs, workspace=ws)
 
     eager_p, eager_d = torch.empty_like(gq_p), torch.empty_like(gq_d)
     call(eager_p, eager_d)
