@@ -68,7 +68,7 @@ def parse():
                          "llama2_7b_mha_f16 | llama3_8b_gqa_bf16 | llama3_70b_fp8kv | llama3_8b_kfp8_vbf16 "
                          "| llama3_8b_int8kv | llama3_70b_fp8kv_tp8 "
                          "| tiny_f32 "
-                         "| mixed_prefix_bf16 | mixed_70b_fp8kv")
+                         "| mixed_prefix_bf16 | mixed_70b_fp8kv | mixed_70b_int8kv")
     ap.add_argument("--rotate", type=int, default=4, help="batches with separate pools")
     ap.add_argument("--partition", type=int, default=None,
                     help="decode partition size override (default: the workload's)")
@@ -351,38 +351,71 @@ def run_mixed_bench(args, dev, spec=None):
     ws = pa.decode_workspace(qd, kp, max_len)
 
     sc = dict(k_scale=ks, v_scale=vs)
+    i8 = cdt == "int8"
+    if i8:
+        # per-(block, KV head) scales: copy-on-write copies them with the codes
+        gks = torch.from_numpy(case.k_block_scales).to(dev)
+        gvs = torch.from_numpy(case.v_block_scales).to(dev)
+
+    def write_step():
+        pa.pa_copy_blocks(kp, vp, pairs)
+        if i8:
+            pa.pa_copy_blocks(gks, gvs, pairs)
+            pa.pa_reshape_and_cache_int8(nk, nv, kp, vp, gks, gvs, slots)
+        else:
+            pa.pa_reshape_and_cache(nk, nv, kp, vp, slots, ks, vs)
+
+    def prefill():
+        if i8:
+            pa.pa_prefill_chunk_int8(out_c, qc, qsl, kp, vp, gks, gvs, ptab, plen, s.scale, max_q)
+        else:
+            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q, **sc)
+
+    def decode_attention():
+        if i8:
+            pa.pa_decode_attention_int8(out_d, qd, kp, vp, gks, gvs, dtab, dlen, s.scale, max_len, workspace=ws)
+        else:
+            pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
+
+    def decode_reduce():
+        if i8:
+            pa.pa_decode_reduce_int8(out_d, qd, kp, vp, gks, gvs, dtab, dlen, s.scale, max_len, workspace=ws)
+        else:
+            pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
 
     def fused_step(ev=None):
-        pa.pa_copy_blocks(kp, vp, pairs)
-        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots, ks, vs)
+        write_step()
         if ev is not None:
             ev[0].record()
-        pa.pa_mixed_attention(out_c, qc, qsl, ptab, plen, max_q, out_d, qd, dtab, dlen, max_len, kp, vp,
-                              s.scale, workspace=ws, **sc)
+        if i8:
+            pa.pa_mixed_attention_int8(out_c, qc, qsl, ptab, plen, max_q, out_d, qd, dtab, dlen, max_len, kp,
+                                       vp, gks, gvs, s.scale, workspace=ws)
+        else:
+            pa.pa_mixed_attention(out_c, qc, qsl, ptab, plen, max_q, out_d, qd, dtab, dlen, max_len, kp, vp,
+                                  s.scale, workspace=ws, **sc)
         if ev is not None:
             ev[1].record()
 
     def step(ev=None, side=None):
-        pa.pa_copy_blocks(kp, vp, pairs)
-        pa.pa_reshape_and_cache(nk, nv, kp, vp, slots, ks, vs)
+        write_step()
         if side is not None:
             # prefill chunks and decodes on two streams (joined at the end)
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
-                pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
-                pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
-            pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q, **sc)
+                decode_attention()
+                decode_reduce()
+            prefill()
             torch.cuda.current_stream().wait_stream(side)
             return
         if ev is not None:
             ev[0].record()
-        pa.pa_prefill_chunk(out_c, qc, qsl, kp, vp, ptab, plen, s.scale, max_q, **sc)
+        prefill()
         if ev is not None:
             ev[1].record()
-        pa.pa_decode_attention(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
+        decode_attention()
         if ev is not None:
             ev[2].record()
-        pa.pa_decode_reduce(out_d, qd, kp, vp, dtab, dlen, s.scale, max_len, workspace=ws, **sc)
+        decode_reduce()
         if ev is not None:
             ev[3].record()
 
@@ -442,6 +475,8 @@ def run_mixed_bench(args, dev, spec=None):
     sep_ms_step = sep_elapsed * 1e3 / args.steps
     flops = mixed_prefill_flops(case)
     eff = W.effective_kv_bytes(case.decode_lens, s.num_kv_heads, s.head_dim, cdt)
+    if i8:
+        eff += W.block_scale_bytes(case.decode_lens, s.num_kv_heads, s.block_size)
     tflops = flops / (pre_ms * 1e-3) / 1e12
     dec_gbps = eff / (dec_ms * 1e-3) / 1e9
     return {
@@ -463,7 +498,8 @@ def run_mixed_bench(args, dev, spec=None):
                             "traffic_unit": "bytes per launch",
                             "algorithmic_bytes_per_launch": eff, "avg_launch_ms": round(dec_ms, 5)},
         "fused_attention": {
-            "kernels": "mixed_kernel + lse_reduce_kernel (pa_mixed_attention)",
+            "kernels": "mixed_kernel + lse_reduce_kernel ("
+                       + ("pa_mixed_attention_int8)" if i8 else "pa_mixed_attention)"),
             "avg_ms": round(fused_ms, 5),
             "prefill_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2),
             "decode_gbps": round(eff / (fused_ms * 1e-3) / 1e9, 1),
@@ -877,7 +913,7 @@ def main():
     if args.config != "all" and args.config not in SUB_CONFIGS + [HEADLINE, "llama3_8b_int8kv",
                                                                    "llama3_8b_kfp8_vbf16",
                                                                    "llama3_70b_fp8kv_tp8",
-                                                                   "mixed_70b_fp8kv"]:
+                                                                   "mixed_70b_fp8kv", "mixed_70b_int8kv"]:
         print(f"unknown --config {args.config}", file=sys.stderr)
         sys.exit(2)
     # the CPU baseline forks oracle processes, so it runs before the GPU is initialised
@@ -892,9 +928,9 @@ def main():
     if name == "mixed_prefix_bf16":
         res = run_mixed_bench(args, dev)
         res["block_ops"] = run_block_ops_bench(dev)
-    elif name == "mixed_70b_fp8kv":
+    elif name in ("mixed_70b_fp8kv", "mixed_70b_int8kv"):
         import workloads as W
-        res = run_mixed_bench(args, dev, W.MIXED_70B_FP8)
+        res = run_mixed_bench(args, dev, W.MIXED_70B_FP8 if name == "mixed_70b_fp8kv" else W.MIXED_70B_INT8)
     else:
         res = run_decode_bench(args, dev, name)
     gpu_by_name = {name: res}

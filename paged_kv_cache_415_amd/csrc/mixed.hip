@@ -42,11 +42,12 @@ constexpr int kMixedWaves = kPThreads / 64;   // waves per workgroup, both kinds
 // kernel's byte rate against the bf16 one, the prefill rate by the fp8
 // prefill tiles' (codes decoded into LDS through registers); on that
 // workload over an fp8 cache any split from 96 to 256 decode workgroups
-// lands within 2 % of the best.  [2], the int8 cache with per-block scales,
-// is scaled the same way from the int8 decode kernel's byte rate and the
-// int8 prefill tiles' flop rate.  Only the
+// lands within 2 % of the best.  [2], the int8 cache with per-block scales:
+// on the 70B-shaped int8 serving step (4 chunks of 512 tokens, 128 decodes,
+// 64/8 heads, block 16) a decode rate of 19 KB/us beside 1.25 Mflop/us gave
+// the shortest launch among 16-29 KB/us (1-5 % apart).  Only the
 // ratio of a pair matters; it sets how many slots the decode part takes.
-constexpr double kDecodeWgBytesPerUs[3] = {24.5e3, 21.2e3, 22.1e3};
+constexpr double kDecodeWgBytesPerUs[3] = {24.5e3, 21.2e3, 19.0e3};
 constexpr double kPrefillSlotFlopsPerUs[3] = {1.34e6, 1.30e6, 1.25e6};
 
 // Sum over the workgroup (every thread gets it); ends with a barrier.

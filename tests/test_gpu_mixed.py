@@ -27,9 +27,18 @@ class MixedRun:
         dt, cdt = s.dtype, s.pool_dtype
         self.sc = dict(k_scale=case.k_scale, v_scale=case.v_scale)
         self.kp, self.vp = up(case.k_pool, cdt), up(case.v_pool, cdt)
+        self.i8 = cdt == "int8"
         pa.pa_copy_blocks(self.kp, self.vp, up_int(case.cow_pairs))
-        pa.pa_reshape_and_cache(up(case.new_k, dt), up(case.new_v, dt), self.kp, self.vp,
-                                up_int(case.slot_mapping), case.k_scale, case.v_scale)
+        if self.i8:
+            # copy-on-write takes the source block's scales with its codes
+            self.ks = torch.from_numpy(case.k_block_scales).to(self.kp.device)
+            self.vs = torch.from_numpy(case.v_block_scales).to(self.kp.device)
+            pa.pa_copy_blocks(self.ks, self.vs, up_int(case.cow_pairs))
+            pa.pa_reshape_and_cache_int8(up(case.new_k, dt), up(case.new_v, dt), self.kp, self.vp, self.ks,
+                                         self.vs, up_int(case.slot_mapping))
+        else:
+            pa.pa_reshape_and_cache(up(case.new_k, dt), up(case.new_v, dt), self.kp, self.vp,
+                                    up_int(case.slot_mapping), case.k_scale, case.v_scale)
         self.qc, self.qd = up(case.q_chunk, dt), up(case.q_decode, dt)
         self.qsl = up_int(case.query_start_loc)
         self.ptab, self.plen = up_int(case.prefill_tables), up_int(case.prefill_lens)
@@ -43,38 +52,60 @@ class MixedRun:
         s = self.case.spec
         out_c, out_d = out if out is not None else (torch.empty_like(self.qc), torch.empty_like(self.qd))
         ws = pa.decode_workspace(self.qd, self.kp, self.max_len, partition_size)
-        pa.pa_mixed_attention(out_c, self.qc, self.qsl, self.ptab, self.plen, self.max_q, out_d, self.qd,
-                              self.dtab, self.dlen, self.max_len, self.kp, self.vp, s.scale,
-                              partition_size=partition_size, workspace=ws, **self.sc)
+        common = (out_c, self.qc, self.qsl, self.ptab, self.plen, self.max_q, out_d, self.qd, self.dtab,
+                  self.dlen, self.max_len, self.kp, self.vp)
+        if self.i8:
+            pa.pa_mixed_attention_int8(*common, self.ks, self.vs, s.scale, partition_size=partition_size,
+                                       workspace=ws)
+        else:
+            pa.pa_mixed_attention(*common, s.scale, partition_size=partition_size, workspace=ws, **self.sc)
         return out_c, out_d
 
     def separate(self):
         pa = lib()
         s = self.case.spec
         out_c, out_d = torch.empty_like(self.qc), torch.empty_like(self.qd)
+        ws = pa.decode_workspace(self.qd, self.kp, self.max_len)
+        if self.i8:
+            if self.max_q > 0:
+                pa.pa_prefill_chunk_int8(out_c, self.qc, self.qsl, self.kp, self.vp, self.ks, self.vs, self.ptab,
+                                         self.plen, s.scale, self.max_q)
+            pa.pa_decode_int8(out_d, self.qd, self.kp, self.vp, self.ks, self.vs, self.dtab, self.dlen, s.scale,
+                              max_seq_len=self.max_len, workspace=ws)
+            return out_c, out_d
         if self.max_q > 0:
             pa.pa_prefill_chunk(out_c, self.qc, self.qsl, self.kp, self.vp, self.ptab, self.plen, s.scale,
                                 self.max_q, **self.sc)
-        ws = pa.decode_workspace(self.qd, self.kp, self.max_len)
         pa.pa_decode(out_d, self.qd, self.kp, self.vp, self.dtab, self.dlen, s.scale,
                      max_seq_len=self.max_len, workspace=ws, **self.sc)
         return out_c, out_d
 
+    def oracle_scales(self):
+        """The int8 pool's block scales after copy-on-write (None otherwise)."""
+        c = self.case
+        if not self.i8:
+            return None, None
+        return oracle.copy_blocks(c.k_block_scales, c.v_block_scales, c.cow_pairs)
+
     def oracle_pools(self):
         c, s = self.case, self.case.spec
         okp, ovp = oracle.copy_blocks(c.k_pool, c.v_pool, c.cow_pairs)
+        oks, ovs = self.oracle_scales()
         return oracle.reshape_and_cache(okp, ovp, s.pool_dtype, c.new_k, c.new_v, s.dtype, c.slot_mapping,
-                                        s.block_size, c.k_scale, c.v_scale)
+                                        s.block_size, c.k_scale, c.v_scale, k_block_scales=oks,
+                                        v_block_scales=ovs)
 
     def oracle(self):
         c, s = self.case, self.case.spec
         okp, ovp = self.oracle_pools()
+        oks, ovs = self.oracle_scales()
+        bsc = dict(k_block_scales=oks, v_block_scales=ovs)
         ref_c = oracle.prefill_chunk_attention(c.q_chunk, s.dtype, c.query_start_loc, okp, ovp, s.pool_dtype,
                                                c.prefill_tables, c.prefill_lens, s.scale, s.block_size,
-                                               s.num_kv_heads, k_scale=c.k_scale, v_scale=c.v_scale)
+                                               s.num_kv_heads, k_scale=c.k_scale, v_scale=c.v_scale, **bsc)
         ref_d = oracle.decode_attention(c.q_decode, s.dtype, okp, ovp, s.pool_dtype, c.decode_tables,
                                         self.dlens, s.scale, s.block_size, s.num_kv_heads,
-                                        k_scale=c.k_scale, v_scale=c.v_scale)
+                                        k_scale=c.k_scale, v_scale=c.v_scale, **bsc)
         return ref_c, ref_d
 
 
@@ -461,4 +492,29 @@ def test_fused_70b_fp8_serving_step_full_size():
     ref_c, ref_d = run.oracle()
     err_c, err_d = max_abs(out_c, ref_c), max_abs(out_d, ref_d)
     print(f"[fused fp8 70b] prefill max-abs {err_c:.3e}, decode max-abs {err_d:.3e}", flush=True)
+    assert err_c <= TOL["bf16"] and err_d <= TOL["bf16"]
+
+
+def test_fused_70b_int8_serving_step_full_size():
+    """The 70B-shaped serving step over an INT8 cache with per-(block, KV head)
+    scales: copy-on-write of the codes and of their scales, then the int8
+    scatter, byte-exact against the oracle; every decode and prefill output of
+    pa_mixed_attention_int8 against the oracle; prefill bits equal to
+    pa_prefill_chunk_int8's."""
+    case = W.make_mixed_case(W.MIXED_70B_INT8)
+    print(f"[fused int8 70b] decode tokens {int(case.decode_lens.sum())}, pool {case.k_pool.shape[0]} blocks",
+          flush=True)
+    run = MixedRun(case)
+    out_c, out_d = run.fused()
+    sep_c, _ = run.separate()
+    torch.cuda.synchronize()
+    assert _bits_equal(out_c, sep_c), "prefill part differs from pa_prefill_chunk_int8"
+    oks, ovs = run.oracle_scales()
+    assert np.array_equal(run.ks.cpu().numpy(), oks) and np.array_equal(run.vs.cpu().numpy(), ovs)
+    okp, ovp = run.oracle_pools()
+    assert np.array_equal(W.torch_to_bits(run.kp, "int8"), okp)
+    assert np.array_equal(W.torch_to_bits(run.vp, "int8"), ovp)
+    ref_c, ref_d = run.oracle()
+    err_c, err_d = max_abs(out_c, ref_c), max_abs(out_d, ref_d)
+    print(f"[fused int8 70b] prefill max-abs {err_c:.3e}, decode max-abs {err_d:.3e}", flush=True)
     assert err_c <= TOL["bf16"] and err_d <= TOL["bf16"]

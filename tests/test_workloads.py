@@ -123,3 +123,33 @@ def test_mixed_case_over_an_fp8_cache():
         finite = vals[np.isfinite(vals)]
         assert np.abs(finite).max() == 448.0
 
+
+
+def test_mixed_case_over_an_int8_cache():
+    """The int8 mixed step: one float32 scale per (block, KV head); after
+    copy-on-write (codes and scales) and the int8 scatter, every block that
+    holds tokens has, in each KV head, a code of magnitude 127 (its scale is
+    the amax of what it holds over 127), and rows past each context keep the
+    unwritten code -128."""
+    import dataclasses
+    import oracle
+    spec = dataclasses.replace(W.MIXED_70B_INT8, num_q_heads=8, num_kv_heads=4, head_dim=64)
+    case = W.make_mixed_case(spec, num_forks=2, prefix_len=32, chunk_len=16, decode_lens=[20, 50, 1])
+    nb, h = case.k_pool.shape[:2]
+    assert case.k_block_scales.shape == (nb, h) and case.k_block_scales.dtype == np.float32
+    assert np.all(case.k_block_scales > 0) and np.all(case.v_block_scales > 0)
+    kp, vp = oracle.copy_blocks(case.k_pool, case.v_pool, case.cow_pairs)
+    ks, vs = oracle.copy_blocks(case.k_block_scales, case.v_block_scales, case.cow_pairs)
+    kp, vp = oracle.reshape_and_cache(kp, vp, "int8", case.new_k, case.new_v, "bf16", case.slot_mapping,
+                                      spec.block_size, k_block_scales=ks, v_block_scales=vs)
+    bs = spec.block_size
+    tables = [(t, int(n)) for t, n in zip(case.prefill_tables, case.prefill_lens)] + \
+             [(t, int(n)) for t, n in zip(case.decode_tables, case.decode_lens)]
+    for pool in (kp, vp):
+        codes = pool.view(np.int8).astype(np.int32)
+        for t, n in tables:
+            flat = codes[t[: W.blocks_for(n, bs)]].transpose(1, 0, 2, 3).reshape(h, -1, spec.head_dim)
+            assert np.all(np.abs(flat[:, :n]) <= 127)
+            assert np.all(flat[:, n:] == -128)
+            for b in range(W.blocks_for(n, bs)):
+                assert np.all(np.abs(flat[:, b * bs: min(n, (b + 1) * bs)]).max(axis=(1, 2)) == 127)

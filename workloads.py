@@ -440,8 +440,9 @@ class MixedSpec:
                         "appends a 512-token causal chunk; 112 others decode one token at lens "
                         "U[256,4096]; 32/8 heads, head_dim 128, block 32, bf16; copy-on-write "
                         "of the first divergent block")
-    cache_dtype: str | None = None   # K/V pools: the same as dtype, or "fp8_e4m3" with
-                                     # per-tensor scales (amax of the values / 448)
+    cache_dtype: str | None = None   # K/V pools: the same as dtype, "fp8_e4m3" with per-tensor
+                                     # scales (amax of the values / 448), or "int8" with one
+                                     # scale per (block, KV head) (the block's amax / 127)
 
     @property
     def pool_dtype(self) -> str:
@@ -468,6 +469,18 @@ MIXED_70B_FP8 = MixedSpec(
                  "activations, fp8 e4m3 K/V with per-tensor scales; copy-on-write of the "
                  "first divergent block"))
 
+# The same step over an INT8 cache with one scale per (block, KV head) for K
+# and for V ([ybb] 6.2 names INT8 beside FP8 for the KV cache); copy-on-write
+# copies the source block's scales with its codes.
+MIXED_70B_INT8 = MixedSpec(
+    name="mixed_70b_int8kv", num_forks=4, num_decode=128, num_q_heads=64, num_kv_heads=8,
+    block_size=16, cache_dtype="int8",
+    description=("70B-shaped serving step over an INT8 cache: 4 sequences share a 1024-token "
+                 "prefix and each appends a 512-token causal chunk; 128 others decode one "
+                 "token at lens U[256,4096]; 64/8 heads, head_dim 128, block 16, bf16 "
+                 "activations, int8 K/V with one float32 scale per block and KV head (amax/127); "
+                 "copy-on-write of the first divergent block with its scales"))
+
 
 @dataclass
 class MixedCase:
@@ -492,6 +505,8 @@ class MixedCase:
     poison_block: int
     k_scale: float = 1.0             # per-tensor scales of an fp8 pool (1.0 otherwise)
     v_scale: float = 1.0
+    k_block_scales: np.ndarray | None = None   # int8 pool: float32 [NB][Hkv] (before copy-on-write)
+    v_block_scales: np.ndarray | None = None
 
 
 def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int | None = None,
@@ -563,7 +578,33 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
     new_k = to_bits(rng.standard_normal((T, H, D), dtype=np.float32), dt)
     new_v = to_bits(rng.standard_normal((T, H, D), dtype=np.float32), dt)
 
+    slot_mapping = np.zeros(T, dtype=np.int64)
+    for f, t in enumerate(forks):
+        for i in range(C):
+            pos = P + i
+            slot_mapping[f * C + i] = t[pos // bs] * bs + pos % bs
+    for d, (t, n) in enumerate(zip(dec_tables, dlens)):
+        pos = int(n) - 1
+        slot_mapping[F * C + d] = t[pos // bs] * bs + pos % bs
+
     scales = {"k": 1.0, "v": 1.0}
+    bscales = {"k": None, "v": None}
+    if cdt == "int8":
+        # one scale per (block, KV head): the amax of everything the block will
+        # hold (its drawn tokens and the new tokens the scatter writes into it)
+        # over 127; copy-on-write destinations take their source's scales when
+        # the step copies them
+        for which, new in (("k", new_k), ("v", new_v)):
+            amax = np.zeros((nb, H), np.float32)
+            for ids, ntok, vals in drawn[which]:
+                flat = np.abs(vals).transpose(1, 0, 2, 3).reshape(H, -1, D)
+                flat[:, ntok:, :] = 0
+                idx = np.asarray(ids, dtype=np.int64)
+                amax[idx] = np.maximum(amax[idx], flat.reshape(H, len(ids), bs, D).max(axis=(2, 3)).T)
+            if T:
+                newa = np.abs(bits_to_torch(new, dt).float().numpy()).max(axis=2)       # [T][H]
+                np.maximum.at(amax, slot_mapping // bs, newa)
+            bscales[which] = np.where(amax > 0, amax / np.float32(INT8_MAX), 1.0).astype(np.float32)
     if cdt == "fp8_e4m3":
         for which, new in (("k", new_k), ("v", new_v)):
             m = float(np.abs(bits_to_torch(new, dt).float().numpy()).max()) if T else 0.0
@@ -574,19 +615,15 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
             scales[which] = float(np.float32(m / FP8_MAX)) if m > 0 else 1.0
     for which, pool in (("k", k_pool), ("v", v_pool)):
         for ids, ntok, vals in drawn[which]:
-            x = vals / np.float32(scales[which]) if cdt == "fp8_e4m3" else vals
-            bits = to_bits(x, cdt)
+            idx = np.asarray(ids, dtype=np.int64)
+            if cdt == "int8":      # torch.round: half to even
+                q8 = torch.from_numpy(vals / bscales[which][idx][:, :, None, None]).round().clamp(-127, 127)
+                bits = q8.to(torch.int8).numpy().view(np.uint8).copy()
+            else:
+                bits = to_bits(vals / np.float32(scales[which]) if cdt == "fp8_e4m3" else vals, cdt)
             flat = bits.transpose(1, 0, 2, 3).reshape(H, -1, D)
             flat[:, ntok:, :] = nan
-            pool[np.asarray(ids, dtype=np.int64)] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
-    slot_mapping = np.zeros(T, dtype=np.int64)
-    for f, t in enumerate(forks):
-        for i in range(C):
-            pos = P + i
-            slot_mapping[f * C + i] = t[pos // bs] * bs + pos % bs
-    for d, (t, n) in enumerate(zip(dec_tables, dlens)):
-        pos = int(n) - 1
-        slot_mapping[F * C + d] = t[pos // bs] * bs + pos % bs
+            pool[idx] = flat.reshape(H, len(ids), bs, D).transpose(1, 0, 2, 3)
 
     mbp = blocks_for(P + C, bs)
     prefill_tables = np.full((F, max(mbp, 1)), poison_block, dtype=np.int32)
@@ -610,7 +647,8 @@ def make_mixed_case(spec: MixedSpec = MIXED_SPEC, rep: int = 0, num_forks: int |
                      prefill_lens=np.full(F, P + C, dtype=np.int32),
                      q_decode=q_decode, decode_tables=decode_tables,
                      decode_lens=dlens.astype(np.int32), poison_block=poison_block,
-                     k_scale=scales["k"], v_scale=scales["v"])
+                     k_scale=scales["k"], v_scale=scales["v"],
+                     k_block_scales=bscales["k"], v_block_scales=bscales["v"])
 
 
 # ---------------------------------------------------------------------------
