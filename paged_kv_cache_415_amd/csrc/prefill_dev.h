@@ -115,6 +115,14 @@ __device__ __forceinline__ void dma16(const void* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_char*)dst, 16, 0, 0);
 }
 
+// The same through a buffer descriptor: `base` is wave-uniform (it lives in
+// scalar registers with the descriptor) and each lane adds its 32-bit byte
+// offset `off` < `nbytes`, so no per-lane 64-bit address is formed.
+__device__ __forceinline__ void bdma16(const char* base, int nbytes, uint32_t off, char* dst) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)dst, 16, off, 0, 0, 0);
+}
+
 // Where a wave's share of a K/V tile comes from.  Wave w copies key rows
 // [16 w, 16 w + 16) of every tile, which lie in one cache block (two for
 // 8-token blocks), RPI rows (1 KB) per LDS-DMA instruction.  Lane l lands
@@ -175,10 +183,11 @@ struct TileSrc {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int bi = (BS < 16 && RPI * i >= 8) ? blk.b : blk.a;   // one block per instruction
+        // the KV head's rows of block bi: BS rows of 2 D bytes
         const char* kb = kpool + bi * blk_bytes + head_off;
         const char* vb = vpool + bi * blk_bytes + head_off;
-        dma16(kb + koff[i], kd + i * 1024);
-        dma16(vb + voff[i], kd + TILE + i * 1024);
+        bdma16(kb, BS * D * 2, koff[i], kd + i * 1024);
+        bdma16(vb, BS * D * 2, voff[i], kd + TILE + i * 1024);
       }
     } else {
 #pragma unroll
