@@ -123,6 +123,12 @@ __device__ __forceinline__ void bdma16(const char* base, int nbytes, uint32_t of
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)dst, 16, off, 0, 0, 0);
 }
 
+// 16 bytes into registers through a buffer descriptor (as bdma16).
+__device__ __forceinline__ u32x4 bld16(const char* base, int nbytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Where a wave's share of a K/V tile comes from.  Wave w copies key rows
 // [16 w, 16 w + 16) of every tile, which lie in one cache block (two for
 // 8-token blocks), RPI rows (1 KB) per LDS-DMA instruction.  Lane l lands
@@ -235,6 +241,19 @@ struct TileSrc8 {
   template <class Blk>
   __device__ __forceinline__ void load(int kt, Blk blk) {
     const int wave_row = row & 15;                      // row among the wave's 16
+    if (BS >= 16 && kt * kKeyTile + (row | 15) < kend) {
+      // the wave's 16 rows lie in block blk.a: one descriptor per pool (its
+      // KV head's BS rows of D bytes), 32-bit offsets per lane
+      const char* kb = kpool + blk.a * blk_bytes + head_off;
+      const char* vb = vpool + blk.a * blk_bytes + head_off;
+      const uint32_t lo = (uint32_t)(((kt * kKeyTile + row) % BS) * D + sub * (D / 4));
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        k[i] = bld16(kb, BS * D, lo + 16 * i);
+        v[i] = bld16(vb, BS * D, lo + 16 * i);
+      }
+      return;
+    }
     int64_t off;
     if (kt * kKeyTile + (row | 15) < kend) {
       const int bi = (BS < 16 && wave_row >= 8) ? blk.b : blk.a;
