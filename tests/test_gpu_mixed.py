@@ -152,24 +152,33 @@ def test_fused_step_empty_decode_sequences():
     assert max_abs(out_d, ref_d) <= TOL["bf16"]
 
 
-def test_fused_step_without_prefill_or_decode():
-    """One part empty: the launch holds only the other kind of workgroup."""
-    case = W.make_mixed_case(num_forks=2, prefix_len=64, chunk_len=48, decode_lens=[100, 2000, 33])
+@pytest.mark.parametrize("cache", ["bf16", "int8"])
+def test_fused_step_without_prefill_or_decode(cache):
+    """One part empty: the launch holds only the other kind of workgroup
+    (16-bit cache, and an int8 cache through pa_mixed_attention_int8)."""
+    spec = W.MIXED_SPEC if cache == "bf16" else W.MIXED_70B_INT8
+    case = W.make_mixed_case(spec, num_forks=2, prefix_len=64, chunk_len=48, decode_lens=[100, 2000, 33])
     run = MixedRun(case)
     ref_c, ref_d = run.oracle()
     pa = lib()
     s = case.spec
+
+    def call(*args, workspace=None):
+        if run.i8:
+            pa.pa_mixed_attention_int8(*args, run.kp, run.vp, run.ks, run.vs, s.scale, workspace=workspace)
+        else:
+            pa.pa_mixed_attention(*args, run.kp, run.vp, s.scale, workspace=workspace)
+
     # decodes only: no query tokens
     out_d = torch.empty_like(run.qd)
     empty_q = run.qc[:0]
     ws = pa.decode_workspace(run.qd, run.kp, run.max_len)
-    pa.pa_mixed_attention(torch.empty_like(empty_q), empty_q, up_int(np.zeros(1, np.int32)), run.ptab[:0],
-                          run.plen[:0], 0, out_d, run.qd, run.dtab, run.dlen, run.max_len, run.kp, run.vp,
-                          s.scale, workspace=ws)
+    call(torch.empty_like(empty_q), empty_q, up_int(np.zeros(1, np.int32)), run.ptab[:0], run.plen[:0], 0, out_d,
+         run.qd, run.dtab, run.dlen, run.max_len, workspace=ws)
     # prefill chunks only: no decode sequences
     out_c = torch.empty_like(run.qc)
-    pa.pa_mixed_attention(out_c, run.qc, run.qsl, run.ptab, run.plen, run.max_q, run.qd[:0], run.qd[:0],
-                          run.dtab[:0], run.dlen[:0], 1, run.kp, run.vp, s.scale)
+    call(out_c, run.qc, run.qsl, run.ptab, run.plen, run.max_q, run.qd[:0], run.qd[:0], run.dtab[:0],
+         run.dlen[:0], 1)
     torch.cuda.synchronize()
     assert max_abs(out_d, ref_d) <= TOL["bf16"]
     assert max_abs(out_c, ref_c) <= TOL["bf16"]
