@@ -314,10 +314,14 @@ def test_fused_fp8_70b_shaped_step():
     assert _bits_equal(out_p, sep_p)
 
 
-def _int8_step(rng, pchunks, pctx, dctx, hq, hkv, d, bs, q_dt, partition):
-    """As _fp8_step over an INT8 pool with per-(block, KV head) scales."""
+def _int8_step(rng, pchunks, pctx, dctx, hq, hkv, d, bs, q_dt, partition, v_scale_mul=1.0, q_mul=1.0):
+    """As _fp8_step over an INT8 pool with per-(block, KV head) scales (V
+    scales times v_scale_mul, queries times q_mul)."""
     q, qsl, kp, vp, tables, lens, ks, vs = random_chunks_int8(rng, list(pchunks) + [1] * len(dctx),
-                                                              list(pctx) + list(dctx), hq, hkv, d, bs, q_dt)
+                                                              list(pctx) + list(dctx), hq, hkv, d, bs, q_dt,
+                                                              v_scale_mul=v_scale_mul)
+    if q_mul != 1.0:
+        q = W.to_bits(W.bits_to_torch(q, q_dt).float().numpy() * q_mul, q_dt)
     P = len(pchunks)
     qsl_p, q_p, tab_p, len_p = qsl[:P + 1], q[:qsl[P]], tables[:P], lens[:P]
     q_d, tab_d, len_d = q[qsl[P]:], tables[P:], lens[P:]
@@ -365,6 +369,23 @@ def test_fused_int8_step_matches_oracle(hq, hkv, d, bs, q_dt, partition):
     assert max_abs(out_p, ref_p) <= TOL[q_dt]
     assert max_abs(out_d, ref_d) <= TOL[q_dt]
     assert _bits_equal(out_p, sep_p), "prefill part differs from pa_prefill_chunk_int8"
+
+
+def test_fused_int8_f16_queries_large_value_scales():
+    """f16 queries over an int8 cache whose V values reach about 4e4 (block V
+    scales near 300) with widely spread logits, in one launch: the value
+    operand p x scale stays inside f16's range in both programs (the
+    reference max moves with every larger logit).  Compared relative to the
+    values' size."""
+    rng = np.random.default_rng(919)
+    out_p, out_d, sep_p, ref_p, ref_d = _int8_step(rng, [64, 33], [300, 700], [1, 90, 1500, 17], 8, 2, 128, 16,
+                                                   "f16", 0, v_scale_mul=1.5e4, q_mul=6.0)
+    vmax = float(max(np.abs(ref_p).max(), np.abs(ref_d).max()))
+    assert vmax > 1e3
+    assert torch.isfinite(out_p).all() and torch.isfinite(out_d).all()
+    assert max_abs(out_p, ref_p) <= TOL["f16"] * vmax / 4
+    assert max_abs(out_d, ref_d) <= TOL["f16"] * vmax / 4
+    assert _bits_equal(out_p, sep_p)
 
 
 def test_fused_int8_70b_shaped_step():
