@@ -623,6 +623,8 @@ def traffic_profile(name: str) -> str:
     """The committed rocprofv3 summary that records a workload's counters."""
     if name == "mixed_prefix_bf16":
         return os.path.join(ROOT, "profiles", "prefill_mfma_mixed_prefix_bf16.md")
+    if name.startswith("mixed_"):
+        return os.path.join(ROOT, "profiles", f"mixed_serving_{name}.md")
     return os.path.join(ROOT, "profiles", f"decode_mfma_{name}.md")
 
 
